@@ -1,0 +1,354 @@
+/*
+ * olk_ref — the oracle for the attention forward.  TEST INFRASTRUCTURE ONLY:
+ * it is loaded by tests/, by the smoke check and by the benchmark's CPU
+ * baseline, never by the product path (transformer_attention_fwd_amd/).
+ * It shares no code, header or table with the HIP library.
+ *
+ * What it computes is the plain definition of scaled dot-product attention,
+ * written out row by row in float64 with libm exp/tanh:
+ *
+ *   Y = Softmax((Q @ K^T) * scale + bias) @ V
+ *     (onnx-light reference kernels header page, "class Attention": the
+ *      baseline computation, the scale default 1/sqrt(head_size), the
+ *      softcap s -> softcap*tanh(s/softcap), GQA head sharing, past/present
+ *      concatenation, nonpad_kv_seqlen)
+ *
+ * with the operator-specific parts of
+ *   - onnx-light-cpu Python API "Custom operators", section "Microsoft
+ *     GroupQueryAttention": causal local window (a positive window counts the
+ *     attended tokens including the current one), present = entire past
+ *     followed by the current step, head_sink as a virtual logit that adds to
+ *     the denominator only, masks applied to real keys only;
+ *   - same page, section "Microsoft MultiHeadAttention": rank-4
+ *     cross-attention K/V, projection bias (only its query segment with rank-4
+ *     K/V), int32 key-padding lengths, additive bias (1|B, 1|N, S, T),
+ *     scale 1/sqrt(H), mask_filter_value -10000;
+ *   - onnx-light-cpu C++ API "Custom operators", GroupQueryAttention gradient
+ *     (default scale 1/sqrt(Shape(Q)[2]/num_heads), grouped K/V heads) and
+ *     GroupQueryAttentionFusionPattern (seqlens_k derived from the key length).
+ *
+ * Readings where the pages leave a step open (each is listed in the design
+ * notes with its support):
+ *   R1  GroupQueryAttention seqlens_k[b] = total_b - 1, past_b = total_b - S.
+ *   R3  causal alignment is bottom-right: query i sits at absolute position
+ *       past_b + i (GQA) or T - S + i (MHA / Attention).
+ *   R4  window W > 0 allows keys j with pos_i - W + 1 <= j <= pos_i.
+ *   R5  query head h reads KV head h / (Hq / Hkv).
+ *   R6  order: scale, + bias, softcap, then masks as exclusion.
+ *   R7  the sink logit is used raw (not scaled, not softcapped).
+ *   R9  MHA key padding adds mask_filter_value to the padded keys' scores;
+ *       they stay in the softmax.
+ *   R10 a row with no allowed key outputs 0.
+ *   R11 MHA projection bias layout is [q (N*H) | k (N*H) | v (N*Hv)].
+ * Intermediate values are not rounded; Y is returned in float64.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { REF_GQA = 0, REF_MHA = 1, REF_ATTENTION = 2 };
+enum { REF_F32 = 0, REF_F16 = 1, REF_BF16 = 2 };
+
+typedef struct {
+  int32_t op, dtype;
+  int32_t batch, q_seq, kv_seq, past_seq;
+  int32_t q_heads, kv_heads, head_size, v_head_size;
+  int32_t q_rank, kv_rank;
+  int32_t causal, window;
+  int32_t has_scale;
+  float scale, softcap, mask_filter_value;
+  int32_t bias_b, bias_h;
+} ref_desc;
+
+typedef struct {
+  const void *q, *k, *v, *past_k, *past_v;
+  const int32_t *lens;
+  const void *bias, *sink, *proj_bias;
+} ref_inputs;
+
+/* ---- element decoding (format definitions, not attention arithmetic) ---- */
+
+/* IEEE 754 binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits. */
+static double half_to_double(uint16_t h) {
+  int sign = (h >> 15) & 1, e = (h >> 10) & 31, f = h & 1023;
+  double v;
+  if (e == 0) v = ldexp((double)f, -24);
+  else if (e == 31) v = f ? NAN : INFINITY;
+  else v = ldexp((double)(1024 + f), e - 25);
+  return sign ? -v : v;
+}
+
+/* bfloat16 is the upper half of an IEEE binary32. */
+static double bf16_to_double(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float x;
+  memcpy(&x, &u, 4);
+  return (double)x;
+}
+
+static double elem(const void *base, int dtype, size_t idx) {
+  if (dtype == REF_F32) return (double)((const float *)base)[idx];
+  uint16_t h = ((const uint16_t *)base)[idx];
+  return dtype == REF_F16 ? half_to_double(h) : bf16_to_double(h);
+}
+
+static size_t esize(int dtype) { return dtype == REF_F32 ? 4 : 2; }
+
+/* ---- index helpers ---- */
+
+static size_t q_index(const ref_desc *d, int b, int h, int i, int c) {
+  if (d->q_rank == 4)
+    return (((size_t)b * d->q_heads + h) * d->q_seq + i) * d->head_size + c;
+  return (((size_t)b * d->q_seq + i) * d->q_heads + h) * d->head_size + c;
+}
+
+static size_t new_kv_index(const ref_desc *d, int b, int g, int j, int c, int width) {
+  if (d->kv_rank == 4)
+    return (((size_t)b * d->kv_heads + g) * d->kv_seq + j) * width + c;
+  return (((size_t)b * d->kv_seq + j) * d->kv_heads + g) * width + c;
+}
+
+static size_t past_index(const ref_desc *d, int b, int g, int j, int c, int width) {
+  return (((size_t)b * d->kv_heads + g) * d->past_seq + j) * width + c;
+}
+
+/* Per-batch sequence bookkeeping of one (b) row set. */
+typedef struct {
+  long past_b;   /* keys taken from the past buffer */
+  long total_b;  /* keys in the concatenated sequence */
+  long valid_b;  /* keys j < valid_b may be attended (exclusion) */
+  long pad_b;    /* MHA: keys j >= pad_b get mask_filter_value added */
+  long q_off;    /* absolute position of query 0 */
+} seqinfo;
+
+static int seq_info(const ref_desc *d, const ref_inputs *in, int b, seqinfo *s) {
+  long T = (long)d->past_seq + d->kv_seq;
+  if (d->op == REF_GQA) {
+    /* R1: seqlens_k = total - 1; the new keys follow the valid past. */
+    s->total_b = (long)in->lens[b] + 1;
+    s->past_b = s->total_b - d->q_seq;
+    if (s->past_b < 0 || s->past_b > d->past_seq) return -1;
+    s->valid_b = s->total_b;
+    s->pad_b = s->total_b;
+    s->q_off = s->past_b;
+  } else {
+    /* MHA / Attention: literal concatenation of the whole past buffer. */
+    s->total_b = T;
+    s->past_b = d->past_seq;
+    s->q_off = T - d->q_seq;
+    s->valid_b = T;
+    s->pad_b = T;
+    if (in->lens) {
+      long n = in->lens[b];
+      if (n < 0) n = 0;
+      if (n > T) n = T;
+      if (d->op == REF_ATTENTION) s->valid_b = n; /* -inf beyond nonpad length */
+      else s->pad_b = n;                           /* R9: additive mask */
+    }
+  }
+  return 0;
+}
+
+static double key_elem(const ref_desc *d, const ref_inputs *in, const seqinfo *s,
+                       int b, int g, long j, int c, int value) {
+  int width = value ? d->v_head_size : d->head_size;
+  const void *past = value ? in->past_v : in->past_k;
+  const void *cur = value ? in->v : in->k;
+  if (j < s->past_b) return elem(past, d->dtype, past_index(d, b, g, (int)j, c, width));
+  return elem(cur, d->dtype, new_kv_index(d, b, g, (int)(j - s->past_b), c, width));
+}
+
+static double scale_of(const ref_desc *d) {
+  /* Explicit scale as its float32 value; default 1/sqrt(head_size). */
+  return d->has_scale ? (double)d->scale : 1.0 / sqrt((double)d->head_size);
+}
+
+/*
+ * Softmax weights of row (b, h, i): w[j] for j < total_b (0 for excluded keys)
+ * and the sink's share *sink_w.  Returns the number of allowed keys, or -1 on
+ * inconsistent lengths.  Writes q into qbuf (head_size doubles).
+ */
+static long row_weights(const ref_desc *d, const ref_inputs *in, int b, int h, int i,
+                        double *w, double *sink_w, double *qbuf, seqinfo *s_out) {
+  seqinfo s;
+  if (seq_info(d, in, b, &s) != 0) return -1;
+  if (s_out) *s_out = s;
+  const int D = d->head_size;
+  const int G = d->q_heads / d->kv_heads;
+  const int g = h / G; /* R5 */
+  for (int c = 0; c < D; ++c) {
+    double x = elem(in->q, d->dtype, q_index(d, b, h, i, c));
+    /* MHA projection bias: the query segment is added to q (R11). */
+    if (d->op == REF_MHA && in->proj_bias) x += elem(in->proj_bias, d->dtype, (size_t)h * D + c);
+    qbuf[c] = x;
+  }
+  const double scale = scale_of(d);
+  const long pos = s.q_off + i;
+  const long T = (long)d->past_seq + d->kv_seq;
+  long n_allowed = 0;
+  double m = -INFINITY;
+  unsigned char *ok = (unsigned char *)malloc((size_t)s.total_b + 1);
+  for (long j = 0; j < s.total_b; ++j) {
+    int allowed = j < s.valid_b;
+    if (d->causal && j > pos) allowed = 0;
+    if (d->window > 0 && j < pos - d->window + 1) allowed = 0;
+    ok[j] = (unsigned char)allowed;
+    if (!allowed) { w[j] = 0.0; continue; }
+    double dot = 0.0;
+    for (int c = 0; c < D; ++c) dot += qbuf[c] * key_elem(d, in, &s, b, g, j, c, 0);
+    double sc = dot * scale;
+    if (in->bias) {
+      size_t bb = d->bias_b > 1 ? (size_t)b : 0, bh = d->bias_h > 1 ? (size_t)h : 0;
+      sc += elem(in->bias, d->dtype, ((bb * d->bias_h + bh) * d->q_seq + i) * (size_t)T + j);
+    }
+    if (d->softcap > 0.0f) sc = (double)d->softcap * tanh(sc / (double)d->softcap);
+    if (d->op == REF_MHA && j >= s.pad_b) sc += (double)d->mask_filter_value;
+    w[j] = sc;
+    if (sc > m) m = sc;
+    ++n_allowed;
+  }
+  *sink_w = 0.0;
+  if (n_allowed == 0) { /* R10 */
+    free(ok);
+    return 0;
+  }
+  double z = 0.0;
+  int has_sink = in->sink != NULL;
+  if (has_sink) {
+    z = elem(in->sink, d->dtype, (size_t)h); /* R7: raw logit */
+    if (z > m) m = z;
+  }
+  double den = has_sink ? exp(z - m) : 0.0;
+  for (long j = 0; j < s.total_b; ++j) {
+    if (!ok[j]) continue;
+    w[j] = exp(w[j] - m);
+    den += w[j];
+  }
+  for (long j = 0; j < s.total_b; ++j) w[j] /= den;
+  if (has_sink) *sink_w = exp(z - m) / den;
+  free(ok);
+  return n_allowed;
+}
+
+static int check_desc(const ref_desc *d, const ref_inputs *in) {
+  if (!d || !in || !in->q || !in->k || !in->v) return -1;
+  if (d->q_heads <= 0 || d->kv_heads <= 0 || d->q_heads % d->kv_heads) return -1;
+  if (d->head_size <= 0 || d->v_head_size <= 0 || d->batch < 0 || d->q_seq < 0) return -1;
+  if (d->op == REF_GQA && (!in->lens || d->kv_seq != d->q_seq)) return -1;
+  if (d->past_seq > 0 && (!in->past_k || !in->past_v)) return -1;
+  return 0;
+}
+
+static int one_row(const ref_desc *d, const ref_inputs *in, int b, int h, int i,
+                   double *out, double *w, double *qbuf) {
+  seqinfo s;
+  double sink_w;
+  long n = row_weights(d, in, b, h, i, w, &sink_w, qbuf, &s);
+  if (n < 0) return -1;
+  const int G = d->q_heads / d->kv_heads, g = h / G;
+  for (int c = 0; c < d->v_head_size; ++c) out[c] = 0.0;
+  if (n == 0) return 0;
+  for (long j = 0; j < s.total_b; ++j) {
+    if (w[j] == 0.0) continue; /* excluded key, or a weight that underflowed */
+    for (int c = 0; c < d->v_head_size; ++c)
+      out[c] += w[j] * key_elem(d, in, &s, b, g, j, c, 1);
+  }
+  return 0;
+}
+
+static long max_keys(const ref_desc *d) { return (long)d->past_seq + d->kv_seq + 1; }
+
+/* Y for every row, float64, logical order (B, S, Hq, Dv). */
+int olk_ref_attention(const ref_desc *d, const ref_inputs *in, double *y, int threads) {
+  if (check_desc(d, in) != 0 || !y) return -1;
+  const long rows = (long)d->batch * d->q_seq * d->q_heads;
+  int err = 0;
+#ifdef _OPENMP
+  if (threads > 0) omp_set_num_threads(threads);
+#endif
+#pragma omp parallel reduction(|| : err)
+  {
+    double *w = (double *)malloc(sizeof(double) * (size_t)max_keys(d));
+    double *qbuf = (double *)malloc(sizeof(double) * (size_t)d->head_size);
+#pragma omp for schedule(dynamic, 4)
+    for (long r = 0; r < rows; ++r) {
+      int h = (int)(r % d->q_heads);
+      int i = (int)((r / d->q_heads) % d->q_seq);
+      int b = (int)(r / ((long)d->q_heads * d->q_seq));
+      if (one_row(d, in, b, h, i, y + (size_t)r * d->v_head_size, w, qbuf)) err = 1;
+    }
+    free(w);
+    free(qbuf);
+  }
+  return err ? -1 : 0;
+}
+
+/* Y for selected rows: rows[3*r .. 3*r+2] = (b, h, i); out is (nrows, Dv). */
+int olk_ref_attention_rows(const ref_desc *d, const ref_inputs *in, const int32_t *rows,
+                           long nrows, double *out, int threads) {
+  if (check_desc(d, in) != 0 || !rows || !out) return -1;
+  int err = 0;
+#ifdef _OPENMP
+  if (threads > 0) omp_set_num_threads(threads);
+#endif
+#pragma omp parallel reduction(|| : err)
+  {
+    double *w = (double *)malloc(sizeof(double) * (size_t)max_keys(d));
+    double *qbuf = (double *)malloc(sizeof(double) * (size_t)d->head_size);
+#pragma omp for schedule(dynamic, 1)
+    for (long r = 0; r < nrows; ++r) {
+      int b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
+      if (b < 0 || b >= d->batch || h < 0 || h >= d->q_heads || i < 0 || i >= d->q_seq) { err = 1; continue; }
+      if (one_row(d, in, b, h, i, out + (size_t)r * d->v_head_size, w, qbuf)) err = 1;
+    }
+    free(w);
+    free(qbuf);
+  }
+  return err ? -1 : 0;
+}
+
+/* Softmax weights of one row: w has room for P+L+1 doubles.  Returns the
+ * number of keys of the row's concatenated sequence (total_b), or -1. */
+long olk_ref_row_weights(const ref_desc *d, const ref_inputs *in, int b, int h, int i,
+                         double *w, double *sink_w) {
+  if (check_desc(d, in) != 0) return -1;
+  double *qbuf = (double *)malloc(sizeof(double) * (size_t)d->head_size);
+  seqinfo s;
+  long n = row_weights(d, in, b, h, i, w, sink_w, qbuf, &s);
+  free(qbuf);
+  return n < 0 ? -1 : s.total_b;
+}
+
+/* present_key / present_value (B, Hkv, P+L, D|Dv): position j < total_b holds
+ * the past prefix followed by the current step, copied bit for bit; positions
+ * at or beyond total_b are left as they are. */
+int olk_ref_present(const ref_desc *d, const ref_inputs *in, void *pk, void *pv) {
+  if (check_desc(d, in) != 0) return -1;
+  const size_t es = esize(d->dtype);
+  const long Tp = (long)d->past_seq + d->kv_seq;
+  for (int b = 0; b < d->batch; ++b) {
+    seqinfo s;
+    if (seq_info(d, in, b, &s) != 0) return -1;
+    for (int g = 0; g < d->kv_heads; ++g) {
+      for (int which = 0; which < 2; ++which) {
+        void *dst = which ? pv : pk;
+        if (!dst) continue;
+        int width = which ? d->v_head_size : d->head_size;
+        const void *past = which ? in->past_v : in->past_k;
+        const void *cur = which ? in->v : in->k;
+        for (long j = 0; j < s.total_b && j < Tp; ++j) {
+          const char *src;
+          if (j < s.past_b) src = (const char *)past + past_index(d, b, g, (int)j, 0, width) * es;
+          else src = (const char *)cur + new_kv_index(d, b, g, (int)(j - s.past_b), 0, width) * es;
+          char *o = (char *)dst + ((((size_t)b * d->kv_heads + g) * Tp + j) * width) * es;
+          memcpy(o, src, (size_t)width * es);
+        }
+      }
+    }
+  }
+  return 0;
+}

@@ -1,0 +1,456 @@
+"""Pins of the oracle against what the operator pages and the mathematics fix.
+
+Every test here runs on the CPU.  None re-types the oracle's loops: each checks
+an invariant, a closed form, a worked statement of the pages, or agreement with
+a library routine (torch's scaled_dot_product_attention in float64).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import olk_ref
+from transformer_attention_fwd_amd.workloads import Problem, make_inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _f64(t):
+    return t.to(torch.float64)
+
+
+# ---------------------------------------------------------------------------
+# Library-routine pin: torch SDPA (float64, CPU) on explicitly concatenated,
+# head-expanded tensors, with the masks built as a float additive mask.
+# ---------------------------------------------------------------------------
+
+def _bnsh_q(p, q):
+    q = _f64(q)
+    return q.view(p.B, p.S, p.Hq, p.D).permute(0, 2, 1, 3) if p.q_rank == 3 else q
+
+
+def _bnsh_kv(p, t, width):
+    t = _f64(t)
+    return t.view(p.B, p.L, p.Hkv, width).permute(0, 2, 1, 3) if p.kv_rank == 3 else t
+
+
+def sdpa_reference(p: Problem, inp) -> np.ndarray:
+    """(B, S, Hq, Dv) via torch SDPA; no sink, no softcap."""
+    assert not p.has_sink and p.softcap == 0.0
+    q = _bnsh_q(p, inp["q"])
+    if p.op == "mha" and "proj_bias" in inp:
+        q = q + _f64(inp["proj_bias"][: p.Hq * p.D]).view(1, p.Hq, 1, p.D)
+    kn = _bnsh_kv(p, inp["k"], p.D)
+    vn = _bnsh_kv(p, inp["v"], p.Dv)
+    G = p.Hq // p.Hkv
+    # an explicit scale attribute is a float32 value
+    scale = float(np.float32(p.scale)) if p.scale is not None else 1.0 / math.sqrt(p.D)
+    out = np.zeros((p.B, p.S, p.Hq, p.Dv))
+    lens = inp.get("lens")
+    for b in range(p.B):
+        if p.op == "gqa":
+            total = int(lens[b]) + 1
+            past = total - p.S
+        else:
+            past = p.P
+            total = p.P + p.L
+        parts_k, parts_v = [], []
+        if past > 0:
+            parts_k.append(_f64(inp["past_k"][b, :, :past]))
+            parts_v.append(_f64(inp["past_v"][b, :, :past]))
+        parts_k.append(kn[b])
+        parts_v.append(vn[b])
+        K = torch.cat(parts_k, dim=1)[:, :total].repeat_interleave(G, dim=0)
+        V = torch.cat(parts_v, dim=1)[:, :total].repeat_interleave(G, dim=0)
+        mask = torch.zeros(p.Hq, p.S, total, dtype=torch.float64)
+        pos = (past if p.op == "gqa" else total - p.S) + torch.arange(p.S).view(-1, 1)
+        j = torch.arange(total).view(1, -1)
+        if p.causal:
+            mask = mask.masked_fill((j > pos).unsqueeze(0), float("-inf"))
+        if p.op == "attention" and lens is not None:
+            mask[..., int(lens[b]):] = float("-inf")
+        if p.op == "mha" and lens is not None:
+            mask[..., int(lens[b]):] += p.mask_filter_value
+        if "bias" in inp:
+            bb, bh = p.bias_bh
+            bias = _f64(inp["bias"][b if bb > 1 else 0])[..., :total]
+            mask = mask + (bias if bh > 1 else bias.expand(p.Hq, -1, -1))
+        y = torch.nn.functional.scaled_dot_product_attention(
+            q[b:b + 1], K.unsqueeze(0), V.unsqueeze(0), attn_mask=mask.unsqueeze(0),
+            scale=scale)
+        out[b] = y[0].permute(1, 0, 2).numpy()
+    return out
+
+
+SDPA_CASES = [
+    Problem(op="gqa", dtype="f32", B=2, S=7, L=7, P=0, Hq=4, Hkv=2, D=8, Dv=8, causal=1),
+    Problem(op="gqa", dtype="bf16", B=2, S=5, L=5, P=9, Hq=6, Hkv=2, D=16, Dv=16,
+            causal=1, lens_range=(0, 9)),
+    Problem(op="gqa", dtype="f16", B=3, S=1, L=1, P=12, Hq=4, Hkv=1, D=8, Dv=8,
+            causal=1, lens_range=(1, 12)),
+    Problem(op="gqa", dtype="f32", B=1, S=6, L=6, P=0, Hq=2, Hkv=2, D=4, Dv=4, causal=0),
+    Problem(op="mha", dtype="f16", B=2, S=5, L=9, P=0, Hq=3, Hkv=3, D=8, Dv=8, kv_rank=4,
+            causal=0, bias_bh=(1, 3), has_lens=True, lens_range=(3, 9), has_proj_bias=True),
+    Problem(op="mha", dtype="f32", B=2, S=4, L=4, P=3, Hq=2, Hkv=2, D=8, Dv=6, kv_rank=3,
+            causal=1, bias_bh=(2, 1), has_lens=False),
+    Problem(op="attention", dtype="f32", B=2, S=5, L=5, P=4, Hq=4, Hkv=2, D=8, Dv=8,
+            kv_rank=3, causal=1, has_lens=True, lens_range=(2, 9), bias_bh=(2, 4)),
+    Problem(op="attention", dtype="bf16", B=1, S=3, L=6, P=0, Hq=2, Hkv=1, D=8, Dv=4,
+            q_rank=4, kv_rank=4, causal=0, has_lens=False, scale=0.3),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(SDPA_CASES)))
+def test_oracle_matches_torch_sdpa(idx):
+    p = SDPA_CASES[idx]
+    inp = make_inputs(p, 100 + idx)
+    ref = sdpa_reference(p, inp)
+    got = olk_ref.attention(p, inp)
+    np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Invariants fixed by the pages.
+# ---------------------------------------------------------------------------
+
+def _rows(p):
+    for b in range(p.B):
+        for h in range(p.Hq):
+            for i in range(p.S):
+                yield b, h, i
+
+
+@pytest.mark.parametrize("p", [
+    Problem(op="gqa", dtype="f32", B=2, S=6, L=6, P=5, Hq=4, Hkv=2, D=8, Dv=8, causal=1,
+            window=3, softcap=2.0, lens_range=(0, 5)),
+    Problem(op="mha", dtype="f16", B=1, S=4, L=7, Hq=2, Hkv=2, D=8, Dv=8, kv_rank=4,
+            causal=0, bias_bh=(1, 2), has_lens=True, lens_range=(2, 7)),
+    Problem(op="attention", dtype="bf16", B=1, S=5, L=5, Hq=2, Hkv=1, D=8, Dv=8, causal=1,
+            softcap=0.5),
+])
+def test_rows_sum_to_one_without_sink(p):
+    inp = make_inputs(p, 7)
+    for b, h, i in _rows(p):
+        w, sw = olk_ref.row_weights(p, inp, b, h, i)
+        assert sw == 0.0
+        assert abs(w.sum() - 1.0) < 1e-12
+        assert (w >= 0).all()
+
+
+def test_sink_only_lowers_the_sum():
+    p = Problem(op="gqa", dtype="f32", B=1, S=6, L=6, Hq=2, Hkv=1, D=8, Dv=8, causal=1,
+                has_sink=True)
+    inp = make_inputs(p, 11)
+    prev = None
+    for z in (-3.0, -1.0, 0.0, 0.5, 2.0, 5.0):
+        inp["sink"] = torch.full((p.Hq,), z, dtype=torch.float32)
+        w, sw = olk_ref.row_weights(p, inp, 0, 1, 4)
+        assert w.sum() < 1.0
+        assert abs(w.sum() + sw - 1.0) < 1e-12
+        if prev is not None:
+            assert w.sum() < prev  # strictly decreasing as the sink logit grows
+        prev = w.sum()
+    # a sink at -inf-like logit is the ordinary normalization
+    inp_far = dict(inp, sink=torch.full((p.Hq,), -1e4, dtype=torch.float32))
+    inp_none = {k: v for k, v in inp.items() if k != "sink"}
+    np.testing.assert_array_equal(olk_ref.attention(p, inp_far),
+                                  olk_ref.attention(p.with_(has_sink=False), inp_none))
+
+
+def test_window_minus_one_equals_full_causal_and_large_window():
+    p = Problem(op="gqa", dtype="bf16", B=2, S=9, L=9, P=6, Hq=4, Hkv=2, D=8, Dv=8,
+                causal=1, window=-1, lens_range=(0, 6))
+    inp = make_inputs(p, 3)
+    full = olk_ref.attention(p, inp)
+    for w in (p.P + p.S, p.P + p.S + 5, 1 << 30):
+        np.testing.assert_array_equal(full, olk_ref.attention(p.with_(window=w), inp))
+    # a window shorter than the history changes late rows
+    assert not np.array_equal(full, olk_ref.attention(p.with_(window=3), inp))
+
+
+def test_window_one_returns_value_at_current_position():
+    p = Problem(op="gqa", dtype="f32", B=2, S=5, L=5, P=4, Hq=2, Hkv=1, D=8, Dv=8,
+                causal=1, window=1, softcap=3.0, lens_range=(0, 4))
+    inp = make_inputs(p, 5)
+    y = olk_ref.attention(p, inp)
+    lens = inp["lens"].numpy()
+    for b in range(p.B):
+        past = int(lens[b]) + 1 - p.S
+        for i in range(p.S):
+            vi = inp["v"][b, i].view(p.Hkv, p.Dv)
+            for h in range(p.Hq):
+                np.testing.assert_array_equal(y[b, i, h], vi[h // 2].double().numpy())
+        assert past >= 0
+
+
+@pytest.mark.parametrize("p", [
+    Problem(op="gqa", dtype="f32", B=1, S=7, L=7, P=3, Hq=4, Hkv=2, D=8, Dv=8, causal=1,
+            window=2, softcap=1.0, lens_range=(0, 3)),
+    Problem(op="mha", dtype="f32", B=2, S=4, L=6, Hq=2, Hkv=2, D=8, Dv=8, kv_rank=4,
+            causal=0, bias_bh=(2, 2), has_lens=True, lens_range=(0, 6),
+            has_proj_bias=True),
+])
+def test_constant_value_passes_through(p):
+    inp = make_inputs(p, 9)
+    c = 0.625
+    inp["v"] = torch.full_like(inp["v"], c)
+    if "past_v" in inp:
+        inp["past_v"] = torch.full_like(inp["past_v"], c)
+    y = olk_ref.attention(p, inp)
+    np.testing.assert_allclose(y, c, rtol=1e-14, atol=0)
+
+
+@pytest.mark.parametrize("p", [
+    Problem(op="gqa", dtype="bf16", B=3, S=4, L=4, P=6, Hq=4, Hkv=2, D=8, Dv=8, causal=1,
+            lens_range=(0, 6)),
+    Problem(op="mha", dtype="f16", B=2, S=3, L=5, P=4, Hq=2, Hkv=2, D=8, Dv=4, kv_rank=4,
+            causal=0, has_lens=False),
+    Problem(op="attention", dtype="f32", B=2, S=2, L=3, P=2, Hq=2, Hkv=2, D=4, Dv=4,
+            kv_rank=3, causal=1, has_lens=False),
+])
+def test_present_is_concat_of_past_and_new(p):
+    inp = make_inputs(p, 13)
+    pk, pv = olk_ref.present(p, inp)
+    lens = inp.get("lens")
+    for b in range(p.B):
+        past = int(lens[b]) + 1 - p.S if p.op == "gqa" else p.P
+        for name, pres, width in (("k", pk, p.D), ("v", pv, p.Dv)):
+            new = inp[name][b]
+            new = new.view(p.L, p.Hkv, width).transpose(0, 1) if p.kv_rank == 3 else new
+            parts = [new]
+            if past > 0:
+                parts.insert(0, inp["past_" + name][b, :, :past])
+            want = torch.cat(parts, dim=1)
+            got = pres[b, :, : past + p.L]
+            assert torch.equal(got.view(torch.int16 if got.element_size() == 2 else torch.int32),
+                               want.view(torch.int16 if want.element_size() == 2 else torch.int32))
+            # positions beyond the batch's total length are left untouched
+            assert torch.isnan(pres[b, :, past + p.L:].float()).all()
+
+
+def test_masked_and_padded_keys_are_irrelevant():
+    # GQA: cache slots beyond the valid past, and keys outside the window.
+    p = Problem(op="gqa", dtype="f16", B=2, S=3, L=3, P=10, Hq=4, Hkv=2, D=8, Dv=8,
+                causal=1, window=4, lens_range=(2, 8))
+    inp = make_inputs(p, 17)
+    y0 = olk_ref.attention(p, inp)
+    lens = inp["lens"].numpy()
+    for b in range(p.B):
+        past = int(lens[b]) + 1 - p.S
+        inp["past_k"][b, :, past:] = float("nan")
+        inp["past_v"][b, :, past:] = float("nan")
+        # keys older than the earliest window start of query 0
+        far = max(0, past - 4 + 1)
+        inp["past_k"][b, :, :far] = float("nan")
+        inp["past_v"][b, :, :far] = float("nan")
+    np.testing.assert_array_equal(y0, olk_ref.attention(p, inp))
+    # Attention: keys at or beyond nonpad_kv_seqlen
+    pa = Problem(op="attention", dtype="f32", B=2, S=4, L=8, Hq=2, Hkv=2, D=8, Dv=8,
+                 causal=0, has_lens=True, lens_range=(1, 8))
+    ia = make_inputs(pa, 19)
+    ya = olk_ref.attention(pa, ia)
+    for b in range(pa.B):
+        n = int(ia["lens"][b])
+        ia["k"][b, n:] = float("nan")
+        ia["v"][b, n:] = float("nan")
+    np.testing.assert_array_equal(ya, olk_ref.attention(pa, ia))
+
+
+def test_rank4_mha_ignores_kv_projection_bias():
+    p = Problem(op="mha", dtype="f32", B=1, S=3, L=5, Hq=2, Hkv=2, D=4, Dv=4, kv_rank=4,
+                causal=0, has_lens=False, has_proj_bias=True)
+    inp = make_inputs(p, 23)
+    y0 = olk_ref.attention(p, inp)
+    pb = inp["proj_bias"].clone()
+    pb[p.Hq * p.D:] = 7.0
+    np.testing.assert_array_equal(y0, olk_ref.attention(p, dict(inp, proj_bias=pb)))
+    pb2 = inp["proj_bias"].clone()
+    pb2[0] += 1.0  # the query segment does matter
+    assert not np.array_equal(y0, olk_ref.attention(p, dict(inp, proj_bias=pb2)))
+
+
+def test_attention_to_gqa_fusion_is_result_preserving():
+    # Rank-3 Attention with q_heads != kv_heads and no past equals GQA with
+    # seqlens_k derived from the key length.
+    pa = Problem(op="attention", dtype="f32", B=2, S=6, L=6, Hq=4, Hkv=2, D=8, Dv=8,
+                 causal=1, has_lens=False, scale=0.4)
+    inp = make_inputs(pa, 29)
+    ya = olk_ref.attention(pa, inp)
+    pg = pa.with_(op="gqa", has_lens=True)
+    ig = dict(inp, lens=torch.full((pa.B,), pa.L - 1, dtype=torch.int32))
+    np.testing.assert_array_equal(ya, olk_ref.attention(pg, ig))
+
+
+def test_gqa_with_equal_heads_equals_mha():
+    pg = Problem(op="gqa", dtype="f16", B=2, S=5, L=5, Hq=3, Hkv=3, D=8, Dv=8, causal=1)
+    inp = make_inputs(pg, 31)
+    pm = pg.with_(op="mha", has_lens=False)
+    im = {k: v for k, v in inp.items() if k != "lens"}
+    np.testing.assert_array_equal(olk_ref.attention(pg, inp), olk_ref.attention(pm, im))
+
+
+def test_scale_folds_into_query_and_default_is_inverse_sqrt():
+    p = Problem(op="gqa", dtype="f32", B=1, S=5, L=5, Hq=2, Hkv=1, D=16, Dv=16, causal=1,
+                scale=0.5)
+    inp = make_inputs(p, 37)
+    y = olk_ref.attention(p, inp)
+    y2 = olk_ref.attention(p.with_(scale=1.0), dict(inp, q=inp["q"] * 0.5))
+    np.testing.assert_allclose(y, y2, rtol=1e-14, atol=1e-15)
+    # default scale 1/sqrt(D): D=16 gives exactly 0.25
+    np.testing.assert_array_equal(olk_ref.attention(p.with_(scale=None), inp),
+                                  olk_ref.attention(p.with_(scale=0.25), inp))
+
+
+def test_batches_are_independent():
+    p = Problem(op="gqa", dtype="bf16", B=3, S=4, L=4, P=5, Hq=2, Hkv=1, D=8, Dv=8,
+                causal=1, lens_range=(0, 5))
+    inp = make_inputs(p, 41)
+    y = olk_ref.attention(p, inp)
+    perm = [2, 0, 1]
+    ip = {k: v[perm] for k, v in inp.items()}
+    np.testing.assert_array_equal(olk_ref.attention(p, ip), y[perm])
+
+
+def test_rank4_query_is_the_transposed_rank3_query():
+    p3 = Problem(op="attention", dtype="f32", B=2, S=4, L=5, Hq=2, Hkv=1, D=4, Dv=4,
+                 causal=1, has_lens=False)
+    inp = make_inputs(p3, 43)
+    p4 = p3.with_(q_rank=4)
+    q4 = inp["q"].view(2, 4, 2, 4).permute(0, 2, 1, 3).contiguous()
+    np.testing.assert_array_equal(olk_ref.attention(p3, inp),
+                                  olk_ref.attention(p4, dict(inp, q=q4)))
+
+
+# ---------------------------------------------------------------------------
+# Closed forms.
+# ---------------------------------------------------------------------------
+
+def test_zero_query_gives_mean_of_allowed_values():
+    p = Problem(op="gqa", dtype="f32", B=1, S=6, L=6, P=4, Hq=2, Hkv=1, D=8, Dv=8,
+                causal=1, window=3, lens_range=(4, 4), has_sink=True)
+    inp = make_inputs(p, 47)
+    inp["q"].zero_()
+    z = inp["sink"].double().numpy()
+    y = olk_ref.attention(p, inp)
+    past = 4
+    keys_v = torch.cat([inp["past_v"][0, 0], inp["v"][0].view(6, 1, 8)[:, 0]]).double()
+    for i in range(p.S):
+        pos = past + i
+        lo = max(0, pos - 3 + 1)
+        n = pos - lo + 1
+        mean = keys_v[lo:pos + 1].mean(0).numpy()
+        for h in range(p.Hq):
+            want = n / (n + math.exp(z[h])) * mean
+            np.testing.assert_allclose(y[0, i, h], want, rtol=1e-12, atol=1e-14)
+
+
+def test_first_causal_row_with_sink_is_logistic():
+    p = Problem(op="gqa", dtype="f32", B=1, S=4, L=4, Hq=2, Hkv=2, D=8, Dv=8, causal=1,
+                has_sink=True)
+    inp = make_inputs(p, 53)
+    y = olk_ref.attention(p, inp)
+    q = inp["q"][0, 0].view(2, 8).double()
+    k0 = inp["k"][0, 0].view(2, 8).double()
+    v0 = inp["v"][0, 0].view(2, 8).double()
+    for h in range(2):
+        s = float(q[h] @ k0[h]) / math.sqrt(8)
+        z = float(inp["sink"][h])
+        frac = 1.0 / (1.0 + math.exp(z - s))
+        np.testing.assert_allclose(y[0, 0, h], frac * v0[h].numpy(), rtol=1e-12)
+
+
+def test_two_keys_weights_are_sigmoid_of_score_difference():
+    p = Problem(op="mha", dtype="f32", B=1, S=1, L=2, Hq=1, Hkv=1, D=8, Dv=8, kv_rank=4,
+                causal=0, has_lens=False, scale=0.7)
+    inp = make_inputs(p, 59)
+    w, _ = olk_ref.row_weights(p, inp, 0, 0, 0)
+    q = inp["q"][0, 0].double()
+    k = inp["k"][0, 0].double()
+    s = (k @ q).numpy() * np.float64(np.float32(0.7))
+    np.testing.assert_allclose(w[0], 1.0 / (1.0 + math.exp(s[1] - s[0])), rtol=1e-13)
+
+
+def test_softcap_bounds_and_saturation():
+    # With a tiny cap every large score saturates to +-cap, so the weights take
+    # the closed form exp(+-cap) / sum.
+    p = Problem(op="attention", dtype="f32", B=1, S=1, L=6, Hq=1, Hkv=1, D=4, Dv=4,
+                causal=0, has_lens=False, softcap=0.5, scale=1.0)
+    inp = make_inputs(p, 61)
+    inp["q"] = torch.tensor([[[100.0, 0.0, 0.0, 0.0]]])
+    signs = np.array([1, -1, 1, 1, -1, 1], dtype=np.float64)
+    k = torch.zeros(1, 6, 4)
+    k[0, :, 0] = torch.tensor(signs * 3.0, dtype=torch.float32)
+    inp["k"] = k
+    w, _ = olk_ref.row_weights(p, inp, 0, 0, 0)
+    e = np.exp(0.5 * signs)
+    np.testing.assert_allclose(w, e / e.sum(), rtol=1e-12)
+    # any cap: weight ratios are bounded by exp(2 * cap)
+    p2 = p.with_(softcap=0.8, scale=None)
+    inp2 = make_inputs(p2, 67)
+    w2, _ = olk_ref.row_weights(p2, inp2, 0, 0, 0)
+    assert w2.max() / w2.min() <= math.exp(1.6) + 1e-12
+    # a very large cap is the uncapped softmax
+    p3 = p.with_(softcap=1e9, scale=None)
+    np.testing.assert_allclose(olk_ref.attention(p3, inp2),
+                               olk_ref.attention(p3.with_(softcap=0.0), inp2), rtol=1e-12)
+
+
+def test_mha_mask_filter_value_is_additive():
+    p = Problem(op="mha", dtype="f32", B=2, S=3, L=7, Hq=2, Hkv=2, D=8, Dv=8, kv_rank=4,
+                causal=0, has_lens=True, lens_range=(2, 6))
+    inp = make_inputs(p, 71)
+    y = olk_ref.attention(p, inp)
+    # -10000 underflows: equals excluding the padded keys (Attention non-pad)
+    ya = olk_ref.attention(p.with_(op="attention"), inp)
+    np.testing.assert_allclose(y, ya, rtol=1e-13, atol=1e-15)
+    # a zero filter value makes the padding a no-op
+    y0 = olk_ref.attention(p.with_(mask_filter_value=0.0), inp)
+    np.testing.assert_allclose(y0, olk_ref.attention(p.with_(has_lens=False),
+                                                     {k: v for k, v in inp.items()
+                                                      if k != "lens"}), rtol=1e-13)
+    # a padded-everything batch is a uniform shift: same as no padding
+    inp0 = dict(inp, lens=torch.zeros(2, dtype=torch.int32))
+    np.testing.assert_allclose(olk_ref.attention(p, inp0), y0, rtol=1e-10)
+
+
+def test_row_without_allowed_keys_is_zero():
+    p = Problem(op="attention", dtype="f32", B=1, S=2, L=3, Hq=1, Hkv=1, D=4, Dv=4,
+                causal=0, has_lens=True)
+    inp = make_inputs(p, 73, lens=np.array([0]))
+    np.testing.assert_array_equal(olk_ref.attention(p, inp), 0.0)
+
+
+def test_half_and_bfloat16_inputs_are_read_exactly():
+    # the oracle's element decoding against torch's exact upcast
+    for dt in ("f16", "bf16"):
+        p = Problem(op="mha", dtype=dt, B=1, S=1, L=1, Hq=1, Hkv=1, D=4, Dv=4,
+                    kv_rank=4, causal=0, has_lens=False)
+        inp = make_inputs(p, 79)
+        vals = torch.tensor([0.0, -0.0, 6.1e-5, 3.0e-6, -65504.0, 1.5, -2.75, 1e-7, 3e38],
+                            dtype=torch.float32).to(p.torch_dtype)
+        for x in vals:
+            # one key: Y equals V exactly
+            iv = dict(inp, v=torch.full_like(inp["v"], float(x)))
+            y = olk_ref.attention(p, iv)
+            assert np.all(y == float(x.double())), (dt, float(x))
+
+
+# ---------------------------------------------------------------------------
+# Worked statement of the pages (golden fixture).
+# ---------------------------------------------------------------------------
+
+def test_window_2048_attends_current_and_2047_preceding():
+    with open(os.path.join(GOLDEN, "window_2048.json")) as f:
+        g = json.load(f)
+    W = g["local_window_size"]
+    p = Problem(op="gqa", dtype="f32", B=1, S=g["seq_len"], L=g["seq_len"], Hq=1, Hkv=1,
+                D=4, Dv=4, causal=1, window=W)
+    inp = make_inputs(p, 83)
+    for case in g["rows"]:
+        w, _ = olk_ref.row_weights(p, inp, 0, 0, case["query"])
+        nz = np.nonzero(w)[0]
+        assert len(nz) == case["attended"]
+        assert nz[0] == case["first_key"] and nz[-1] == case["last_key"]
