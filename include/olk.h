@@ -1,0 +1,165 @@
+/*
+ * olk.h — C ABI of the MI355X (gfx950) attention-forward library libolk.so.
+ *
+ * One computation, three operator contracts:
+ *
+ *   Y = Softmax((Q @ K^T) * scale + bias) @ V
+ *
+ * - com.microsoft::GroupQueryAttention (onnx-light-cpu Python API page
+ *   "Custom operators", section "Microsoft GroupQueryAttention"): grouped KV
+ *   heads, causal and local_window_size masking, head_sink virtual logits,
+ *   seqlens_k, present = past cache followed by the current step;
+ * - com.microsoft::MultiHeadAttention (same page, section "Microsoft
+ *   MultiHeadAttention"): rank-3 or rank-4 (cross-attention) K/V, projection
+ *   bias, int32 key-padding lengths with mask_filter_value, additive bias;
+ * - ai.onnx::Attention (onnx-light reference kernels header page,
+ *   "class Attention", its Attributes and Result structs): scale, is_causal,
+ *   softcap, grouped heads, past/present concatenation, non-padding lengths.
+ *
+ * Conventions shared by every entry point
+ * - Ownership: the caller owns every buffer (inputs, outputs, workspace).  The
+ *   library allocates no device memory and keeps no pointer after a call
+ *   returns.  NULL means "absent" for optional tensors (as the comprehensive
+ *   Attention overload takes nullptr for absent inputs).
+ * - Memory: every tensor pointer is a device pointer on the current HIP
+ *   device, row-major and densely packed in the layout stated at its field.
+ *   Element type of every floating tensor is desc->dtype; lengths are int32.
+ * - Asynchrony: launches go to `stream` (a hipStream_t; NULL = the null
+ *   stream).  Outputs are valid after the stream has synchronised.  Lengths
+ *   stay on the device: no call synchronises with the host.
+ * - Errors: every check happens on the host before any launch and returns a
+ *   status; nothing is launched when a check fails.  Unsupported
+ *   representations are rejected, not reinterpreted.  Device lengths that are
+ *   out of range are clamped (memory-safe; values then unspecified).  There is
+ *   no CPU fallback.
+ * - Aliasing: outputs must not overlap inputs, except in kv_inplace mode (see
+ *   olk_attn_desc.kv_inplace).
+ * - Thread safety: reentrant; the only global state is the per-thread name of
+ *   the last kernel launched.
+ */
+#ifndef OLK_H
+#define OLK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  OLK_OK = 0,
+  OLK_E_NULL = 1,        /* a required pointer is NULL */
+  OLK_E_ATTR = 2,        /* an attribute value the operator contract rejects */
+  OLK_E_SHAPE = 3,       /* inconsistent sizes or ranks */
+  OLK_E_UNSUPPORTED = 4, /* valid for the operator, not implemented here */
+  OLK_E_WORKSPACE = 5,   /* workspace missing or smaller than olk_workspace_bytes */
+  OLK_E_HIP = 6          /* a HIP launch failed */
+} olk_status;
+
+typedef enum { OLK_F32 = 0, OLK_F16 = 1, OLK_BF16 = 2 } olk_dtype;
+
+typedef enum { OLK_OP_GQA = 0, OLK_OP_MHA = 1, OLK_OP_ATTENTION = 2 } olk_op;
+
+/* Kernel family requested by the caller (diagnostics and tests). */
+typedef enum {
+  OLK_KERNEL_AUTO = 0,    /* the library picks */
+  OLK_KERNEL_GENERIC = 1, /* one-wave-per-row VALU kernel: any dtype, any head size <= 256 */
+  OLK_KERNEL_TILED = 2    /* MFMA tiled kernel (f16/bf16, head size 64 or 128) */
+} olk_kernel;
+
+/*
+ * Attributes and sizes of one call.
+ *  B = batch, S = q_seq, L = kv_seq (new keys), P = past_seq (past buffer
+ *  length), T = P + L (present length), Hq/Hkv = heads, D/Dv = head sizes.
+ */
+typedef struct {
+  int32_t op;                /* olk_op */
+  int32_t dtype;             /* olk_dtype: Q, K, V, past, bias, sink, proj_bias, Y, present */
+  int32_t batch;             /* B >= 0 */
+  int32_t q_seq;             /* S >= 0 */
+  int32_t kv_seq;            /* L >= 0; GroupQueryAttention requires L == S */
+  int32_t past_seq;          /* P >= 0; 0 = no past inputs */
+  int32_t q_num_heads;       /* Hq > 0 */
+  int32_t kv_num_heads;      /* Hkv > 0, Hq % Hkv == 0; MultiHeadAttention: Hkv == Hq */
+  int32_t head_size;         /* D */
+  int32_t v_head_size;       /* Dv */
+  int32_t q_rank;            /* 3: Q (B,S,Hq*D), Y (B,S,Hq*Dv); 4 (Attention only): Q (B,Hq,S,D), Y (B,Hq,S,Dv) */
+  int32_t kv_rank;           /* 3: K (B,L,Hkv*D), V (B,L,Hkv*Dv); 4 (MHA/Attention): K (B,Hkv,L,D), V (B,Hkv,L,Dv) */
+  int32_t causal;            /* 0/1: GQA causal, MHA unidirectional, Attention is_causal;
+                                bottom-right aligned (query i at position past_b + i) */
+  int32_t local_window_size; /* GroupQueryAttention only: -1 = full; W > 0 attends the
+                                current key and up to W-1 preceding; needs causal = 1 */
+  int32_t has_scale;         /* 0: scale = 1/sqrt(D) */
+  float scale;               /* used when has_scale != 0; must be finite */
+  float softcap;             /* > 0: s -> softcap*tanh(s/softcap) after the bias (GQA, Attention) */
+  float mask_filter_value;   /* MultiHeadAttention: added to scores of padded keys (default -10000) */
+  int32_t bias_b, bias_h;    /* attn_bias broadcast extents: 1 or B, 1 or Hq */
+  int32_t kv_inplace;        /* GroupQueryAttention only.  0: present = concat(past, new)
+                                written out of place.  1: present_k/v already hold the
+                                valid past at [0, past_b) (past_k/v NULL or equal to
+                                present_k/v); only the new positions are written. */
+  int32_t kernel;            /* olk_kernel */
+} olk_attn_desc;
+
+/* Device pointers (caller-owned); NULL = absent. */
+typedef struct {
+  const void *q;             /* required; see q_rank */
+  const void *k, *v;         /* required; see kv_rank */
+  const void *past_k;        /* (B,Hkv,P,D) or NULL */
+  const void *past_v;        /* (B,Hkv,P,Dv) or NULL */
+  const int32_t *seqlens;    /* (B) int32.  GQA: seqlens_k = total length - 1 (required);
+                                MHA: key-padding lengths; Attention: non-padding lengths */
+  const void *attn_bias;     /* (bias_b, bias_h, S, T) additive, or NULL */
+  const void *head_sink;     /* (Hq) GroupQueryAttention virtual logits, or NULL */
+  const void *proj_bias;     /* MultiHeadAttention (2*Hq*D + Hq*Dv) = [q | k | v], or NULL;
+                                with rank-4 K/V only the q segment applies */
+  void *y;                   /* required output; see q_rank */
+  void *present_k;           /* (B,Hkv,T,D) output, or NULL = not requested */
+  void *present_v;           /* (B,Hkv,T,Dv) output, or NULL = not requested */
+} olk_attn_io;
+
+/*
+ * Host-only check of desc and io (no GPU is touched).  Returns the status the
+ * compute entry points would return before launching.
+ */
+olk_status olk_validate(const olk_attn_desc *desc, const olk_attn_io *io);
+
+/*
+ * Bytes of workspace olk_attention_decode needs for this desc (0 when the
+ * call needs none).  Depends only on sizes, never on device data.
+ */
+size_t olk_workspace_bytes(const olk_attn_desc *desc);
+
+/*
+ * Attention forward, one pass over every query row (prefill and general
+ * shapes).  Computes Y and, when requested, present_key/present_value
+ * (onnx-light reference kernels header page, "class Attention", comprehensive
+ * overload and Result; GroupQueryAttention and MultiHeadAttention sections of
+ * the onnx-light-cpu Python API page).  Needs no workspace.
+ * `stream` is a hipStream_t.
+ */
+olk_status olk_attention_fwd(const olk_attn_desc *desc, const olk_attn_io *io, void *stream);
+
+/*
+ * Same result as olk_attention_fwd, computed split-KV for short query
+ * sequences against long key sequences (decode): the keys of each (batch, KV
+ * head) are cut into chunks whose partial softmax states are merged by a
+ * second kernel.  workspace: device memory of at least
+ * olk_workspace_bytes(desc) bytes, 16-byte aligned, owned by the caller; its
+ * contents on entry do not matter.  `stream` is a hipStream_t.
+ */
+olk_status olk_attention_decode(const olk_attn_desc *desc, const olk_attn_io *io,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static string naming a status. */
+const char *olk_status_str(olk_status status);
+
+/* Name of the last kernel this thread launched through the library ("" if none). */
+const char *olk_last_kernel_name(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OLK_H */

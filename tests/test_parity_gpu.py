@@ -1,0 +1,197 @@
+"""GPU parity: the HIP path through the C ABI against the oracle.
+
+Small problems are compared element by element over every output; the five
+full-size workloads are compared on sampled rows (in the launch configuration
+the benchmark times) and present_key/present_value bit for bit.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import olk_ref
+from tests.parity import (assert_close, assert_present_exact, check_rows, sample_rows,
+                          to_dev, y_logical)
+from transformer_attention_fwd_amd.workloads import (WORKLOAD_ORDER, WORKLOADS, Problem,
+                                                     make_inputs, workload)
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from transformer_attention_fwd_amd import olk
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# Small problems spanning every feature: several 64-key tiles plus ragged tails.
+SMALL = {
+    "gqa_causal_bf16": Problem(op="gqa", dtype="bf16", B=2, S=197, L=197, Hq=8, Hkv=2,
+                               D=128, Dv=128, causal=1),
+    "gqa_causal_f16_d64": Problem(op="gqa", dtype="f16", B=2, S=150, L=150, Hq=4, Hkv=4,
+                                  D=64, Dv=64, causal=1),
+    "gqa_window_sink_softcap_bf16": Problem(op="gqa", dtype="bf16", B=2, S=300, L=300, Hq=8,
+                                            Hkv=2, D=128, Dv=128, causal=1, window=70,
+                                            softcap=2.0, has_sink=True),
+    "gqa_past_f16": Problem(op="gqa", dtype="f16", B=3, S=37, L=37, P=200, Hq=8, Hkv=2, D=128,
+                            Dv=128, causal=1, lens_range=(0, 200)),
+    "gqa_decode_f16": Problem(op="gqa", dtype="f16", B=5, S=1, L=1, P=700, Hq=8, Hkv=2,
+                              D=128, Dv=128, causal=1, lens_range=(0, 700)),
+    "gqa_decode_sink_window_bf16": Problem(op="gqa", dtype="bf16", B=3, S=2, L=2, P=300,
+                                           Hq=4, Hkv=1, D=64, Dv=64, causal=1, window=100,
+                                           has_sink=True, lens_range=(50, 300)),
+    "gqa_noncausal_f32": Problem(op="gqa", dtype="f32", B=2, S=40, L=40, Hq=4, Hkv=2, D=32,
+                                 Dv=32, causal=0),
+    "gqa_softcap_small_f32": Problem(op="gqa", dtype="f32", B=1, S=50, L=50, Hq=2, Hkv=1,
+                                     D=48, Dv=48, causal=1, softcap=0.5, has_sink=True),
+    "mha_cross_f16": Problem(op="mha", dtype="f16", B=2, S=70, L=333, Hq=4, Hkv=4, D=64,
+                             Dv=64, kv_rank=4, causal=0, bias_bh=(1, 4), has_lens=True,
+                             lens_range=(100, 333), has_proj_bias=True),
+    "mha_self_bias_f32": Problem(op="mha", dtype="f32", B=2, S=33, L=33, P=20, Hq=3, Hkv=3,
+                                 D=40, Dv=24, kv_rank=3, causal=1, bias_bh=(2, 3),
+                                 has_lens=False),
+    "mha_small_filter_bf16": Problem(op="mha", dtype="bf16", B=2, S=20, L=90, Hq=2, Hkv=2,
+                                     D=64, Dv=64, kv_rank=4, causal=0, has_lens=True,
+                                     lens_range=(10, 60), mask_filter_value=-2.0),
+    "attention_rank4_bf16": Problem(op="attention", dtype="bf16", B=2, S=65, L=129, P=31,
+                                    Hq=4, Hkv=2, D=128, Dv=128, q_rank=4, kv_rank=4, causal=1,
+                                    has_lens=True, lens_range=(1, 160), bias_bh=(2, 4),
+                                    softcap=10.0),
+    "attention_dv_ne_d_f16": Problem(op="attention", dtype="f16", B=1, S=40, L=70, Hq=2,
+                                     Hkv=1, D=96, Dv=160, causal=0, has_lens=False,
+                                     scale=0.05),
+    "gqa_headsize256_f32": Problem(op="gqa", dtype="f32", B=1, S=20, L=20, Hq=2, Hkv=1,
+                                   D=256, Dv=256, causal=1),
+}
+
+
+def _run(p, dev, **kw):
+    c = olk.Call(p, dev, **kw)
+    c.launch()
+    torch.cuda.synchronize()
+    return c
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("mode,kernel", [("fwd", "generic"), ("fwd", "auto"),
+                                         ("decode", "auto")])
+def test_small_parity(name, mode, kernel):
+    p = SMALL[name]
+    inp = make_inputs(p, 500 + list(SMALL).index(name))
+    _say(f"[parity] {name} mode={mode} kernel={kernel}")
+    c = _run(p, to_dev(inp), mode=mode, kernel=kernel)
+    want = olk_ref.attention(p, inp)
+    assert_close(p, y_logical(p, c.y), want)
+    assert_present_exact(p, inp, c.present_k, c.present_v)
+
+
+@pytest.mark.parametrize("name", WORKLOAD_ORDER)
+def test_workload_parity(name):
+    p, inp = workload(name)
+    mode = "decode" if p.S == 1 else "fwd"
+    _say(f"[parity] workload {name} mode={mode}")
+    dev = to_dev(inp)
+    c = _run(p, dev, mode=mode)
+    _say(f"[parity] {name} kernel={olk.olk_last_kernel_name()}")
+    if p.B * p.S * p.Hq <= 4096:
+        assert_close(p, y_logical(p, c.y), olk_ref.attention(p, inp))
+    else:
+        check_rows(p, inp, c.y, sample_rows(p, 160, seed=1))
+    if p.op == "gqa":
+        assert_present_exact(p, inp, c.present_k, c.present_v)
+
+
+def test_decode_inplace_cache_append():
+    # present already holds the past (a KV cache): only the new step is written
+    p, inp = workload("gqa_decode_f16")
+    dev = to_dev(inp)
+    pk = dev["past_k"].new_empty((p.B, p.Hkv, p.P + 1, p.D))
+    pv = dev["past_v"].new_empty((p.B, p.Hkv, p.P + 1, p.Dv))
+    pk[:, :, : p.P] = dev.pop("past_k")
+    pv[:, :, : p.P] = dev.pop("past_v")
+    c = _run(p, dev, mode="decode", kv_inplace=True, present_k=pk, present_v=pv)
+    check_rows(p, inp, c.y, sample_rows(p, 128, seed=2))
+    assert_present_exact(p, inp, c.present_k, c.present_v)
+
+
+def test_fwd_equals_decode_and_is_deterministic():
+    p = SMALL["gqa_past_f16"]
+    inp = make_inputs(p, 77)
+    dev = to_dev(inp)
+    ys = []
+    for mode in ("fwd", "fwd", "decode", "decode"):
+        ys.append(_run(p, dev, mode=mode).y.clone())
+    assert torch.equal(ys[0], ys[1])
+    assert torch.equal(ys[2], ys[3])
+    np.testing.assert_allclose(y_logical(p, ys[0]), y_logical(p, ys[2]), atol=2e-2)
+
+
+def test_poisoned_padding_and_guard_bands():
+    # Cache slots beyond each batch's valid past hold NaN; outputs sit inside
+    # guard bands.  Y must stay finite and equal the clean run; nothing may be
+    # written outside the outputs or past each batch's total length.
+    p = SMALL["gqa_past_f16"]
+    inp = make_inputs(p, 91)
+    clean = _run(p, to_dev(inp)).y.clone()
+    lens = inp["lens"].numpy()
+    for b in range(p.B):
+        past = int(lens[b]) + 1 - p.S
+        inp["past_k"][b, :, past:] = float("nan")
+        inp["past_v"][b, :, past:] = float("nan")
+    dev = to_dev(inp)
+    guard = 4096
+    sentinel = -12345.0
+
+    def banded(shape):
+        n = int(np.prod(shape))
+        buf = torch.full((n + 2 * guard,), sentinel, dtype=p.torch_dtype, device="cuda")
+        return buf, buf[guard: guard + n].view(shape)
+
+    from transformer_attention_fwd_amd.workloads import present_shape, y_shape
+    for mode in ("fwd", "decode"):
+        by, y = banded(y_shape(p))
+        bk, pk = banded(present_shape(p, False))
+        bv, pv = banded(present_shape(p, True))
+        pk.fill_(sentinel)
+        pv.fill_(sentinel)
+        c = _run(p, dev, mode=mode, y=y, present_k=pk, present_v=pv)
+        assert torch.isfinite(c.y.float()).all()
+        if mode == "fwd":
+            assert torch.equal(c.y, clean)
+        for buf in (by, bk, bv):
+            assert (buf[:guard].float() == sentinel).all() and (buf[-guard:].float() == sentinel).all()
+        for b in range(p.B):  # the tail beyond total_b is untouched
+            total = int(lens[b]) + 1
+            assert (pk[b, :, total:].float() == sentinel).all()
+            assert (pv[b, :, total:].float() == sentinel).all()
+
+
+def test_empty_and_degenerate_shapes():
+    # no batch, no query rows, and a row with no allowed key (zeros)
+    for p in (Problem(op="gqa", dtype="bf16", B=0, S=16, L=16, Hq=4, Hkv=2, D=64, Dv=64),
+              Problem(op="attention", dtype="f16", B=2, S=0, L=16, Hq=2, Hkv=2, D=64, Dv=64,
+                      has_lens=False)):
+        inp = make_inputs(p, 5)
+        c = _run(p, to_dev(inp))
+        assert c.y.numel() == 0
+    p = Problem(op="attention", dtype="bf16", B=2, S=5, L=40, Hq=2, Hkv=1, D=64, Dv=64,
+                causal=0, has_lens=True)
+    inp = make_inputs(p, 6, lens=np.array([0, 17]))
+    for mode in ("fwd", "decode"):
+        c = _run(p, to_dev(inp), mode=mode)
+        y = y_logical(p, c.y)
+        assert (y[0] == 0).all()
+        assert_close(p, y, olk_ref.attention(p, inp))
+
+
+def test_first_token_decode_and_full_cache():
+    # past_b = 0 (first step) and past_b = P (cache full) in one batch
+    p = Problem(op="gqa", dtype="bf16", B=2, S=1, L=1, P=256, Hq=8, Hkv=2, D=128, Dv=128,
+                causal=1)
+    inp = make_inputs(p, 8, lens=np.array([0, 256]))
+    for mode in ("fwd", "decode"):
+        c = _run(p, to_dev(inp), mode=mode)
+        assert_close(p, y_logical(p, c.y), olk_ref.attention(p, inp))
+        assert_present_exact(p, inp, c.present_k, c.present_v)

@@ -1,0 +1,281 @@
+// Host side of libolk: validation, planning, kernel choice and launches.
+//
+// Validation follows the operator contracts: local_window_size -1 or positive
+// and only with causal=1 (onnx-light-cpu Python API "Custom operators",
+// "Microsoft GroupQueryAttention"); q_num_heads a multiple of kv_num_heads
+// (onnx-light reference kernels header page, "class Attention"); MultiHeadAttention
+// uses one head count, rank-3 or rank-4 K/V, and rejects what it does not
+// model ("Microsoft MultiHeadAttention").  Nothing here reads device memory.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/olk.h"
+#include "olk_internal.h"
+
+namespace olk {
+hipError_t launch_tiled(const Params &p, int dtype, hipStream_t st);
+bool tiled_supports(const Params &p, int dtype);
+}  // namespace olk
+
+namespace {
+
+thread_local const char *g_last_kernel = "";
+
+constexpr int kGenericSplitChunk = 512;  // keys per split of the generic decode path
+
+size_t esize_of(int dtype) { return dtype == OLK_F32 ? 4 : 2; }
+
+struct Range {
+  const char *p;
+  size_t n;
+};
+
+bool overlaps(Range a, Range b) {
+  if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+  return a.p < b.p + b.n && b.p < a.p + a.n;
+}
+
+// Sizes of every tensor in bytes (int64 arithmetic, checked by the caller).
+struct Sizes {
+  size_t q, k, v, past_k, past_v, bias, sink, proj, y, pres_k, pres_v;
+};
+
+Sizes sizes_of(const olk_attn_desc *d) {
+  const size_t es = esize_of(d->dtype);
+  const size_t B = d->batch, S = d->q_seq, L = d->kv_seq, P = d->past_seq;
+  const size_t Hq = d->q_num_heads, Hkv = d->kv_num_heads, D = d->head_size,
+               Dv = d->v_head_size, T = P + L;
+  Sizes s;
+  s.q = B * S * Hq * D * es;
+  s.k = B * L * Hkv * D * es;
+  s.v = B * L * Hkv * Dv * es;
+  s.past_k = B * Hkv * P * D * es;
+  s.past_v = B * Hkv * P * Dv * es;
+  s.bias = (size_t)(d->bias_b > 0 ? d->bias_b : 0) * (size_t)(d->bias_h > 0 ? d->bias_h : 0) *
+           S * T * es;
+  s.sink = Hq * es;
+  s.proj = (2 * Hq * D + Hq * Dv) * es;
+  s.y = B * S * Hq * Dv * es;
+  s.pres_k = B * Hkv * T * D * es;
+  s.pres_v = B * Hkv * T * Dv * es;
+  return s;
+}
+
+olk_status validate(const olk_attn_desc *d, const olk_attn_io *io) {
+  if (!d || !io) return OLK_E_NULL;
+  if (d->op < OLK_OP_GQA || d->op > OLK_OP_ATTENTION) return OLK_E_ATTR;
+  if (d->dtype < OLK_F32 || d->dtype > OLK_BF16) return OLK_E_ATTR;
+  if (d->kernel < OLK_KERNEL_AUTO || d->kernel > OLK_KERNEL_TILED) return OLK_E_ATTR;
+  if (d->causal != 0 && d->causal != 1) return OLK_E_ATTR;
+  if (d->kv_inplace != 0 && d->kv_inplace != 1) return OLK_E_ATTR;
+  if (d->has_scale && !isfinite(d->scale)) return OLK_E_ATTR;
+  if (!(d->softcap >= 0.f) || isinf(d->softcap)) return OLK_E_ATTR;
+  if (d->op == OLK_OP_MHA && !isfinite(d->mask_filter_value)) return OLK_E_ATTR;
+  // local_window_size: -1 (full) or positive; zero and values below -1 are
+  // rejected, and so is a local window without causal masking.
+  const int w = d->local_window_size;
+  if (w == 0 || w < -1) return OLK_E_ATTR;
+  if (w > 0 && (d->op != OLK_OP_GQA || !d->causal)) return OLK_E_ATTR;
+  if (d->softcap > 0.f && d->op == OLK_OP_MHA) return OLK_E_ATTR;
+
+  if (d->batch < 0 || d->q_seq < 0 || d->kv_seq < 0 || d->past_seq < 0) return OLK_E_SHAPE;
+  if (d->q_num_heads <= 0 || d->kv_num_heads <= 0) return OLK_E_SHAPE;
+  if (d->q_num_heads % d->kv_num_heads) return OLK_E_SHAPE;
+  if (d->head_size <= 0 || d->v_head_size <= 0) return OLK_E_SHAPE;
+  if (d->q_rank != 3 && d->q_rank != 4) return OLK_E_SHAPE;
+  if (d->kv_rank != 3 && d->kv_rank != 4) return OLK_E_SHAPE;
+  if ((int64_t)d->past_seq + d->kv_seq > INT32_MAX) return OLK_E_SHAPE;
+  if (io->attn_bias) {
+    if (d->bias_b != 1 && d->bias_b != d->batch) return OLK_E_SHAPE;
+    if (d->bias_h != 1 && d->bias_h != d->q_num_heads) return OLK_E_SHAPE;
+  }
+
+  switch (d->op) {
+    case OLK_OP_GQA:
+      if (d->q_rank != 3 || d->kv_rank != 3) return OLK_E_SHAPE;
+      if (d->kv_seq != d->q_seq) return OLK_E_SHAPE;
+      if (io->proj_bias) return OLK_E_ATTR;
+      if (!io->seqlens) return OLK_E_NULL;
+      break;
+    case OLK_OP_MHA:
+      if (d->q_rank != 3) return OLK_E_SHAPE;
+      if (d->kv_num_heads != d->q_num_heads) return OLK_E_SHAPE;
+      if (io->head_sink || d->kv_inplace) return OLK_E_ATTR;
+      // rank-3 K/V with their projection-bias segments: not implemented
+      if (io->proj_bias && d->kv_rank == 3) return OLK_E_UNSUPPORTED;
+      break;
+    default:  // ai.onnx::Attention
+      if (io->head_sink || io->proj_bias || d->kv_inplace) return OLK_E_ATTR;
+      break;
+  }
+
+  const Sizes sz = sizes_of(d);
+  if (!io->q && sz.q) return OLK_E_NULL;
+  if ((!io->k && sz.k) || (!io->v && sz.v)) return OLK_E_NULL;
+  if (!io->y && sz.y) return OLK_E_NULL;
+  if (d->kv_inplace) {
+    if ((!io->present_k && sz.pres_k) || (!io->present_v && sz.pres_v)) return OLK_E_NULL;
+    if (io->past_k && io->past_k != io->present_k) return OLK_E_SHAPE;
+    if (io->past_v && io->past_v != io->present_v) return OLK_E_SHAPE;
+  } else if (d->past_seq > 0) {
+    if ((!io->past_k && sz.past_k) || (!io->past_v && sz.past_v)) return OLK_E_NULL;
+  }
+  if (d->head_size > 256 || d->v_head_size > 256) return OLK_E_UNSUPPORTED;
+  if (d->q_num_heads > 65535 || d->batch > 65535) return OLK_E_UNSUPPORTED;
+
+  // Outputs must not overlap inputs or each other (kv_inplace: present is the past).
+  const Range outs[3] = {{(const char *)io->y, sz.y},
+                         {(const char *)io->present_k, sz.pres_k},
+                         {(const char *)io->present_v, sz.pres_v}};
+  const Range ins[8] = {{(const char *)io->q, sz.q},
+                        {(const char *)io->k, sz.k},
+                        {(const char *)io->v, sz.v},
+                        {d->kv_inplace ? nullptr : (const char *)io->past_k,
+                         d->past_seq ? sz.past_k : 0},
+                        {d->kv_inplace ? nullptr : (const char *)io->past_v,
+                         d->past_seq ? sz.past_v : 0},
+                        {(const char *)io->attn_bias, io->attn_bias ? sz.bias : 0},
+                        {(const char *)io->head_sink, io->head_sink ? sz.sink : 0},
+                        {(const char *)io->proj_bias, io->proj_bias ? sz.proj : 0}};
+  for (int a = 0; a < 3; ++a) {
+    for (int b = 0; b < 8; ++b)
+      if (overlaps(outs[a], ins[b])) return OLK_E_SHAPE;
+    for (int b = a + 1; b < 3; ++b)
+      if (overlaps(outs[a], outs[b])) return OLK_E_SHAPE;
+  }
+  return OLK_OK;
+}
+
+olk::Params make_params(const olk_attn_desc *d, const olk_attn_io *io) {
+  olk::Params p;
+  memset(&p, 0, sizeof(p));
+  p.q = io->q;
+  p.k = io->k;
+  p.v = io->v;
+  p.past_k = d->kv_inplace ? io->present_k : io->past_k;
+  p.past_v = d->kv_inplace ? io->present_v : io->past_v;
+  p.seqlens = io->seqlens;
+  p.bias = io->attn_bias;
+  p.sink = io->head_sink;
+  p.proj_bias = d->op == OLK_OP_MHA ? io->proj_bias : nullptr;
+  p.y = io->y;
+  p.present_k = io->present_k;
+  p.present_v = io->present_v;
+  const int64_t S = d->q_seq, L = d->kv_seq, Hq = d->q_num_heads, Hkv = d->kv_num_heads,
+                D = d->head_size, Dv = d->v_head_size;
+  p.B = d->batch;
+  p.S = d->q_seq;
+  p.L = d->kv_seq;
+  p.P = d->past_seq;
+  p.T = d->past_seq + d->kv_seq;
+  p.past_rows = d->kv_inplace ? p.T : p.P;
+  p.Hq = d->q_num_heads;
+  p.Hkv = d->kv_num_heads;
+  p.G = d->q_num_heads / d->kv_num_heads;
+  p.D = d->head_size;
+  p.Dv = d->v_head_size;
+  if (d->q_rank == 3) {  // (B, S, Hq*D)
+    p.q_sb = S * Hq * D; p.q_ss = Hq * D; p.q_sh = D;
+    p.y_sb = S * Hq * Dv; p.y_ss = Hq * Dv; p.y_sh = Dv;
+  } else {               // (B, Hq, S, D)
+    p.q_sb = Hq * S * D; p.q_sh = S * D; p.q_ss = D;
+    p.y_sb = Hq * S * Dv; p.y_sh = S * Dv; p.y_ss = Dv;
+  }
+  if (d->kv_rank == 3) {  // (B, L, Hkv*D)
+    p.k_sb = L * Hkv * D; p.k_ss = Hkv * D; p.k_sh = D;
+    p.v_sb = L * Hkv * Dv; p.v_ss = Hkv * Dv; p.v_sh = Dv;
+  } else {                // (B, Hkv, L, D)
+    p.k_sb = Hkv * L * D; p.k_sh = L * D; p.k_ss = D;
+    p.v_sb = Hkv * L * Dv; p.v_sh = L * Dv; p.v_ss = Dv;
+  }
+  const int64_t T = p.T;
+  p.bias_sh = d->bias_h > 1 ? S * T : 0;
+  p.bias_sb = d->bias_b > 1 ? (int64_t)d->bias_h * S * T : 0;
+  p.op = d->op;
+  p.causal = d->causal;
+  p.window = d->local_window_size > 0 ? d->local_window_size : -1;
+  p.kv_inplace = d->kv_inplace;
+  p.scale = d->has_scale ? d->scale : 1.0f / sqrtf((float)d->head_size);
+  p.softcap = d->softcap;
+  p.mfv = d->mask_filter_value;
+  p.pad_add = (d->op == OLK_OP_MHA && io->seqlens) ? 1 : 0;
+  return p;
+}
+
+int generic_splits(const olk_attn_desc *d) {
+  const int64_t T = (int64_t)d->past_seq + d->kv_seq;
+  const int64_t n = (T + kGenericSplitChunk - 1) / kGenericSplitChunk;
+  return n < 1 ? 1 : (int)n;
+}
+
+}  // namespace
+
+extern "C" {
+
+olk_status olk_validate(const olk_attn_desc *desc, const olk_attn_io *io) {
+  return validate(desc, io);
+}
+
+size_t olk_workspace_bytes(const olk_attn_desc *d) {
+  if (!d || d->batch <= 0 || d->q_seq <= 0 || d->q_num_heads <= 0 || d->v_head_size <= 0)
+    return 0;
+  const size_t rows = (size_t)d->batch * d->q_seq * d->q_num_heads;
+  const size_t bytes = rows * (size_t)generic_splits(d) * (size_t)(d->v_head_size + 2) * 4;
+  return (bytes + 255) & ~(size_t)255;
+}
+
+olk_status olk_attention_fwd(const olk_attn_desc *desc, const olk_attn_io *io, void *stream) {
+  const olk_status st = validate(desc, io);
+  if (st != OLK_OK) return st;
+  const olk::Params p = make_params(desc, io);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = olk::launch_present(p, desc->dtype, s);
+  if (e != hipSuccess) return OLK_E_HIP;
+  const bool tiled_ok = olk::tiled_supports(p, desc->dtype);
+  if (desc->kernel == OLK_KERNEL_TILED && !tiled_ok) return OLK_E_UNSUPPORTED;
+  if (desc->kernel != OLK_KERNEL_GENERIC && tiled_ok) {
+    e = olk::launch_tiled(p, desc->dtype, s);
+    g_last_kernel = "olk_tiled_fwd";
+  } else {
+    e = olk::launch_generic(p, desc->dtype, s);
+    g_last_kernel = "olk_generic_fwd";
+  }
+  return e == hipSuccess ? OLK_OK : OLK_E_HIP;
+}
+
+olk_status olk_attention_decode(const olk_attn_desc *desc, const olk_attn_io *io,
+                                void *workspace, size_t workspace_bytes, void *stream) {
+  const olk_status st = validate(desc, io);
+  if (st != OLK_OK) return st;
+  if ((int64_t)desc->batch * desc->q_seq > 65535) return OLK_E_UNSUPPORTED;
+  const size_t need = olk_workspace_bytes(desc);
+  if (need && (!workspace || workspace_bytes < need)) return OLK_E_WORKSPACE;
+  if (((uintptr_t)workspace & 15) != 0) return OLK_E_WORKSPACE;
+  const olk::Params p = make_params(desc, io);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = olk::launch_present(p, desc->dtype, s);
+  if (e != hipSuccess) return OLK_E_HIP;
+  const int n_split = generic_splits(desc);
+  e = olk::launch_generic_split(p, desc->dtype, kGenericSplitChunk, n_split, (float *)workspace, s);
+  if (e != hipSuccess) return OLK_E_HIP;
+  e = olk::launch_combine(p, desc->dtype, n_split, (const float *)workspace, s);
+  g_last_kernel = "olk_generic_split+combine";
+  return e == hipSuccess ? OLK_OK : OLK_E_HIP;
+}
+
+const char *olk_status_str(olk_status s) {
+  switch (s) {
+    case OLK_OK: return "ok";
+    case OLK_E_NULL: return "required pointer is NULL";
+    case OLK_E_ATTR: return "attribute value rejected by the operator contract";
+    case OLK_E_SHAPE: return "inconsistent sizes, ranks or overlapping buffers";
+    case OLK_E_UNSUPPORTED: return "valid but not supported by this library";
+    case OLK_E_WORKSPACE: return "workspace missing, misaligned or too small";
+    case OLK_E_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+const char *olk_last_kernel_name(void) { return g_last_kernel; }
+
+}  // extern "C"

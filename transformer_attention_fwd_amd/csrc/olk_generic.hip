@@ -1,0 +1,257 @@
+// Generic attention kernels: one 64-lane wavefront per query row, fp32 VALU
+// arithmetic, every dtype and head size up to 256.  They cover every feature of
+// the contract and serve the shapes the MFMA kernels do not (fp32, odd head
+// sizes), plus the split-KV partial/combine pair behind olk_attention_decode.
+//
+// Score pipeline order (onnx-light reference kernels header page, "class
+// Attention", qk_matmul_output_mode stages): (Q.K) * scale, + bias, softcap,
+// then the masks.  The softmax runs online over 64-key chunks: running max m,
+// running sum l, output rescaled by exp(m_old - m_new).  A head_sink (onnx-light-cpu
+// Python API, "Microsoft GroupQueryAttention") joins only the denominator.
+#include "olk_internal.h"
+
+namespace olk {
+namespace {
+
+constexpr int kWave = 64;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+  return x;
+}
+
+// Row of key (value=false) or value (value=true) j of KV head g in batch b.
+template <typename T>
+__device__ __forceinline__ const T *kv_row(const Params &p, const Seq &s, int b, int g, int j,
+                                           bool value) {
+  const int width = value ? p.Dv : p.D;
+  if (j < s.past) {
+    const T *past = (const T *)(value ? p.past_v : p.past_k);
+    return past + (((int64_t)b * p.Hkv + g) * p.past_rows + j) * width;
+  }
+  const T *cur = (const T *)(value ? p.v : p.k);
+  const int64_t sb = value ? p.v_sb : p.k_sb, ss = value ? p.v_ss : p.k_ss,
+                sh = value ? p.v_sh : p.k_sh;
+  return cur + b * sb + (int64_t)(j - s.past) * ss + g * sh;
+}
+
+struct RowState {
+  float m, l;
+  float o[4];
+};
+
+// Online softmax over keys [j_lo, j_hi) of row (b, h, i); keys outside the
+// row's allowed set are skipped by the caller's range and the per-key masks.
+template <typename T>
+__device__ void row_range(const Params &p, const Seq &s, int b, int h, int i, int j_lo,
+                          int j_hi, const float *qs, float *ps, RowState &st) {
+  const int lane = threadIdx.x;
+  const int g = h / p.G;
+  const int pos = s.qoff + i;
+  for (int j0 = j_lo; j0 < j_hi; j0 += kWave) {
+    const int j = j0 + lane;
+    float sc = kNegInf;
+    if (j < j_hi) {
+      const T *kr = kv_row<T>(p, s, b, g, j, false);
+      float dot = 0.f;
+      for (int c = 0; c < p.D; ++c) dot = fmaf(qs[c], to_f32(kr[c]), dot);
+      sc = dot * p.scale;
+      if (p.bias) {
+        const T *br = (const T *)p.bias + b * p.bias_sb + h * p.bias_sh + (int64_t)i * p.T;
+        sc += to_f32(br[j]);
+      }
+      if (p.softcap > 0.f) sc = p.softcap * tanhf(sc / p.softcap);
+      if (p.op == OP_MHA && j >= s.pad) sc += p.mfv;
+      // masks (exclusion) after the score pipeline
+      bool ok = j < s.valid;
+      if (p.causal && j > pos) ok = false;
+      if (p.window > 0 && j < pos - p.window + 1) ok = false;
+      if (!ok) sc = kNegInf;
+    }
+    const float cmax = wave_max(sc);
+    if (cmax == kNegInf) continue;  // whole chunk masked
+    const float m_new = fmaxf(st.m, cmax);
+    const float alpha = st.m == kNegInf ? 0.f : expf(st.m - m_new);
+    const float pj = sc == kNegInf ? 0.f : expf(sc - m_new);
+    st.l = st.l * alpha + wave_sum(pj);
+    st.m = m_new;
+    ps[lane] = pj;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) st.o[k] *= alpha;
+    const int nj = min(kWave, j_hi - j0);
+    for (int jj = 0; jj < nj; ++jj) {
+      const float w = ps[jj];
+      if (w == 0.f) continue;
+      const T *vr = kv_row<T>(p, s, b, g, j0 + jj, true);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int d = lane + k * kWave;
+        if (d < p.Dv) st.o[k] = fmaf(w, to_f32(vr[d]), st.o[k]);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <typename T>
+__device__ void load_q(const Params &p, int b, int h, int i, float *qs) {
+  const T *qr = (const T *)p.q + b * p.q_sb + (int64_t)i * p.q_ss + h * p.q_sh;
+  for (int c = threadIdx.x; c < p.D; c += kWave) {
+    float x = to_f32(qr[c]);
+    if (p.op == OP_MHA && p.proj_bias) x += to_f32(((const T *)p.proj_bias)[h * p.D + c]);
+    qs[c] = x;
+  }
+  __syncthreads();
+}
+
+// Allowed key range of query row i: [lo, hi).
+__device__ __forceinline__ void key_range(const Params &p, const Seq &s, int i, int &lo,
+                                          int &hi) {
+  const int pos = s.qoff + i;
+  hi = s.valid;
+  if (p.causal) hi = min(hi, pos + 1);
+  lo = 0;
+  if (p.window > 0) lo = max(0, pos - p.window + 1);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kWave) void generic_kernel(Params p) {
+  __shared__ float qs[256];
+  __shared__ float ps[kWave];
+  const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const Seq s = seq_info(p, b);
+  load_q<T>(p, b, h, i, qs);
+  int lo, hi;
+  key_range(p, s, i, lo, hi);
+  RowState st{kNegInf, 0.f, {0.f, 0.f, 0.f, 0.f}};
+  row_range<T>(p, s, b, h, i, lo, hi, qs, ps, st);
+  float inv = 0.f;
+  if (st.m != kNegInf) {
+    if (p.sink) {
+      const float z = to_f32(((const T *)p.sink)[h]);
+      const float mf = fmaxf(st.m, z);
+      const float a = expf(st.m - mf);
+      st.l = st.l * a + expf(z - mf);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) st.o[k] *= a;
+    }
+    inv = 1.f / st.l;
+  }
+  T *yr = (T *)p.y + b * p.y_sb + (int64_t)i * p.y_ss + h * p.y_sh;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int d = threadIdx.x + k * kWave;
+    if (d < p.Dv) yr[d] = from_f32<T>(st.o[k] * inv);
+  }
+}
+
+// Split-KV partial: block (split, h, b*S + i) handles keys
+// [split*chunk, (split+1)*chunk) of the row and stores (m, l, o[Dv]) unnormalised.
+template <typename T>
+__global__ __launch_bounds__(kWave) void generic_split_kernel(Params p, int chunk, int n_split,
+                                                              float *ws) {
+  __shared__ float qs[256];
+  __shared__ float ps[kWave];
+  const int split = blockIdx.x, h = blockIdx.y;
+  const int b = blockIdx.z / p.S, i = blockIdx.z % p.S;
+  const Seq s = seq_info(p, b);
+  load_q<T>(p, b, h, i, qs);
+  int lo, hi;
+  key_range(p, s, i, lo, hi);
+  const int c_lo = max(lo, split * chunk), c_hi = min(hi, (split + 1) * chunk);
+  RowState st{kNegInf, 0.f, {0.f, 0.f, 0.f, 0.f}};
+  if (c_lo < c_hi) row_range<T>(p, s, b, h, i, c_lo, c_hi, qs, ps, st);
+  const int64_t row = ((int64_t)b * p.S + i) * p.Hq + h;
+  float *out = ws + (row * n_split + split) * (int64_t)(p.Dv + 2);
+  if (threadIdx.x == 0) {
+    out[0] = st.m;
+    out[1] = st.l;
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int d = threadIdx.x + k * kWave;
+    if (d < p.Dv) out[2 + d] = st.o[k];
+  }
+}
+
+// Merge of the split partials of one row, with the sink in the denominator:
+// M = max(max_s m_s, z); Y = sum_s e^{m_s-M} o_s / (sum_s e^{m_s-M} l_s + e^{z-M}).
+template <typename T>
+__global__ __launch_bounds__(kWave) void combine_kernel(Params p, int n_split, const float *ws) {
+  const int h = blockIdx.x;
+  const int b = blockIdx.y / p.S, i = blockIdx.y % p.S;
+  const int64_t row = ((int64_t)b * p.S + i) * p.Hq + h;
+  const float *part = ws + row * n_split * (int64_t)(p.Dv + 2);
+  float M = kNegInf;
+  for (int sp = 0; sp < n_split; ++sp) M = fmaxf(M, part[sp * (int64_t)(p.Dv + 2)]);
+  T *yr = (T *)p.y + b * p.y_sb + (int64_t)i * p.y_ss + h * p.y_sh;
+  if (M == kNegInf) {  // no allowed key: zeros
+    for (int d = threadIdx.x; d < p.Dv; d += kWave) yr[d] = from_f32<T>(0.f);
+    return;
+  }
+  float z = kNegInf;
+  if (p.sink) z = to_f32(((const T *)p.sink)[h]);
+  const float Mf = fmaxf(M, z);
+  float l = p.sink ? expf(z - Mf) : 0.f;
+  for (int sp = 0; sp < n_split; ++sp) {
+    const float m = part[sp * (int64_t)(p.Dv + 2)];
+    if (m != kNegInf) l += part[sp * (int64_t)(p.Dv + 2) + 1] * expf(m - Mf);
+  }
+  const float inv = 1.f / l;
+  for (int d = threadIdx.x; d < p.Dv; d += kWave) {
+    float acc = 0.f;
+    for (int sp = 0; sp < n_split; ++sp) {
+      const float m = part[sp * (int64_t)(p.Dv + 2)];
+      if (m != kNegInf) acc += part[sp * (int64_t)(p.Dv + 2) + 2 + d] * expf(m - Mf);
+    }
+    yr[d] = from_f32<T>(acc * inv);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_generic(const Params &p, int dtype, hipStream_t st) {
+  if (p.B == 0 || p.S == 0 || p.Hq == 0) return hipSuccess;
+  dim3 grid(p.S, p.Hq, p.B);
+  if (dtype == DT_F32) hipLaunchKernelGGL(generic_kernel<float>, grid, dim3(kWave), 0, st, p);
+  else if (dtype == DT_F16) hipLaunchKernelGGL(generic_kernel<f16>, grid, dim3(kWave), 0, st, p);
+  else hipLaunchKernelGGL(generic_kernel<bf16>, grid, dim3(kWave), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_generic_split(const Params &p, int dtype, int chunk, int n_split, float *ws,
+                                hipStream_t st) {
+  if (p.B == 0 || p.S == 0 || p.Hq == 0) return hipSuccess;
+  dim3 grid(n_split, p.Hq, p.B * p.S);
+  if (dtype == DT_F32)
+    hipLaunchKernelGGL(generic_split_kernel<float>, grid, dim3(kWave), 0, st, p, chunk, n_split, ws);
+  else if (dtype == DT_F16)
+    hipLaunchKernelGGL(generic_split_kernel<f16>, grid, dim3(kWave), 0, st, p, chunk, n_split, ws);
+  else
+    hipLaunchKernelGGL(generic_split_kernel<bf16>, grid, dim3(kWave), 0, st, p, chunk, n_split, ws);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const Params &p, int dtype, int n_split, const float *ws,
+                          hipStream_t st) {
+  if (p.B == 0 || p.S == 0 || p.Hq == 0) return hipSuccess;
+  dim3 grid(p.Hq, p.B * p.S);
+  if (dtype == DT_F32)
+    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(kWave), 0, st, p, n_split, ws);
+  else if (dtype == DT_F16)
+    hipLaunchKernelGGL(combine_kernel<f16>, grid, dim3(kWave), 0, st, p, n_split, ws);
+  else
+    hipLaunchKernelGGL(combine_kernel<bf16>, grid, dim3(kWave), 0, st, p, n_split, ws);
+  return hipGetLastError();
+}
+
+}  // namespace olk

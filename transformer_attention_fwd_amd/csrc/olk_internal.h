@@ -1,0 +1,88 @@
+// Internal declarations shared by the HIP sources of libolk (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace olk {
+
+enum { OP_GQA = 0, OP_MHA = 1, OP_ATTENTION = 2 };
+enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+
+typedef _Float16 f16;
+typedef __bf16 bf16;
+
+// Everything a kernel needs about one call, resolved on the host.  Strides are
+// in elements.  Past and present tensors are (B, Hkv, P|T, D|Dv), dense.
+struct Params {
+  const void *q, *k, *v, *past_k, *past_v;
+  const int32_t *seqlens;
+  const void *bias, *sink, *proj_bias;
+  void *y, *present_k, *present_v;
+  int64_t q_sb, q_ss, q_sh;   // Q: batch, sequence, head strides (last dim dense)
+  int64_t k_sb, k_ss, k_sh;   // new K
+  int64_t v_sb, v_ss, v_sh;   // new V
+  int64_t y_sb, y_ss, y_sh;   // Y
+  int64_t bias_sb, bias_sh;   // bias batch / head strides (0 when broadcast); row stride T
+  int B, S, L, P, T, Hq, Hkv, G, D, Dv;
+  int past_rows;   // rows per (b, g) of the past buffer: P, or T when the past lives in present
+  int op, causal, window;
+  int pad_add;     // MultiHeadAttention: 1 = padded keys get mfv added, 0 = excluded
+  int kv_inplace;  // present already holds the valid past
+  float scale;     // score multiplier
+  float softcap;   // > 0: softcap * tanh(s / softcap)
+  float mfv;       // mask_filter_value
+};
+
+// Per-batch sequence bookkeeping (integer; read once per workgroup).
+struct Seq {
+  int past;   // keys taken from the past buffer
+  int total;  // keys in the concatenated sequence
+  int valid;  // keys j < valid may be attended
+  int pad;    // keys j >= pad get mfv added (MultiHeadAttention, additive mode)
+  int qoff;   // absolute position of query 0 (bottom-right causal alignment)
+};
+
+__device__ __forceinline__ Seq seq_info(const Params &p, int b) {
+  Seq s;
+  if (p.op == OP_GQA) {
+    // seqlens_k = total length - 1; the new keys follow the valid past.
+    long long past = (long long)p.seqlens[b] + 1 - p.S;
+    past = past < 0 ? 0 : (past > p.P ? p.P : past);
+    s.past = (int)past;
+    s.total = s.past + p.S;
+    s.valid = s.total;
+    s.pad = s.total;
+    s.qoff = s.past;
+  } else {
+    s.past = p.P;
+    s.total = p.T;
+    s.qoff = p.T - p.S;
+    s.valid = p.T;
+    s.pad = p.T;
+    if (p.seqlens) {
+      int n = p.seqlens[b];
+      n = n < 0 ? 0 : (n > p.T ? p.T : n);
+      if (p.op == OP_ATTENTION) {
+        s.valid = n;
+      } else if (n > 0) {  // MHA: a fully padded row is a uniform shift = no mask
+        if (p.pad_add) s.pad = n;
+        else s.valid = n;
+      }
+    }
+  }
+  return s;
+}
+
+template <typename T> __device__ __forceinline__ float to_f32(T x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x) { return (T)x; }
+
+// Launchers (defined in the .hip files); return hipSuccess or the launch error.
+hipError_t launch_generic(const Params &p, int dtype, hipStream_t st);
+hipError_t launch_generic_split(const Params &p, int dtype, int chunk, int n_split,
+                                float *ws, hipStream_t st);
+hipError_t launch_combine(const Params &p, int dtype, int n_split, const float *ws,
+                          hipStream_t st);
+hipError_t launch_present(const Params &p, int dtype, hipStream_t st);
+
+}  // namespace olk

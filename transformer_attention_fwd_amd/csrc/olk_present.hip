@@ -1,0 +1,62 @@
+// present_key / present_value writer (onnx-light-cpu Python API page "Custom
+// operators": GroupQueryAttention present outputs hold the entire past cache
+// followed by the current step; MultiHeadAttention present has P+L positions;
+// onnx-light reference kernels header page, "class Attention" Result: present
+// equals K/V or their concatenation with the past).
+//
+// Pure copies: position j < total_b of (b, g) takes row j of the past buffer
+// when j < past_b, else row j - past_b of the new K/V.  Bits are copied, never
+// converted.  Positions at or beyond total_b are not touched.  In kv_inplace
+// mode the past rows are already in place and only the new rows are written.
+#include "olk_internal.h"
+
+namespace olk {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRowsPerBlock = 16;
+
+// Copies rows [blockIdx.x*kRowsPerBlock, ...) of (g = blockIdx.y, b = blockIdx.z)
+// for both K (which = 0) and V (which = 1) in units of U (4 or 2 bytes).
+template <typename U>
+__global__ __launch_bounds__(kThreads) void present_kernel(Params p, int esize) {
+  const int g = blockIdx.y, b = blockIdx.z;
+  const Seq s = seq_info(p, b);
+  const int j0 = blockIdx.x * kRowsPerBlock;
+  for (int which = 0; which < 2; ++which) {
+    char *dst_base = (char *)(which ? p.present_v : p.present_k);
+    if (!dst_base) continue;
+    const int width = which ? p.Dv : p.D;
+    const int row_words = width * esize / (int)sizeof(U);
+    const char *past = (const char *)(which ? p.past_v : p.past_k);
+    const char *cur = (const char *)(which ? p.v : p.k);
+    const int64_t sb = which ? p.v_sb : p.k_sb, ss = which ? p.v_ss : p.k_ss,
+                  sh = which ? p.v_sh : p.k_sh;
+    const int n = kRowsPerBlock * row_words;
+    for (int t = threadIdx.x; t < n; t += kThreads) {
+      const int j = j0 + t / row_words, w = t % row_words;
+      if (j >= s.total || j >= p.T) continue;
+      if (p.kv_inplace && j < s.past) continue;
+      const char *src;
+      if (j < s.past) src = past + ((((int64_t)b * p.Hkv + g) * p.past_rows + j) * width) * esize;
+      else src = cur + (b * sb + (int64_t)(j - s.past) * ss + g * sh) * esize;
+      char *dst = dst_base + ((((int64_t)b * p.Hkv + g) * p.T + j) * width) * esize;
+      ((U *)dst)[w] = ((const U *)src)[w];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_present(const Params &p, int dtype, hipStream_t st) {
+  if ((!p.present_k && !p.present_v) || p.B == 0 || p.T == 0) return hipSuccess;
+  const int esize = dtype == DT_F32 ? 4 : 2;
+  dim3 grid((p.T + kRowsPerBlock - 1) / kRowsPerBlock, p.Hkv, p.B);
+  if ((p.D * esize) % 4 == 0 && (p.Dv * esize) % 4 == 0)
+    hipLaunchKernelGGL(present_kernel<uint32_t>, grid, dim3(kThreads), 0, st, p, esize);
+  else
+    hipLaunchKernelGGL(present_kernel<uint16_t>, grid, dim3(kThreads), 0, st, p, esize);
+  return hipGetLastError();
+}
+
+}  // namespace olk
