@@ -1,0 +1,287 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention forward on one MI355X.
+
+One step = one call of the whole path (validate/plan on the host, sequence
+metadata, Q load, K/V staging + present write, QK^T, score epilogue, online
+softmax, PV, finalize) on the bf16 GQA causal prefill workload
+(B=4, S=2048, 32 query / 8 KV heads, head size 128), inputs resident in HBM.
+
+Prints one JSON line: the headline TFLOP/s (algorithmic FLOPs: 4*D per
+unmasked (query, key) pair, i.e. QK^T + PV), the roofline of the dominant
+kernel (timed alone with HIP events on the stream it runs on), the oracle's CPU
+throughput on a bounded sample, and secondary figures for the other workloads
+(decode as KV GB/s).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}  # dense, MI355X
+HBM_PEAK_GBS = 8000.0
+HEADLINE = "gqa_prefill_causal_bf16"
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+TILED_SRC = os.path.join(ROOT, "transformer_attention_fwd_amd", "csrc", "olk_tiled.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--no-secondary", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+# ---- algorithmic work (bookkeeping of the definition's masks) ---------------
+
+def allowed_pairs(p, inputs) -> np.ndarray:
+    """Number of attended keys per (b, i) row (same for every head)."""
+    from transformer_attention_fwd_amd.workloads import valid_lengths
+    tot = valid_lengths(p, inputs)
+    out = np.zeros((p.B, p.S), dtype=np.int64)
+    for b in range(p.B):
+        if p.op == "gqa":
+            total = int(tot[b])
+            qoff = total - p.S
+            valid = total
+        else:
+            total = p.T
+            qoff = total - p.S
+            valid = int(tot[b]) if (p.op == "attention" or p.mask_filter_value <= -5000) else total
+            if p.op == "mha" and valid == 0:
+                valid = total
+        pos = qoff + np.arange(p.S)
+        hi = np.full(p.S, valid)
+        if p.causal:
+            hi = np.minimum(hi, pos + 1)
+        lo = np.zeros(p.S, dtype=np.int64)
+        if p.window > 0:
+            lo = np.maximum(0, pos - p.window + 1)
+        out[b] = np.maximum(0, hi - lo)
+    return out
+
+
+def flops(p, inputs) -> float:
+    return 2.0 * (p.D + p.Dv) * float(allowed_pairs(p, inputs).sum()) * p.Hq
+
+
+def decode_bytes(p, inputs, inplace: bool) -> float:
+    """KV bytes read + Q/Y + new K/V + present append (or full copy)."""
+    from transformer_attention_fwd_amd.workloads import valid_lengths
+    es = 2 if p.dtype != "f32" else 4
+    tot = valid_lengths(p, inputs).astype(np.float64)
+    kv = float((tot - p.S).sum()) * p.Hkv * (p.D + p.Dv) * es          # past rows read
+    new = p.B * p.S * p.Hkv * (p.D + p.Dv) * es                         # new K/V read
+    qy = p.B * p.S * p.Hq * (p.D + p.Dv) * es
+    append = new if inplace else float(tot.sum()) * p.Hkv * (p.D + p.Dv) * es
+    return kv + new + qy + append
+
+
+# ---- timing ---------------------------------------------------------------------
+
+def time_launches(call, steps: int, warmup: int):
+    import torch
+    for _ in range(warmup):
+        call.launch()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        call.launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def traffic_for(workload: str):
+    """HBM bytes per launch from committed rocprofv3 counters, if they were
+    taken on the current kernel source (else None)."""
+    try:
+        with open(PROFILE_TRAFFIC) as f:
+            rec = json.load(f)
+        h = hashlib.sha256(open(TILED_SRC, "rb").read()).hexdigest()
+        ent = rec.get(workload)
+        if ent and ent.get("kernel_sha256") == h:
+            return float(ent["fetch_bytes"]) + float(ent["write_bytes"])
+    except (OSError, ValueError, KeyError):
+        pass
+    return None
+
+
+def cpu_baseline(p, inputs, kind: str, target_s: float):
+    """Oracle throughput on a bounded random sample of rows."""
+    from oracle import olk_ref
+    cores = len(os.sched_getaffinity(0))
+    rng = np.random.default_rng(7)
+    pairs = allowed_pairs(p, inputs)
+    # calibrate on a small sample, then size the sample to ~target_s
+    n = 64
+    rows = None
+    spent = 0.0
+    work = 0.0
+    n_rows = 0
+    for _ in range(3):
+        rows = np.stack([rng.integers(0, p.B, n), rng.integers(0, p.Hq, n),
+                         rng.integers(0, p.S, n)], axis=1).astype(np.int32)
+        t0 = time.perf_counter()
+        olk_ref.attention_rows(p, inputs, rows, threads=cores)
+        dt = time.perf_counter() - t0
+        spent += dt
+        n_rows += len(rows)
+        npairs = float(pairs[rows[:, 0], rows[:, 2]].sum())
+        if kind == "flops":
+            work += 2.0 * (p.D + p.Dv) * npairs
+        else:
+            es = 2 if p.dtype != "f32" else 4
+            work += npairs * (p.D + p.Dv) * es
+        if spent >= target_s:
+            break
+        n = int(min(200000, max(n * 2, n * (target_s - spent) / max(dt, 1e-3))))
+    value = work / spent / (1e12 if kind == "flops" else 1e9)
+    return {"value": round(value, 6), "unit": "TFLOP/s" if kind == "flops" else "GB/s",
+            "cores": cores, "kind": "oracle",
+            "sample": f"{n_rows} random (b, h, i) query rows of {p.B}x{p.Hq}x{p.S} "
+                      f"({spent:.1f} s of float64 oracle time)"}
+
+
+def check_rows(p, inputs, y, n=48):
+    """Sampled-row parity against the oracle before timing."""
+    import torch
+    from oracle import olk_ref
+    rng = np.random.default_rng(3)
+    rows = np.stack([rng.integers(0, p.B, n), rng.integers(0, p.Hq, n),
+                     rng.integers(0, p.S, n)], axis=1).astype(np.int32)
+    want = olk_ref.attention_rows(p, inputs, rows)
+    yl = y.detach().to("cpu").to(torch.float64)
+    yl = yl.view(p.B, p.S, p.Hq, p.Dv) if p.q_rank == 3 else yl.permute(0, 2, 1, 3)
+    got = yl.numpy()[rows[:, 0], rows[:, 2], rows[:, 1]]
+    return float(np.abs(got - want).max())
+
+
+def run_workload(name, steps, warmup, with_cpu, cpu_s, is_headline):
+    import torch
+    from transformer_attention_fwd_amd import olk
+    from transformer_attention_fwd_amd.workloads import workload
+    p, inputs = workload(name)
+    dev = {k: v.to("cuda") for k, v in inputs.items()}
+    decode = p.S == 1
+    res = {"workload": name}
+    if decode:
+        # KV-cache decode: present already holds the past (in-place append)
+        pk = torch.empty((p.B, p.Hkv, p.P + p.L, p.D), dtype=p.torch_dtype, device="cuda")
+        pv = torch.empty((p.B, p.Hkv, p.P + p.L, p.Dv), dtype=p.torch_dtype, device="cuda")
+        pk[:, :, : p.P] = dev.pop("past_k")
+        pv[:, :, : p.P] = dev.pop("past_v")
+        call = olk.Call(p, dev, mode="decode", kv_inplace=True, present_k=pk, present_v=pv)
+    else:
+        call = olk.Call(p, dev, mode="fwd", want_present=(p.op == "gqa"))
+    call.launch()
+    torch.cuda.synchronize()
+    res["kernel"] = olk.olk_last_kernel_name()
+    res["max_abs_err_sampled"] = check_rows(p, inputs, call.y)
+    ms, wall = time_launches(call, steps, warmup)
+    res["ms_per_step"] = ms
+    res["wall_s"] = wall
+    if decode:
+        by = decode_bytes(p, inputs, inplace=True)
+        res["value"] = by / (ms * 1e-3) / 1e9
+        res["unit"] = "GB/s"
+        res["frac_of_peak"] = res["value"] / HBM_PEAK_GBS
+        res["bytes_per_step"] = by
+    else:
+        fl = flops(p, inputs)
+        res["value"] = fl / (ms * 1e-3) / 1e12
+        res["unit"] = "TFLOP/s"
+        res["frac_of_peak"] = res["value"] / MFMA_PEAK_TFLOPS[p.dtype]
+        res["flops_per_step"] = fl
+        if is_headline:
+            # dominant kernel alone: the same call without present outputs
+            kcall = olk.Call(p, dev, mode="fwd", want_present=False)
+            kms, _ = time_launches(kcall, steps, warmup)
+            ach = fl / (kms * 1e-3) / 1e12
+            peak = MFMA_PEAK_TFLOPS[p.dtype]
+            res["roofline"] = {"bound": "mfma", "achieved": round(ach, 3), "peak": peak,
+                               "unit": "TFLOP/s", "frac": round(ach / peak, 5),
+                               "traffic": traffic_for(name), "kernel": "tiled_kernel",
+                               "kernel_ms": kms}
+    if with_cpu:
+        res["cpu_baseline"] = cpu_baseline(p, inputs, "bytes" if decode else "flops", cpu_s)
+    del call, dev
+    torch.cuda.empty_cache()
+    return p, res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus_requested": args.gpus}))
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs an MI355X"
+    torch.cuda.set_device(0)
+    t_start = time.perf_counter()
+    p, head = run_workload(args.workload, args.steps, args.warmup, not args.no_cpu,
+                           args.cpu_seconds, True)
+    print(f"[bench] {args.workload}: {head['value']:.1f} {head['unit']} "
+          f"({head['ms_per_step']:.3f} ms/step) err={head['max_abs_err_sampled']:.2e}",
+          file=sys.stderr, flush=True)
+    secondary = {}
+    if not args.no_secondary:
+        from transformer_attention_fwd_amd.workloads import WORKLOAD_ORDER
+        for name in WORKLOAD_ORDER:
+            if name == args.workload:
+                continue
+            _, r = run_workload(name, max(5, args.steps // 5), max(2, args.warmup // 5), False,
+                                0, False)
+            print(f"[bench] {name}: {r['value']:.1f} {r['unit']} ({r['ms_per_step']:.4f} ms) "
+                  f"err={r['max_abs_err_sampled']:.2e}", file=sys.stderr, flush=True)
+            secondary[name] = {k: r[k] for k in ("value", "unit", "frac_of_peak", "ms_per_step",
+                                                 "kernel", "max_abs_err_sampled")}
+    line = {
+        "metric": "attention TFLOP/s (prefill) + KV GB/s (decode), % of MI355X MFMA/HBM peak",
+        "value": round(head["value"], 3),
+        "unit": head["unit"],
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": p.dtype,
+        "data": "synthetic (seeded N(0,1) inputs; no dataset)",
+        "config": {"workload": args.workload, "op": p.op, "batch": p.B, "seq_len": p.S,
+                   "q_heads": p.Hq, "kv_heads": p.Hkv, "head_size": p.D,
+                   "causal": p.causal, "local_window_size": p.window,
+                   "outputs": "Y + present_key/present_value"},
+        "frac_of_peak": round(head["frac_of_peak"], 5),
+        "kernel": head["kernel"],
+        "max_abs_err_sampled": head["max_abs_err_sampled"],
+        "roofline": head.get("roofline"),
+        "cpu_baseline": head.get("cpu_baseline"),
+        "secondary": secondary,
+        "bench_wall_s": round(time.perf_counter() - t_start, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

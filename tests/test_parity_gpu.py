@@ -74,14 +74,24 @@ def _run(p, dev, **kw):
     return c
 
 
+def tiled_capable(p):
+    return p.dtype in ("f16", "bf16") and p.D == p.Dv and p.D in (64, 128)
+
+
 @pytest.mark.parametrize("name", list(SMALL))
-@pytest.mark.parametrize("mode,kernel", [("fwd", "generic"), ("fwd", "auto"),
-                                         ("decode", "auto")])
+@pytest.mark.parametrize("mode,kernel", [("fwd", "generic"), ("fwd", "tiled"),
+                                         ("decode", "generic"), ("decode", "tiled"),
+                                         ("fwd", "auto")])
 def test_small_parity(name, mode, kernel):
     p = SMALL[name]
+    if kernel == "tiled" and not tiled_capable(p):
+        pytest.skip("the tiled kernel covers f16/bf16 with head size 64 or 128")
     inp = make_inputs(p, 500 + list(SMALL).index(name))
     _say(f"[parity] {name} mode={mode} kernel={kernel}")
     c = _run(p, to_dev(inp), mode=mode, kernel=kernel)
+    name_ran = olk.olk_last_kernel_name()
+    if kernel != "generic" and tiled_capable(p):
+        assert "tiled" in name_ran, name_ran
     want = olk_ref.attention(p, inp)
     assert_close(p, y_logical(p, c.y), want)
     assert_present_exact(p, inp, c.present_k, c.present_v)
@@ -95,6 +105,8 @@ def test_workload_parity(name):
     dev = to_dev(inp)
     c = _run(p, dev, mode=mode)
     _say(f"[parity] {name} kernel={olk.olk_last_kernel_name()}")
+    if tiled_capable(p):
+        assert "tiled" in olk.olk_last_kernel_name()
     if p.B * p.S * p.Hq <= 4096:
         assert_close(p, y_logical(p, c.y), olk_ref.attention(p, inp))
     else:
@@ -142,7 +154,8 @@ def test_poisoned_padding_and_guard_bands():
         inp["past_v"][b, :, past:] = float("nan")
     dev = to_dev(inp)
     guard = 4096
-    sentinel = -12345.0
+    # a value every element type represents exactly
+    sentinel = -777.0 if p.dtype != "bf16" else -776.0
 
     def banded(shape):
         n = int(np.prod(shape))

@@ -14,6 +14,8 @@
 
 namespace olk {
 hipError_t launch_tiled(const Params &p, int dtype, hipStream_t st);
+hipError_t launch_tiled_split(const Params &p, int dtype, int split_tiles, float *ws,
+                              hipStream_t st);
 bool tiled_supports(const Params &p, int dtype);
 }  // namespace olk
 
@@ -21,7 +23,9 @@ namespace {
 
 thread_local const char *g_last_kernel = "";
 
-constexpr int kGenericSplitChunk = 512;  // keys per split of the generic decode path
+// Keys per split of the decode path (both kernel families; a multiple of the
+// tiled kernel's 64-key tile).
+constexpr int kSplitKeys = 512;
 
 size_t esize_of(int dtype) { return dtype == OLK_F32 ? 4 : 2; }
 
@@ -95,7 +99,7 @@ olk_status validate(const olk_attn_desc *d, const olk_attn_io *io) {
       if (d->q_rank != 3 || d->kv_rank != 3) return OLK_E_SHAPE;
       if (d->kv_seq != d->q_seq) return OLK_E_SHAPE;
       if (io->proj_bias) return OLK_E_ATTR;
-      if (!io->seqlens) return OLK_E_NULL;
+      if (!io->seqlens && d->batch > 0) return OLK_E_NULL;
       break;
     case OLK_OP_MHA:
       if (d->q_rank != 3) return OLK_E_SHAPE;
@@ -202,9 +206,9 @@ olk::Params make_params(const olk_attn_desc *d, const olk_attn_io *io) {
   return p;
 }
 
-int generic_splits(const olk_attn_desc *d) {
+int n_splits(const olk_attn_desc *d) {
   const int64_t T = (int64_t)d->past_seq + d->kv_seq;
-  const int64_t n = (T + kGenericSplitChunk - 1) / kGenericSplitChunk;
+  const int64_t n = (T + kSplitKeys - 1) / kSplitKeys;
   return n < 1 ? 1 : (int)n;
 }
 
@@ -220,7 +224,8 @@ size_t olk_workspace_bytes(const olk_attn_desc *d) {
   if (!d || d->batch <= 0 || d->q_seq <= 0 || d->q_num_heads <= 0 || d->v_head_size <= 0)
     return 0;
   const size_t rows = (size_t)d->batch * d->q_seq * d->q_num_heads;
-  const size_t bytes = rows * (size_t)generic_splits(d) * (size_t)(d->v_head_size + 2) * 4;
+  // one record [m, l, -, -, O[Dv]] of floats per (row, split)
+  const size_t bytes = rows * (size_t)n_splits(d) * (size_t)(d->v_head_size + 4) * 4;
   return (bytes + 255) & ~(size_t)255;
 }
 
@@ -255,11 +260,18 @@ olk_status olk_attention_decode(const olk_attn_desc *desc, const olk_attn_io *io
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = olk::launch_present(p, desc->dtype, s);
   if (e != hipSuccess) return OLK_E_HIP;
-  const int n_split = generic_splits(desc);
-  e = olk::launch_generic_split(p, desc->dtype, kGenericSplitChunk, n_split, (float *)workspace, s);
+  const int n_split = n_splits(desc);
+  const bool tiled_ok = olk::tiled_supports(p, desc->dtype);
+  if (desc->kernel == OLK_KERNEL_TILED && !tiled_ok) return OLK_E_UNSUPPORTED;
+  if (desc->kernel != OLK_KERNEL_GENERIC && tiled_ok) {
+    e = olk::launch_tiled_split(p, desc->dtype, kSplitKeys / 64, (float *)workspace, s);
+    g_last_kernel = "olk_tiled_split+combine";
+  } else {
+    e = olk::launch_generic_split(p, desc->dtype, kSplitKeys, n_split, (float *)workspace, s);
+    g_last_kernel = "olk_generic_split+combine";
+  }
   if (e != hipSuccess) return OLK_E_HIP;
   e = olk::launch_combine(p, desc->dtype, n_split, (const float *)workspace, s);
-  g_last_kernel = "olk_generic_split+combine";
   return e == hipSuccess ? OLK_OK : OLK_E_HIP;
 }
 

@@ -155,7 +155,8 @@ __global__ __launch_bounds__(kWave) void generic_kernel(Params p) {
 }
 
 // Split-KV partial: block (split, h, b*S + i) handles keys
-// [split*chunk, (split+1)*chunk) of the row and stores (m, l, o[Dv]) unnormalised.
+// [split*chunk, (split+1)*chunk) of the row and stores the record
+// [m, l, -, -, o[Dv]] (natural-log units, unnormalised; stride Dv + 4 floats).
 template <typename T>
 __global__ __launch_bounds__(kWave) void generic_split_kernel(Params p, int chunk, int n_split,
                                                               float *ws) {
@@ -171,7 +172,7 @@ __global__ __launch_bounds__(kWave) void generic_split_kernel(Params p, int chun
   RowState st{kNegInf, 0.f, {0.f, 0.f, 0.f, 0.f}};
   if (c_lo < c_hi) row_range<T>(p, s, b, h, i, c_lo, c_hi, qs, ps, st);
   const int64_t row = ((int64_t)b * p.S + i) * p.Hq + h;
-  float *out = ws + (row * n_split + split) * (int64_t)(p.Dv + 2);
+  float *out = ws + (row * n_split + split) * (int64_t)(p.Dv + 4);
   if (threadIdx.x == 0) {
     out[0] = st.m;
     out[1] = st.l;
@@ -179,7 +180,7 @@ __global__ __launch_bounds__(kWave) void generic_split_kernel(Params p, int chun
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int d = threadIdx.x + k * kWave;
-    if (d < p.Dv) out[2 + d] = st.o[k];
+    if (d < p.Dv) out[4 + d] = st.o[k];
   }
 }
 
@@ -190,9 +191,10 @@ __global__ __launch_bounds__(kWave) void combine_kernel(Params p, int n_split, c
   const int h = blockIdx.x;
   const int b = blockIdx.y / p.S, i = blockIdx.y % p.S;
   const int64_t row = ((int64_t)b * p.S + i) * p.Hq + h;
-  const float *part = ws + row * n_split * (int64_t)(p.Dv + 2);
+  const int64_t rec = p.Dv + 4;
+  const float *part = ws + row * n_split * rec;
   float M = kNegInf;
-  for (int sp = 0; sp < n_split; ++sp) M = fmaxf(M, part[sp * (int64_t)(p.Dv + 2)]);
+  for (int sp = 0; sp < n_split; ++sp) M = fmaxf(M, part[sp * rec]);
   T *yr = (T *)p.y + b * p.y_sb + (int64_t)i * p.y_ss + h * p.y_sh;
   if (M == kNegInf) {  // no allowed key: zeros
     for (int d = threadIdx.x; d < p.Dv; d += kWave) yr[d] = from_f32<T>(0.f);
@@ -203,15 +205,15 @@ __global__ __launch_bounds__(kWave) void combine_kernel(Params p, int n_split, c
   const float Mf = fmaxf(M, z);
   float l = p.sink ? expf(z - Mf) : 0.f;
   for (int sp = 0; sp < n_split; ++sp) {
-    const float m = part[sp * (int64_t)(p.Dv + 2)];
-    if (m != kNegInf) l += part[sp * (int64_t)(p.Dv + 2) + 1] * expf(m - Mf);
+    const float m = part[sp * rec];
+    if (m != kNegInf) l += part[sp * rec + 1] * expf(m - Mf);
   }
   const float inv = 1.f / l;
   for (int d = threadIdx.x; d < p.Dv; d += kWave) {
     float acc = 0.f;
     for (int sp = 0; sp < n_split; ++sp) {
-      const float m = part[sp * (int64_t)(p.Dv + 2)];
-      if (m != kNegInf) acc += part[sp * (int64_t)(p.Dv + 2) + 2 + d] * expf(m - Mf);
+      const float m = part[sp * rec];
+      if (m != kNegInf) acc += part[sp * rec + 4 + d] * expf(m - Mf);
     }
     yr[d] = from_f32<T>(acc * inv);
   }
