@@ -13,6 +13,8 @@
 #include "olk_internal.h"
 
 namespace olk {
+hipError_t launch_flash(const Params &p, int dtype, hipStream_t st);
+bool flash_fuses_present(const Params &p);
 hipError_t launch_tiled(const Params &p, int dtype, hipStream_t st);
 hipError_t launch_tiled_split(const Params &p, int dtype, int split_tiles, float *ws,
                               hipStream_t st);
@@ -232,14 +234,16 @@ size_t olk_workspace_bytes(const olk_attn_desc *d) {
 olk_status olk_attention_fwd(const olk_attn_desc *desc, const olk_attn_io *io, void *stream) {
   const olk_status st = validate(desc, io);
   if (st != OLK_OK) return st;
-  const olk::Params p = make_params(desc, io);
+  olk::Params p = make_params(desc, io);
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = olk::launch_present(p, desc->dtype, s);
-  if (e != hipSuccess) return OLK_E_HIP;
   const bool tiled_ok = olk::tiled_supports(p, desc->dtype);
   if (desc->kernel == OLK_KERNEL_TILED && !tiled_ok) return OLK_E_UNSUPPORTED;
-  if (desc->kernel != OLK_KERNEL_GENERIC && tiled_ok) {
-    e = olk::launch_tiled(p, desc->dtype, s);
+  const bool use_tiled = desc->kernel != OLK_KERNEL_GENERIC && tiled_ok;
+  if (use_tiled && olk::flash_fuses_present(p)) p.present_past_only = 1;
+  hipError_t e = olk::launch_present(p, desc->dtype, s);
+  if (e != hipSuccess) return OLK_E_HIP;
+  if (use_tiled) {
+    e = olk::launch_flash(p, desc->dtype, s);
     g_last_kernel = "olk_tiled_fwd";
   } else {
     e = olk::launch_generic(p, desc->dtype, s);

@@ -1,0 +1,489 @@
+// Prefill attention forward for gfx950 (CDNA4): f16/bf16 inputs, head size 64
+// or 128, fp32 accumulation.
+//
+// Computes Y = Softmax((Q K^T) * scale + bias) V with grouped KV heads, causal /
+// local-window / length masks, softcap, head_sink and the present outputs of
+// the GroupQueryAttention, MultiHeadAttention and ai.onnx Attention contracts
+// (onnx-light-cpu Python API "Custom operators"; onnx-light reference kernels
+// header page, "class Attention").  The decomposition is ours:
+//
+// * A workgroup is 4 wavefronts x 32 row slots; two workgroups share a CU
+//   (two wavefronts per SIMD, so one wave's MFMAs overlap the other's softmax).
+//   Slots pack the GH query heads sharing one KV head with consecutive queries
+//   (slot -> (query, head)): every K/V tile in LDS serves the whole head group.
+// * S^T = K Q^T and O^T += V^T P^T run on v_mfma_f32_32x32x16.  In the S^T
+//   accumulator layout a lane owns one row slot and half of a tile's keys, so
+//   the softmax max/sum are in-lane plus one exchange with lane ^ 32, and P^T
+//   is already the B operand of the PV MFMA.
+// * K is staged row-major; V is staged transposed (V^T, key-major rows per head
+//   dimension) by a 4x4 register transpose, so every MFMA operand is one
+//   ds_read_b128.  The key order inside each 16-key group of V^T follows the
+//   MFMA's k order of P^T.  Rows are padded by 16 bytes so the operand reads
+//   are conflict-free, and 16-byte chunks are XOR-swizzled by (row / 32) to
+//   spread the transposing writes; that key is uniform across each read
+//   instruction, so reads keep immediate offsets.
+// * Keys advance in tiles of 32 (head size 128) or 64 (head size 64).
+// * K/V tiles are double-buffered in LDS, one barrier per tile; the next
+//   tile's global loads are in flight while the current tile computes.
+// * Online softmax in the exp2 domain, the scale folded into the exponent's
+//   FMA; per-key masks only on boundary tiles, written as -inf in place.  O is rescaled only when a row's running max grows by more
+//   than 2^8 (the final division uses the same max, so the result is unchanged).
+// * GroupQueryAttention present rows of the new keys are stored by the
+//   workgroup whose queries sit at those positions, while the rows pass
+//   through registers.
+#include "olk_internal.h"
+
+namespace olk {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <typename T> struct FV;
+template <> struct FV<bf16> { typedef bf16x8 v8; typedef bf16x4 v4; };
+template <> struct FV<f16> { typedef f16x8 v8; typedef f16x4 v4; };
+
+__device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mma(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+constexpr int kThreads = 256;
+constexpr int kSlots = 128;  // row slots per workgroup (4 wavefronts x 32)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kRescale = 8.0f;
+
+template <typename T> __device__ __forceinline__ float lo16(uint32_t w);
+template <> __device__ __forceinline__ float lo16<bf16>(uint32_t w) { return __uint_as_float(w << 16); }
+template <> __device__ __forceinline__ float lo16<f16>(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)(w & 0xffff));
+}
+template <typename T> __device__ __forceinline__ float hi16(uint32_t w);
+template <> __device__ __forceinline__ float hi16<bf16>(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+template <> __device__ __forceinline__ float hi16<f16>(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)(w >> 16));
+}
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// tanh x = 1 - 2 / (e^{2x} + 1); saturates to +-1 without NaN.
+__device__ __forceinline__ float tanh_e(float x) {
+  return 1.0f - 2.0f * __builtin_amdgcn_rcpf(ex2(x * (2.0f * kLog2e)) + 1.0f);
+}
+
+// Position of key k (0 <= k < 16) inside its 16-key group of a V^T row: the
+// group stores keys {0-3, 8-11, 4-7, 12-15}, so the 8 keys that lane half h
+// supplies to one 16-key MFMA step (4h..4h+3 and 8+4h..8+4h+3) are contiguous.
+__device__ __forceinline__ int quad_slot(int qq) { return ((qq & 1) << 1) | (qq >> 1); }
+
+struct FPlan {
+  int GH, n_hg, QW, n_qt;
+  int xcd_remap;
+  int bias_vec;
+  int fuse_present;
+};
+
+template <typename T, int D, bool BIAS, bool SOFTCAP>
+__global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Params p, FPlan pl) {
+  typedef typename FV<T>::v8 vec8;
+  constexpr int CH = D / 8;             // 16-byte chunks per K/V row
+  constexpr int QPW = 64 / CH;          // key quads per wavefront in the loader
+  constexpr int BN = 64;                // keys per tile
+  constexpr int NQ = BN / 4;            // key quads per tile
+  constexpr int KB = BN / 32;           // 32-key blocks per tile
+  constexpr int NST = BN / 16;          // 16-key PV steps per tile
+  constexpr int NKS = D / 16;           // QK^T k-steps
+  constexpr int NDB = D / 32;           // 32-wide output blocks
+  constexpr int KST = D + 8;            // K row stride (elements)
+  constexpr int VST = BN + 8;           // V^T row stride (elements)
+  constexpr int NCH_V = BN / 8;         // 16-byte chunks per V^T row
+  __shared__ __attribute__((aligned(16))) T klds[2][BN * KST];
+  __shared__ __attribute__((aligned(16))) T vlds[2][D * VST];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, col = lane & 31;
+
+  // ---- workgroup -> (q tile, b, g, hg); late (heavy) query tiles first ----
+  const int n_bg = p.B * p.Hkv * pl.n_hg;
+  const int wid = blockIdx.x;
+  int bg, qrank;
+  if (pl.xcd_remap) {  // ids go round-robin over 8 XCDs: keep one (b, g) on one XCD
+    const int per = n_bg / 8, xcd = wid & 7, k = wid >> 3;
+    qrank = k / per;
+    bg = (k % per) * 8 + xcd;
+  } else {
+    qrank = wid / n_bg;
+    bg = wid % n_bg;
+  }
+  const int qt = pl.n_qt - 1 - qrank;
+  const int hg = bg % pl.n_hg;
+  const int g = (bg / pl.n_hg) % p.Hkv;
+  const int b = bg / (pl.n_hg * p.Hkv);
+  const Seq s = seq_info(p, b);
+  const int i0 = qt * pl.QW;
+  const int i_last = min(i0 + pl.QW, p.S) - 1;
+  const int pos_min = s.qoff + i0, pos_max = s.qoff + i_last;
+  int hi = p.pad_add ? s.total : s.valid;
+  if (p.causal) hi = min(hi, pos_max + 1);
+  const int lo = p.window > 0 ? max(0, pos_min - p.window + 1) : 0;
+  const int kt0 = lo / BN, kt1 = (hi + BN - 1) / BN;
+
+  // ---- this lane's row slot ----
+  const int slot = wave * 32 + col;
+  const int row_i = i0 + slot / pl.GH;
+  const int row_h = g * p.G + hg * pl.GH + slot % pl.GH;
+  const bool row_ok = row_i < p.S;
+  const int row_pos = s.qoff + row_i;
+  const bool wave_active = i0 + (wave * 32) / pl.GH < p.S;
+
+  // ---- Q^T operand (B of S^T = K Q^T): slot col, d = 16 ks + 8 half + e ----
+  vec8 qreg[NKS];
+  {
+    const T *qr = (const T *)p.q + b * p.q_sb + (int64_t)(row_ok ? row_i : 0) * p.q_ss +
+                  row_h * p.q_sh;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int d0 = ks * 16 + half * 8;
+      uint4 raw = make_uint4(0, 0, 0, 0);
+      if (row_ok) raw = *(const uint4 *)(qr + d0);
+      if (p.proj_bias && row_ok) {
+        const uint4 braw = *(const uint4 *)((const T *)p.proj_bias + row_h * D + d0);
+        const uint32_t *w = (const uint32_t *)&raw, *bw = (const uint32_t *)&braw;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qreg[ks][2 * e] = (T)(lo16<T>(w[e]) + lo16<T>(bw[e]));
+          qreg[ks][2 * e + 1] = (T)(hi16<T>(w[e]) + hi16<T>(bw[e]));
+        }
+      } else {
+        qreg[ks] = __builtin_bit_cast(vec8, raw);
+      }
+    }
+  }
+
+  // ---- staging: thread owns key quad q (4 keys) x 16-byte chunk c; at head
+  // size 64 the upper half of the workgroup has no quad to stage ----
+  const int ql = lane % QPW, c = lane / QPW;
+  const int q = wave * QPW + ql;                 // quad index within the tile
+  const bool stager = q < NQ;
+  const int vslot = 16 * (q >> 2) + 4 * quad_slot(q & 3);  // V^T slot of the quad's key 0
+  // V^T column offset of the quad: chunk XOR-swizzled by (row / 32) = c / 4,
+  // which is the same for all 8 rows a thread writes
+  const int vchunk_off = (((vslot >> 3) ^ (2 * ((c >> 2) & (NCH_V / 2 - 1)))) * 8) + (vslot & 7);
+  const T *kpast = (const T *)p.past_k + ((int64_t)b * p.Hkv + g) * p.past_rows * D;
+  const T *vpast = (const T *)p.past_v + ((int64_t)b * p.Hkv + g) * p.past_rows * D;
+  const T *knew = (const T *)p.k + b * p.k_sb + g * p.k_sh;
+  const T *vnew = (const T *)p.v + b * p.v_sb + g * p.v_sh;
+  const bool fuse = pl.fuse_present && hg == 0;
+  const int own_lo = s.past + i0, own_hi = s.past + i_last + 1;
+  T *pres_k = (T *)p.present_k + ((int64_t)b * p.Hkv + g) * p.T * D;
+  T *pres_v = (T *)p.present_v + ((int64_t)b * p.Hkv + g) * p.T * D;
+  uint4 kreg[4], vreg[4];
+
+  // Source row of key j: the past buffer below past_b, the new K/V above.
+  // Whole tiles inside one source use a uniform base plus 32-bit lane offsets.
+  auto load_rows = [&](int kt, const T *pastp, const T *newp, int64_t new_ss, uint4 *buf) {
+    if (!stager) return;
+    const int j0 = kt * BN;
+    const bool full = j0 >= lo && j0 + BN <= hi;
+    if (full && j0 >= s.past) {
+      const char *base = (const char *)(newp + (int64_t)(j0 - s.past) * new_ss);
+      const uint32_t rs = (uint32_t)new_ss * (uint32_t)sizeof(T);
+      const uint32_t off = (uint32_t)(4 * q) * rs + (uint32_t)c * 16u;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) buf[u] = *(const uint4 *)(base + off + u * rs);
+    } else if (full && j0 + BN <= s.past) {
+      const char *base = (const char *)(pastp + (int64_t)j0 * D);
+      const uint32_t off = ((uint32_t)(4 * q) * D + (uint32_t)c * 8u) * (uint32_t)sizeof(T);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) buf[u] = *(const uint4 *)(base + off + u * D * sizeof(T));
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = j0 + 4 * q + u;
+        const T *src = j >= s.past ? newp + (int64_t)(j - s.past) * new_ss : pastp + (int64_t)j * D;
+        if (j >= lo && j < hi) buf[u] = *(const uint4 *)(src + c * 8);
+        else buf[u] = make_uint4(0, 0, 0, 0);  // outside the key range: zeros, never NaN
+      }
+    }
+  };
+  auto store_k = [&](int kt, int buf) {
+    if (!stager) return;
+    T *kl = klds[buf];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) *(uint4 *)&kl[(4 * q + u) * KST + c * 8] = kreg[u];
+    if (fuse && kt * BN < own_hi && kt * BN + BN > own_lo) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = kt * BN + 4 * q + u;
+        if (j >= own_lo && j < own_hi)
+          *(uint4 *)((char *)pres_k + ((uint32_t)j * D + (uint32_t)c * 8u) * sizeof(T)) = kreg[u];
+      }
+    }
+  };
+  // 4 keys x 8 dims -> 8 dims x 4 keys (V^T), 8 bytes per dim row
+  auto store_v = [&](int kt, int buf) {
+    if (!stager) return;
+    T *vl = vlds[buf];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t r0 = ((const uint32_t *)&vreg[0])[w], r1 = ((const uint32_t *)&vreg[1])[w];
+      const uint32_t r2 = ((const uint32_t *)&vreg[2])[w], r3 = ((const uint32_t *)&vreg[3])[w];
+#pragma unroll
+      for (int hl = 0; hl < 2; ++hl) {
+        const uint32_t sel = hl ? 0x07060302u : 0x05040100u;
+        const uint2 kk = make_uint2(__builtin_amdgcn_perm(r1, r0, sel), __builtin_amdgcn_perm(r3, r2, sel));
+        const int d = c * 8 + 2 * w + hl;
+        *(uint2 *)&vl[d * VST + vchunk_off] = kk;
+      }
+    }
+    if (fuse && kt * BN < own_hi && kt * BN + BN > own_lo) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = kt * BN + 4 * q + u;
+        if (j >= own_lo && j < own_hi)
+          *(uint4 *)((char *)pres_v + ((uint32_t)j * D + (uint32_t)c * 8u) * sizeof(T)) = vreg[u];
+      }
+    }
+  };
+
+  const float sl = p.scale * kLog2e;
+  const bool scale_pos = p.scale > 0.f;
+  const float inv_cap = SOFTCAP ? 1.0f / p.softcap : 0.f;
+  const float cap_l2 = p.softcap * kLog2e;
+  const float mfv_l2 = p.mfv * kLog2e;
+  const float mfv_raw = p.mfv / p.scale;  // the same offset before the scale (scale > 0)
+  const T *bias_row = BIAS ? (const T *)p.bias + b * p.bias_sb + row_h * p.bias_sh +
+                                 (int64_t)(row_ok ? row_i : 0) * p.T
+                           : nullptr;
+
+  f32x16 o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+  float m = kNegInf, l = 0.f;
+
+  // S^T of one tile: KB blocks of 32 keys
+  auto qk = [&](int buf, f32x16 (&sacc)[KB]) {
+    const T *kl = klds[buf];
+    const f32x16 zero = {};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const vec8 a = *(const vec8 *)&kl[(kb * 32 + col) * KST + ks * 16 + half * 8];
+        sacc[kb] = mma(a, qreg[ks], ks == 0 ? zero : sacc[kb]);
+      }
+    }
+  };
+
+  // Softmax and PV of one tile.  With bias or softcap (GENERAL) the scores
+  // are rewritten into the log2 domain; otherwise they stay raw (scale > 0,
+  // folded into the exponent's FMA) and masking only writes -inf in place, so
+  // masked and unmasked tiles share one body.
+  auto softmax_pv = [&](int kt, int buf, f32x16 (&sacc)[KB], bool masked) {
+    constexpr bool GENERAL = BIAS || SOFTCAP;
+    const T *vl = vlds[buf];
+    const int j0 = kt * BN;
+    auto allowed = [&](int j) {
+      bool ok = j >= lo && j < hi;
+      if (p.causal && j > row_pos) ok = false;
+      if (p.window > 0 && j < row_pos - p.window + 1) ok = false;
+      return ok;
+    };
+    if (GENERAL) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int jb = j0 + kb * 32 + 8 * q4 + 4 * half;  // 4 consecutive keys
+          float bv[4] = {0.f, 0.f, 0.f, 0.f};
+          if (BIAS) {
+            if (pl.bias_vec && jb + 3 < p.T) {
+              const uint2 raw = *(const uint2 *)(bias_row + jb);
+              bv[0] = lo16<T>(raw.x); bv[1] = hi16<T>(raw.x);
+              bv[2] = lo16<T>(raw.y); bv[3] = hi16<T>(raw.y);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) bv[e] = jb + e < p.T ? (float)bias_row[jb + e] : 0.f;
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float t;
+            if (SOFTCAP) t = cap_l2 * tanh_e((sacc[kb][4 * q4 + e] * p.scale + bv[e]) * inv_cap);
+            else t = (sacc[kb][4 * q4 + e] * p.scale + bv[e]) * kLog2e;
+            sacc[kb][4 * q4 + e] = t;
+          }
+        }
+    }
+    if (masked) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = j0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          float t = sacc[kb][r];
+          if (p.pad_add && j >= s.pad) t += GENERAL ? mfv_l2 : mfv_raw;
+          sacc[kb][r] = allowed(j) ? t : kNegInf;
+        }
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (!GENERAL) mx *= sl;
+    const float m_new = fmaxf(m, mx);
+    const bool grow = m_new > m + kRescale;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float alpha = grow ? ex2(m - m_new) : 1.0f;
+      m = grow ? m_new : m;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    }
+    const float mu = m == kNegInf ? 0.f : m;
+    vec8 pb[NST];
+    float lsum = 0.f;
+#pragma unroll
+    for (int st = 0; st < NST; ++st)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = sacc[st >> 1][8 * (st & 1) + e];
+        const float pv = GENERAL ? ex2(x - mu) : ex2(__builtin_fmaf(x, sl, -mu));
+        lsum += pv;
+        pb[st][e] = (T)pv;
+      }
+    l += lsum;
+    // O^T += V^T P^T: lane half supplies keys 16st + {4h..4h+3, 8+4h..8+4h+3}
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int d = db * 32 + col;
+      const int swz = 2 * (db & (NCH_V / 2 - 1));  // uniform across the instruction
+#pragma unroll
+      for (int st = 0; st < NST; ++st) {
+        const vec8 a = *(const vec8 *)&vl[d * VST + (((2 * st + half) ^ swz) * 8)];
+        o[db] = mma(a, pb[st], o[db]);
+      }
+    }
+  };
+
+  if (kt0 < kt1) {
+    load_rows(kt0, kpast, knew, p.k_ss, kreg);
+    load_rows(kt0, vpast, vnew, p.v_ss, vreg);
+    store_k(kt0, 0);
+    store_v(kt0, 0);
+  }
+  __syncthreads();
+  // The next tile's loads go out first and land in the other LDS buffer
+  // after this tile's compute, so a full tile (and the other workgroup on the
+  // CU) covers their latency.
+  for (int kt = kt0; kt < kt1; ++kt) {
+    const int buf = (kt - kt0) & 1;
+    const bool more = kt + 1 < kt1;
+    if (more) {
+      load_rows(kt + 1, kpast, knew, p.k_ss, kreg);
+      load_rows(kt + 1, vpast, vnew, p.v_ss, vreg);
+    }
+    if (wave_active) {
+      f32x16 sacc[KB];
+      qk(buf, sacc);
+      const int j0 = kt * BN;
+      const bool need_mask = (p.causal && j0 + BN - 1 > pos_min) ||
+                             (p.window > 0 && j0 < pos_max - p.window + 1) || j0 + BN > hi ||
+                             j0 < lo || (p.pad_add && j0 + BN > s.pad);
+      softmax_pv(kt, buf, sacc, need_mask);
+    }
+    if (more) {
+      store_k(kt + 1, buf ^ 1);
+      store_v(kt + 1, buf ^ 1);
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: combine halves, sink, normalise, store ----
+  const float l_tot = l + __shfl_xor(l, 32, 64);
+  if (!row_ok) return;
+  float inv = 0.f;
+  if (m != kNegInf) {
+    float lt = l_tot;
+    if (p.sink) {
+      const float z = (float)((const T *)p.sink)[row_h] * kLog2e;
+      if (z > m) {
+        const float a = ex2(m - z);
+        lt = lt * a + 1.0f;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[db][r] *= a;
+      } else {
+        lt += ex2(z - m);
+      }
+    }
+    inv = 1.0f / lt;
+  }
+  T *yr = (T *)p.y + b * p.y_sb + (int64_t)row_i * p.y_ss + row_h * p.y_sh;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d = db * 32 + 8 * q4 + 4 * half;
+      typename FV<T>::v4 v4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v4[e] = (T)(o[db][4 * q4 + e] * inv);
+      *(typename FV<T>::v4 *)&yr[d] = v4;
+    }
+}
+
+int gh_for(int G) {
+  for (int gh = 32; gh >= 1; gh >>= 1)
+    if (G % gh == 0) return gh;
+  return 1;
+}
+
+template <typename T, int D>
+hipError_t launch_td(const Params &p, const FPlan &pl, hipStream_t st) {
+  const int64_t n = (int64_t)p.B * p.Hkv * pl.n_hg * pl.n_qt;
+  if (n == 0) return hipSuccess;
+  const dim3 grid((unsigned)n), block(kThreads);
+  const bool bias = p.bias != nullptr, cap = p.softcap > 0.f;
+  if (bias && cap) hipLaunchKernelGGL((flash_fwd_kernel<T, D, true, true>), grid, block, 0, st, p, pl);
+  else if (bias) hipLaunchKernelGGL((flash_fwd_kernel<T, D, true, false>), grid, block, 0, st, p, pl);
+  else if (cap) hipLaunchKernelGGL((flash_fwd_kernel<T, D, false, true>), grid, block, 0, st, p, pl);
+  else hipLaunchKernelGGL((flash_fwd_kernel<T, D, false, false>), grid, block, 0, st, p, pl);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Whether the prefill kernel writes the present rows of the new keys itself.
+bool flash_fuses_present(const Params &p) {
+  return p.op == OP_GQA && p.present_k != nullptr && p.present_v != nullptr;
+}
+
+hipError_t launch_flash(const Params &p, int dtype, hipStream_t st) {
+  FPlan pl;
+  pl.GH = gh_for(p.G);
+  pl.n_hg = p.G / pl.GH;
+  pl.QW = kSlots / pl.GH;
+  pl.n_qt = (p.S + pl.QW - 1) / pl.QW;
+  const int n_bg = p.B * p.Hkv * pl.n_hg;
+  pl.xcd_remap = n_bg % 8 == 0 ? 1 : 0;
+  pl.bias_vec = (p.T % 4 == 0 && ((uintptr_t)p.bias & 7) == 0) ? 1 : 0;
+  pl.fuse_present = flash_fuses_present(p) ? 1 : 0;
+  if (dtype == DT_BF16)
+    return p.D == 64 ? launch_td<bf16, 64>(p, pl, st) : launch_td<bf16, 128>(p, pl, st);
+  return p.D == 64 ? launch_td<f16, 64>(p, pl, st) : launch_td<f16, 128>(p, pl, st);
+}
+
+}  // namespace olk

@@ -29,6 +29,8 @@ struct Params {
   int op, causal, window;
   int pad_add;     // MultiHeadAttention: 1 = padded keys get mfv added, 0 = excluded
   int kv_inplace;  // present already holds the valid past
+  int present_past_only;  // present writer copies only rows j < past_b (the
+                          // attention kernel writes the new rows itself)
   float scale;     // score multiplier
   float softcap;   // > 0: softcap * tanh(s / softcap)
   float mfv;       // mask_filter_value

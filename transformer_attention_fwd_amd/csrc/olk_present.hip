@@ -37,6 +37,7 @@ __global__ __launch_bounds__(kThreads) void present_kernel(Params p, int esize) 
       const int j = j0 + t / row_words, w = t % row_words;
       if (j >= s.total || j >= p.T) continue;
       if (p.kv_inplace && j < s.past) continue;
+      if (p.present_past_only && j >= s.past) continue;
       const char *src;
       if (j < s.past) src = past + ((((int64_t)b * p.Hkv + g) * p.past_rows + j) * width) * esize;
       else src = cur + (b * sb + (int64_t)(j - s.past) * ss + g * sh) * esize;
@@ -50,6 +51,9 @@ __global__ __launch_bounds__(kThreads) void present_kernel(Params p, int esize) 
 
 hipError_t launch_present(const Params &p, int dtype, hipStream_t st) {
   if ((!p.present_k && !p.present_v) || p.B == 0 || p.T == 0) return hipSuccess;
+  // nothing left to copy: the past is already in place and the new rows are
+  // written by the attention kernel
+  if (p.present_past_only && (p.kv_inplace || p.P == 0)) return hipSuccess;
   const int esize = dtype == DT_F32 ? 4 : 2;
   dim3 grid((p.T + kRowsPerBlock - 1) / kRowsPerBlock, p.Hkv, p.B);
   if ((p.D * esize) % 4 == 0 && (p.Dv * esize) % 4 == 0)

@@ -472,6 +472,8 @@ bool tiled_supports(const Params &p, int dtype) {
   if (!aligned16(p.q) || !aligned16(p.k) || !aligned16(p.v) || !aligned16(p.y)) return false;
   if (p.P > 0 && (!aligned16(p.past_k) || !aligned16(p.past_v))) return false;
   if (p.proj_bias && !aligned16(p.proj_bias)) return false;
+  // without bias or softcap the prefill kernel folds a positive scale into exp2
+  if (!(p.scale > 0.f) && !p.bias && !(p.softcap > 0.f)) return false;
   return true;
 }
 
