@@ -19,6 +19,9 @@ hipError_t launch_tiled(const Params &p, int dtype, hipStream_t st);
 hipError_t launch_tiled_split(const Params &p, int dtype, int split_tiles, float *ws,
                               hipStream_t st);
 bool tiled_supports(const Params &p, int dtype);
+bool decode_supports(const Params &p, int dtype);
+hipError_t launch_decode(const Params &p, int dtype, int split_keys, int n_split, float *ws,
+                         hipStream_t st);
 }  // namespace olk
 
 namespace {
@@ -257,6 +260,7 @@ olk_status olk_attention_decode(const olk_attn_desc *desc, const olk_attn_io *io
   const olk_status st = validate(desc, io);
   if (st != OLK_OK) return st;
   if ((int64_t)desc->batch * desc->q_seq > 65535) return OLK_E_UNSUPPORTED;
+  if (n_splits(desc) > 4096) return OLK_E_UNSUPPORTED;  // combine kernel's weight buffer
   const size_t need = olk_workspace_bytes(desc);
   if (need && (!workspace || workspace_bytes < need)) return OLK_E_WORKSPACE;
   if (((uintptr_t)workspace & 15) != 0) return OLK_E_WORKSPACE;
@@ -267,7 +271,10 @@ olk_status olk_attention_decode(const olk_attn_desc *desc, const olk_attn_io *io
   const int n_split = n_splits(desc);
   const bool tiled_ok = olk::tiled_supports(p, desc->dtype);
   if (desc->kernel == OLK_KERNEL_TILED && !tiled_ok) return OLK_E_UNSUPPORTED;
-  if (desc->kernel != OLK_KERNEL_GENERIC && tiled_ok) {
+  if (desc->kernel != OLK_KERNEL_GENERIC && tiled_ok && olk::decode_supports(p, desc->dtype)) {
+    e = olk::launch_decode(p, desc->dtype, kSplitKeys, n_split, (float *)workspace, s);
+    g_last_kernel = "olk_decode_split+combine";
+  } else if (desc->kernel != OLK_KERNEL_GENERIC && tiled_ok) {
     e = olk::launch_tiled_split(p, desc->dtype, kSplitKeys / 64, (float *)workspace, s);
     g_last_kernel = "olk_tiled_split+combine";
   } else {

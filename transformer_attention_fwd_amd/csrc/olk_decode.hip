@@ -1,0 +1,317 @@
+// Split-KV decode for gfx950: a few query rows (G heads x S queries <= 16 per
+// KV head) against a long key sequence.  HBM-bound: every cached key row is
+// read once per (batch, KV head) and serves all G query heads of the group.
+//
+// Same result as the prefill path (onnx-light-cpu Python API "Custom
+// operators", "Microsoft GroupQueryAttention": grouped heads, causal / local
+// window masks, head_sink; onnx-light reference kernels header page, "class
+// Attention"); the decomposition is ours:
+//
+// * A workgroup owns one split (a range of SPLIT keys) of one (batch, KV head);
+//   its 4 wavefronts take interleaved 16-key steps of the split.
+// * QK^T: v_mfma_f32_16x16x32 with K loaded from global memory straight into
+//   the A operand (16 keys x 32 dims, 16 bytes per lane) and Q^T held in VGPRs
+//   as the B operand (16 columns = the row slots (query, head)).
+// * The S^T accumulator puts each row slot's 16 scores in 4 lanes; the online
+//   softmax (exp2 domain, lazy rescale) reduces across them with lane swaps.
+// * PV on the VALU: P goes through a 1 KB LDS buffer per wavefront and is
+//   read back as broadcasts; lanes own 4 head dimensions of one key (two keys
+//   per instruction), so V rows are read fully coalesced and never transposed.
+// * The next step's K and V are in flight while the current step computes;
+//   waves stay small so many of them per CU keep enough bytes in flight.
+// * The 4 wavefronts merge (m, l, O) through LDS and write one partial record
+//   [m (natural log), l, -, -, O[Dv]] per (row, split); the combine kernel
+//   merges the splits and adds the sink.
+#include "olk_internal.h"
+
+namespace olk {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T> struct DV;
+template <> struct DV<bf16> { typedef bf16x8 v8; };
+template <> struct DV<f16> { typedef f16x8 v8; };
+
+__device__ __forceinline__ f32x4 mma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+template <typename T> __device__ __forceinline__ float lo16(uint32_t w);
+template <> __device__ __forceinline__ float lo16<bf16>(uint32_t w) { return __uint_as_float(w << 16); }
+template <> __device__ __forceinline__ float lo16<f16>(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)(w & 0xffff));
+}
+template <typename T> __device__ __forceinline__ float hi16(uint32_t w);
+template <> __device__ __forceinline__ float hi16<bf16>(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+template <> __device__ __forceinline__ float hi16<f16>(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)(w >> 16));
+}
+
+constexpr int kThreads = 256;
+constexpr int kStep = 16;  // keys per wavefront step
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kRescale = 8.0f;
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// x of lanes l and l ^ 32 combined (v_permlane32_swap with both operands x).
+__device__ __forceinline__ float max32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+struct DPlan {
+  int n_split;     // splits per (batch, KV head)
+  int split_keys;  // keys per split (multiple of 4 * kStep)
+  float *ws;       // records [m, l, -, -, O[Dv]] per (row, split)
+};
+
+// NR: row slots (G * S) rounded up to a power of two <= 16.
+template <typename T, int D, int NR>
+__global__ __launch_bounds__(kThreads) void decode_kernel(Params p, DPlan pl) {
+  typedef typename DV<T>::v8 vec8;
+  constexpr int NKS = D / 32;  // k-steps of QK^T (32 dims each)
+  constexpr int DPL = D / 32;  // head dims per lane in PV (lanes 0-31 span D)
+  __shared__ __attribute__((aligned(16))) float pbuf[4][16 * kStep];     // P per wave: [slot][key]
+  __shared__ __attribute__((aligned(16))) float mrg_ml[4][2][16];        // per-wave m, l per slot
+  __shared__ __attribute__((aligned(16))) float mrg_o[4][NR][D];         // per-wave O
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int split = blockIdx.x % pl.n_split;
+  const int bg = blockIdx.x / pl.n_split;
+  const int g = bg % p.Hkv, b = bg / p.Hkv;
+  const Seq s = seq_info(p, b);
+  const int nrows = p.G * p.S;
+
+  // key range of the workgroup: union over its rows, cut to the split
+  const int pos_min = s.qoff, pos_max = s.qoff + p.S - 1;
+  int hi = p.pad_add ? s.total : s.valid;
+  if (p.causal) hi = min(hi, pos_max + 1);
+  int lo = p.window > 0 ? max(0, pos_min - p.window + 1) : 0;
+  const int sp_lo = max(lo, split * pl.split_keys);
+  const int sp_hi = min(hi, (split + 1) * pl.split_keys);
+  const int base = (sp_lo / kStep) * kStep;
+  const int n_steps = sp_lo < sp_hi ? (sp_hi - base + kStep - 1) / kStep : 0;
+
+  // ---- Q^T operand: column n = lane % 16 is row slot n = (query n / G, head n % G) ----
+  const int n = lane & 15, kq = lane >> 4;
+  const int row_q = n / p.G, row_h = g * p.G + n % p.G;
+  const bool col_ok = n < nrows;
+  const int col_pos = s.qoff + row_q;
+  vec8 qreg[NKS];
+  {
+    const T *qr = (const T *)p.q + b * p.q_sb + (int64_t)(col_ok ? row_q : 0) * p.q_ss +
+                  (col_ok ? row_h : 0) * p.q_sh;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      uint4 raw = make_uint4(0, 0, 0, 0);
+      if (col_ok) raw = *(const uint4 *)(qr + ks * 32 + kq * 8);
+      qreg[ks] = __builtin_bit_cast(vec8, raw);
+    }
+  }
+
+  const T *kpast = (const T *)p.past_k + ((int64_t)b * p.Hkv + g) * p.past_rows * D;
+  const T *vpast = (const T *)p.past_v + ((int64_t)b * p.Hkv + g) * p.past_rows * D;
+  const T *knew = (const T *)p.k + b * p.k_sb + g * p.k_sh;
+  const T *vnew = (const T *)p.v + b * p.v_sb + g * p.v_sh;
+  auto krow = [&](int j) { return j < s.past ? kpast + (int64_t)j * D : knew + (int64_t)(j - s.past) * p.k_ss; };
+  auto vrow = [&](int j) { return j < s.past ? vpast + (int64_t)j * D : vnew + (int64_t)(j - s.past) * p.v_ss; };
+
+  // per-step registers: K (A operand: key lane % 16, dims 32 ks + 8 kq + e) and
+  // V (key 2 t + lane / 32, dims DPL * (lane % 32) + e)
+  uint4 kr[NKS];
+  uint2 vr[kStep / 2];
+  const int vcol = DPL * (lane & 31), vpar = lane >> 5;
+  static_assert(DPL == 4 || DPL == 2, "head size 64 or 128");
+  auto load_step = [&](int st, uint4 (&kk)[NKS], uint2 (&vv)[kStep / 2]) {
+    const int j0 = base + (wave + 4 * st) * kStep;
+    const int jk = j0 + n;  // this lane's K row (lane % 16)
+    const bool kin = jk >= sp_lo && jk < sp_hi;
+    const T *ks = krow(kin ? jk : sp_lo);
+#pragma unroll
+    for (int s2 = 0; s2 < NKS; ++s2)
+      kk[s2] = kin ? *(const uint4 *)(ks + s2 * 32 + kq * 8) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < kStep / 2; ++t) {
+      const int jv = j0 + 2 * t + vpar;
+      const bool vin = jv >= sp_lo && jv < sp_hi;
+      if (DPL == 4) {
+        vv[t] = vin ? *(const uint2 *)(vrow(vin ? jv : sp_lo) + vcol) : make_uint2(0, 0);
+      } else {
+        const uint32_t w = vin ? *(const uint32_t *)(vrow(vin ? jv : sp_lo) + vcol) : 0u;
+        vv[t] = make_uint2(w, 0);
+      }
+    }
+  };
+
+  float m = kNegInf, l = 0.f;
+  float o[NR][DPL];
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) o[r][e] = 0.f;
+  const float sl = p.scale * kLog2e;
+
+  const int my_steps = n_steps > wave ? (n_steps - wave + 3) / 4 : 0;
+  uint4 kn[NKS];
+  uint2 vn[kStep / 2];
+  if (my_steps > 0) load_step(0, kr, vr);
+  for (int it = 0; it < my_steps; ++it) {
+    if (it + 1 < my_steps) load_step(it + 1, kn, vn);
+    const int j0 = base + (wave + 4 * it) * kStep;
+    // S^T (16 keys x 16 slots)
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s2 = 0; s2 < NKS; ++s2) sacc = mma16(__builtin_bit_cast(vec8, kr[s2]), qreg[s2], sacc);
+    // scores of slot n for keys j0 + 4 kq + r, log2 domain, masked
+    float t4[4];
+    float mx = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = j0 + 4 * kq + r;
+      float t = sacc[r] * sl;
+      bool ok = j >= sp_lo && j < sp_hi;
+      if (p.causal && j > col_pos) ok = false;
+      if (p.window > 0 && j < col_pos - p.window + 1) ok = false;
+      if (p.pad_add && j >= s.pad) t += p.mfv * kLog2e;
+      t4[r] = ok ? t : kNegInf;
+      mx = fmaxf(mx, t4[r]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = max32(mx);
+    const float m_new = fmaxf(m, mx);
+    const bool grow = m_new > m + kRescale;
+    const float alpha = grow ? ex2(m - m_new) : 1.0f;  // same in the 4 lanes of slot n
+    if (grow) m = m_new;
+    const float mu = m == kNegInf ? 0.f : m;
+    float pv[4], lsum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pv[r] = ex2(t4[r] - mu);
+      lsum += pv[r];
+    }
+    l = l * alpha + lsum;  // lane-local partial of slot n
+    // P of this step for the broadcast reads of the PV loop (same wavefront:
+    // LDS operations of one wave complete in order)
+    *(float4 *)&pbuf[wave][n * kStep + 4 * kq] = make_float4(pv[0], pv[1], pv[2], pv[3]);
+    // O rows scale by their slot's factor, which lane r holds
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const float ar = __builtin_amdgcn_readlane(__float_as_int(alpha), r);
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) o[r][e] *= __int_as_float(ar);
+    }
+    // PV: this lane accumulates keys 2t + vpar for its DPL dims
+#pragma unroll
+    for (int t = 0; t < kStep / 2; ++t) {
+      const int kk = 2 * t + vpar;
+      float vf[DPL];
+      if (DPL == 4) {
+        vf[0] = lo16<T>(vr[t].x); vf[1] = hi16<T>(vr[t].x);
+        vf[2] = lo16<T>(vr[t].y); vf[3] = hi16<T>(vr[t].y);
+      } else {
+        vf[0] = lo16<T>(vr[t].x); vf[1] = hi16<T>(vr[t].x);
+      }
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const float w = pbuf[wave][r * kStep + kk];
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) o[r][e] = __builtin_fmaf(w, vf[e], o[r][e]);
+      }
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < NKS; ++s2) kr[s2] = kn[s2];
+#pragma unroll
+    for (int t = 0; t < kStep / 2; ++t) vr[t] = vn[t];
+  }
+
+  // ---- wave partials -> LDS: m, l per slot (from the 4 lanes of each slot) ----
+  float lsl = l + __shfl_xor(l, 16, 64);
+  lsl = sum32(lsl);
+  if (lane < 16) {
+    mrg_ml[wave][0][lane] = m;
+    mrg_ml[wave][1][lane] = lsl;
+  }
+  // O rows: lanes of parity 0 and 1 hold different keys of the same dims
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) {
+      const float v = sum32(o[r][e]);
+      if (lane < 32) mrg_o[wave][r][vcol + e] = v;
+    }
+  __syncthreads();
+
+  // ---- merge the 4 wavefronts; one record per valid row slot ----
+  for (int r = wave; r < NR; r += 4) {
+    if (r >= nrows) continue;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, mrg_ml[w][0][r]);
+    float sc[4], L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = mrg_ml[w][0][r];
+      sc[w] = mw == kNegInf ? 0.f : ex2(mw - M);
+      L += sc[w] * mrg_ml[w][1][r];
+    }
+    const int rq = r / p.G, rh = g * p.G + r % p.G;
+    const int64_t row = ((int64_t)b * p.S + rq) * p.Hq + rh;
+    float *out = pl.ws + (row * pl.n_split + split) * (int64_t)(D + 4);
+    if (lane == 0) {
+      out[0] = M == kNegInf ? kNegInf : M * kLn2;
+      out[1] = M == kNegInf ? 0.f : L;
+    }
+    for (int d = lane; d < D; d += 64) {
+      float acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) acc += sc[w] * mrg_o[w][r][d];
+      out[4 + d] = M == kNegInf ? 0.f : acc;
+    }
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_nr(const Params &p, const DPlan &pl, int nr, dim3 grid, hipStream_t st) {
+  if (nr <= 4) hipLaunchKernelGGL((decode_kernel<T, D, 4>), grid, dim3(kThreads), 0, st, p, pl);
+  else if (nr <= 8) hipLaunchKernelGGL((decode_kernel<T, D, 8>), grid, dim3(kThreads), 0, st, p, pl);
+  else hipLaunchKernelGGL((decode_kernel<T, D, 16>), grid, dim3(kThreads), 0, st, p, pl);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// The decode kernel takes every (query, head) row of one KV head in 16 slots.
+bool decode_supports(const Params &p, int dtype) {
+  return (dtype == DT_F16 || dtype == DT_BF16) && p.D == p.Dv && (p.D == 64 || p.D == 128) &&
+         p.G * p.S <= 16 && !p.bias && !(p.softcap > 0.f) && p.scale > 0.f && !p.proj_bias;
+}
+
+hipError_t launch_decode(const Params &p, int dtype, int split_keys, int n_split, float *ws,
+                         hipStream_t st) {
+  DPlan pl;
+  pl.n_split = n_split;
+  pl.split_keys = split_keys;
+  pl.ws = ws;
+  const int64_t n = (int64_t)p.B * p.Hkv * n_split;
+  if (n == 0) return hipSuccess;
+  const dim3 grid((unsigned)n);
+  const int nr = p.G * p.S;
+  if (dtype == DT_BF16)
+    return p.D == 64 ? launch_nr<bf16, 64>(p, pl, nr, grid, st) : launch_nr<bf16, 128>(p, pl, nr, grid, st);
+  return p.D == 64 ? launch_nr<f16, 64>(p, pl, nr, grid, st) : launch_nr<f16, 128>(p, pl, nr, grid, st);
+}
+
+}  // namespace olk

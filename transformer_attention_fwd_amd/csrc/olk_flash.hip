@@ -72,6 +72,17 @@ template <> __device__ __forceinline__ float hi16<f16>(uint32_t w) {
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Value of lane ^ 32 combined with this lane's, via v_permlane32_swap (with
+// both operands x, the two results hold x of lane l and of lane l ^ 32).
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // tanh x = 1 - 2 / (e^{2x} + 1); saturates to +-1 without NaN.
 __device__ __forceinline__ float tanh_e(float x) {
   return 1.0f - 2.0f * __builtin_amdgcn_rcpf(ex2(x * (2.0f * kLog2e)) + 1.0f);
@@ -262,6 +273,25 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Params p, FPlan 
                                  (int64_t)(row_ok ? row_i : 0) * p.T
                            : nullptr;
 
+  // 4 bias values of keys jb..jb+3 as raw 16-bit pairs (zeros past T)
+  auto bias4 = [&](int jb) {
+    if (pl.bias_vec && jb + 3 < p.T) return *(const uint2 *)(bias_row + jb);
+    uint16_t e4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      e4[e] = jb + e < p.T ? __builtin_bit_cast(uint16_t, bias_row[jb + e]) : (uint16_t)0;
+    return make_uint2(e4[0] | ((uint32_t)e4[1] << 16), e4[2] | ((uint32_t)e4[3] << 16));
+  };
+  // At head size 64 the bias of the next tile is prefetched with its K/V.
+  constexpr bool BPRE = BIAS && D == 64;
+  uint2 bcur[BPRE ? KB : 1][4], bnext[BPRE ? KB : 1][4];
+  auto load_bias = [&](int kt, uint2 (&bb)[BPRE ? KB : 1][4]) {
+#pragma unroll
+    for (int kb = 0; kb < (BPRE ? KB : 1); ++kb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) bb[kb][q4] = bias4(kt * BN + kb * 32 + 8 * q4 + 4 * half);
+  };
+
   f32x16 o[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -305,14 +335,9 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Params p, FPlan 
           const int jb = j0 + kb * 32 + 8 * q4 + 4 * half;  // 4 consecutive keys
           float bv[4] = {0.f, 0.f, 0.f, 0.f};
           if (BIAS) {
-            if (pl.bias_vec && jb + 3 < p.T) {
-              const uint2 raw = *(const uint2 *)(bias_row + jb);
-              bv[0] = lo16<T>(raw.x); bv[1] = hi16<T>(raw.x);
-              bv[2] = lo16<T>(raw.y); bv[3] = hi16<T>(raw.y);
-            } else {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) bv[e] = jb + e < p.T ? (float)bias_row[jb + e] : 0.f;
-            }
+            const uint2 raw = BPRE ? bcur[BPRE ? kb : 0][q4] : bias4(jb);
+            bv[0] = lo16<T>(raw.x); bv[1] = hi16<T>(raw.x);
+            bv[2] = lo16<T>(raw.y); bv[3] = hi16<T>(raw.y);
           }
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -339,7 +364,7 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Params p, FPlan 
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = max_halves(mx);
     if (!GENERAL) mx *= sl;
     const float m_new = fmaxf(m, mx);
     const bool grow = m_new > m + kRescale;
@@ -381,6 +406,7 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Params p, FPlan 
   if (kt0 < kt1) {
     load_rows(kt0, kpast, knew, p.k_ss, kreg);
     load_rows(kt0, vpast, vnew, p.v_ss, vreg);
+    if (BPRE) load_bias(kt0, bcur);
     store_k(kt0, 0);
     store_v(kt0, 0);
   }
@@ -394,6 +420,7 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Params p, FPlan 
     if (more) {
       load_rows(kt + 1, kpast, knew, p.k_ss, kreg);
       load_rows(kt + 1, vpast, vnew, p.v_ss, vreg);
+      if (BPRE) load_bias(kt + 1, bnext);
     }
     if (wave_active) {
       f32x16 sacc[KB];
@@ -407,12 +434,18 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Params p, FPlan 
     if (more) {
       store_k(kt + 1, buf ^ 1);
       store_v(kt + 1, buf ^ 1);
+      if (BPRE) {
+#pragma unroll
+        for (int kb = 0; kb < (BPRE ? KB : 1); ++kb)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) bcur[kb][q4] = bnext[kb][q4];
+      }
     }
     __syncthreads();
   }
 
   // ---- epilogue: combine halves, sink, normalise, store ----
-  const float l_tot = l + __shfl_xor(l, 32, 64);
+  const float l_tot = sum_halves(l);
   if (!row_ok) return;
   float inv = 0.f;
   if (m != kNegInf) {

@@ -186,35 +186,45 @@ __global__ __launch_bounds__(kWave) void generic_split_kernel(Params p, int chun
 
 // Merge of the split partials of one row, with the sink in the denominator:
 // M = max(max_s m_s, z); Y = sum_s e^{m_s-M} o_s / (sum_s e^{m_s-M} l_s + e^{z-M}).
+// Lanes first take one split each (max, then one exponential per split into
+// LDS), then one dimension each, summing the weighted records.
+constexpr int kMaxSplits = 4096;
+
 template <typename T>
 __global__ __launch_bounds__(kWave) void combine_kernel(Params p, int n_split, const float *ws) {
+  __shared__ float wgt[kMaxSplits];
   const int h = blockIdx.x;
   const int b = blockIdx.y / p.S, i = blockIdx.y % p.S;
+  const int lane = threadIdx.x;
   const int64_t row = ((int64_t)b * p.S + i) * p.Hq + h;
   const int64_t rec = p.Dv + 4;
   const float *part = ws + row * n_split * rec;
   float M = kNegInf;
-  for (int sp = 0; sp < n_split; ++sp) M = fmaxf(M, part[sp * rec]);
+  for (int sp = lane; sp < n_split; sp += kWave) M = fmaxf(M, part[sp * rec]);
+  M = wave_max(M);
   T *yr = (T *)p.y + b * p.y_sb + (int64_t)i * p.y_ss + h * p.y_sh;
   if (M == kNegInf) {  // no allowed key: zeros
-    for (int d = threadIdx.x; d < p.Dv; d += kWave) yr[d] = from_f32<T>(0.f);
+    for (int d = lane; d < p.Dv; d += kWave) yr[d] = from_f32<T>(0.f);
     return;
   }
   float z = kNegInf;
   if (p.sink) z = to_f32(((const T *)p.sink)[h]);
   const float Mf = fmaxf(M, z);
-  float l = p.sink ? expf(z - Mf) : 0.f;
-  for (int sp = 0; sp < n_split; ++sp) {
+  float l = 0.f;
+  for (int sp = lane; sp < n_split; sp += kWave) {
     const float m = part[sp * rec];
-    if (m != kNegInf) l += part[sp * rec + 1] * expf(m - Mf);
+    const float w = m == kNegInf ? 0.f : expf(m - Mf);
+    wgt[sp] = w;
+    l += w * part[sp * rec + 1];
   }
+  l = wave_sum(l);
+  if (p.sink) l += expf(z - Mf);
+  __syncthreads();
   const float inv = 1.f / l;
-  for (int d = threadIdx.x; d < p.Dv; d += kWave) {
+  for (int d = lane; d < p.Dv; d += kWave) {
     float acc = 0.f;
-    for (int sp = 0; sp < n_split; ++sp) {
-      const float m = part[sp * rec];
-      if (m != kNegInf) acc += part[sp * rec + 4 + d] * expf(m - Mf);
-    }
+#pragma unroll 8
+    for (int sp = 0; sp < n_split; ++sp) acc += wgt[sp] * part[sp * rec + 4 + d];
     yr[d] = from_f32<T>(acc * inv);
   }
 }

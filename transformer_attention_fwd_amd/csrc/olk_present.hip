@@ -16,13 +16,17 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kRowsPerBlock = 16;
 
-// Copies rows [blockIdx.x*kRowsPerBlock, ...) of (g = blockIdx.y, b = blockIdx.z)
-// for both K (which = 0) and V (which = 1) in units of U (4 or 2 bytes).
+// Copies rows of (g = blockIdx.y, b = blockIdx.z) for both K (which = 0) and
+// V (which = 1) in units of U (4 or 2 bytes).  Row r of the launch is key
+// position j = first + r, where `first` is 0, or past_b when only the new
+// rows are written (kv_inplace); the launch covers no more rows than the mode
+// can write, so a KV-cache append costs one row per (b, g), not a cache scan.
 template <typename U>
-__global__ __launch_bounds__(kThreads) void present_kernel(Params p, int esize) {
+__global__ __launch_bounds__(kThreads) void present_kernel(Params p, int esize, int new_only) {
   const int g = blockIdx.y, b = blockIdx.z;
   const Seq s = seq_info(p, b);
-  const int j0 = blockIdx.x * kRowsPerBlock;
+  const int first = new_only ? s.past : 0;
+  const int j0 = first + blockIdx.x * kRowsPerBlock;
   for (int which = 0; which < 2; ++which) {
     char *dst_base = (char *)(which ? p.present_v : p.present_k);
     if (!dst_base) continue;
@@ -55,11 +59,15 @@ hipError_t launch_present(const Params &p, int dtype, hipStream_t st) {
   // written by the attention kernel
   if (p.present_past_only && (p.kv_inplace || p.P == 0)) return hipSuccess;
   const int esize = dtype == DT_F32 ? 4 : 2;
-  dim3 grid((p.T + kRowsPerBlock - 1) / kRowsPerBlock, p.Hkv, p.B);
+  // rows the launch must cover: the new keys only when the past is in place
+  const int new_only = p.kv_inplace ? 1 : 0;
+  const int rows = new_only ? p.L : (p.present_past_only ? p.P : p.T);
+  if (rows == 0) return hipSuccess;
+  dim3 grid((rows + kRowsPerBlock - 1) / kRowsPerBlock, p.Hkv, p.B);
   if ((p.D * esize) % 4 == 0 && (p.Dv * esize) % 4 == 0)
-    hipLaunchKernelGGL(present_kernel<uint32_t>, grid, dim3(kThreads), 0, st, p, esize);
+    hipLaunchKernelGGL(present_kernel<uint32_t>, grid, dim3(kThreads), 0, st, p, esize, new_only);
   else
-    hipLaunchKernelGGL(present_kernel<uint16_t>, grid, dim3(kThreads), 0, st, p, esize);
+    hipLaunchKernelGGL(present_kernel<uint16_t>, grid, dim3(kThreads), 0, st, p, esize, new_only);
   return hipGetLastError();
 }
 
