@@ -31,6 +31,7 @@ thread_local const char *g_last_kernel = "";
 // Keys per split of the decode path (both kernel families; a multiple of the
 // tiled kernel's 64-key tile).
 constexpr int kSplitKeys = 512;
+constexpr int kDecodeSplitKeys = 1024;  // keys per split of the dedicated decode kernel
 
 size_t esize_of(int dtype) { return dtype == OLK_F32 ? 4 : 2; }
 
@@ -211,9 +212,9 @@ olk::Params make_params(const olk_attn_desc *d, const olk_attn_io *io) {
   return p;
 }
 
-int n_splits(const olk_attn_desc *d) {
+int n_splits(const olk_attn_desc *d, int split_keys = kSplitKeys) {
   const int64_t T = (int64_t)d->past_seq + d->kv_seq;
-  const int64_t n = (T + kSplitKeys - 1) / kSplitKeys;
+  const int64_t n = (T + split_keys - 1) / split_keys;
   return n < 1 ? 1 : (int)n;
 }
 
@@ -271,8 +272,10 @@ olk_status olk_attention_decode(const olk_attn_desc *desc, const olk_attn_io *io
   const int n_split = n_splits(desc);
   const bool tiled_ok = olk::tiled_supports(p, desc->dtype);
   if (desc->kernel == OLK_KERNEL_TILED && !tiled_ok) return OLK_E_UNSUPPORTED;
+  int n_comb = n_split;
   if (desc->kernel != OLK_KERNEL_GENERIC && tiled_ok && olk::decode_supports(p, desc->dtype)) {
-    e = olk::launch_decode(p, desc->dtype, kSplitKeys, n_split, (float *)workspace, s);
+    n_comb = n_splits(desc, kDecodeSplitKeys);
+    e = olk::launch_decode(p, desc->dtype, kDecodeSplitKeys, n_comb, (float *)workspace, s);
     g_last_kernel = "olk_decode_split+combine";
   } else if (desc->kernel != OLK_KERNEL_GENERIC && tiled_ok) {
     e = olk::launch_tiled_split(p, desc->dtype, kSplitKeys / 64, (float *)workspace, s);
@@ -282,7 +285,7 @@ olk_status olk_attention_decode(const olk_attn_desc *desc, const olk_attn_io *io
     g_last_kernel = "olk_generic_split+combine";
   }
   if (e != hipSuccess) return OLK_E_HIP;
-  e = olk::launch_combine(p, desc->dtype, n_split, (const float *)workspace, s);
+  e = olk::launch_combine(p, desc->dtype, n_comb, (const float *)workspace, s);
   return e == hipSuccess ? OLK_OK : OLK_E_HIP;
 }
 

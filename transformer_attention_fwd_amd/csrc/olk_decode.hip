@@ -17,8 +17,8 @@
 // * PV on the VALU: P goes through a 1 KB LDS buffer per wavefront and is
 //   read back as broadcasts; lanes own 4 head dimensions of one key (two keys
 //   per instruction), so V rows are read fully coalesced and never transposed.
-// * The next step's K and V are in flight while the current step computes;
-//   waves stay small so many of them per CU keep enough bytes in flight.
+// * The K and V of the next two steps are in flight while a step computes;
+//   the stream is read once, with non-temporal loads.
 // * The 4 wavefronts merge (m, l, O) through LDS and write one partial record
 //   [m (natural log), l, -, -, O[Dv]] per (row, split); the combine kernel
 //   merges the splits and adds the sink.
@@ -30,6 +30,17 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+// Streaming (read-once) loads: non-temporal, so the KV stream does not evict
+// reusable lines from the caches.
+__device__ __forceinline__ uint4 ld_stream16(const char *p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4 *)p));
+}
+__device__ __forceinline__ uint2 ld_stream8(const char *p) {
+  return __builtin_bit_cast(uint2, __builtin_nontemporal_load((const u32x2 *)p));
+}
 
 template <typename T> struct DV;
 template <> struct DV<bf16> { typedef bf16x8 v8; };
@@ -84,7 +95,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p, DPlan pl) {
   typedef typename DV<T>::v8 vec8;
   constexpr int NKS = D / 32;  // k-steps of QK^T (32 dims each)
   constexpr int DPL = D / 32;  // head dims per lane in PV (lanes 0-31 span D)
-  __shared__ __attribute__((aligned(16))) float pbuf[4][16 * kStep];     // P per wave: [slot][key]
+  __shared__ __attribute__((aligned(16))) float pbuf[4][16 * kStep];     // P per wave: [slot][parity-major key]
   __shared__ __attribute__((aligned(16))) float mrg_ml[4][2][16];        // per-wave m, l per slot
   __shared__ __attribute__((aligned(16))) float mrg_o[4][NR][D];         // per-wave O
 
@@ -131,12 +142,32 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p, DPlan pl) {
 
   // per-step registers: K (A operand: key lane % 16, dims 32 ks + 8 kq + e) and
   // V (key 2 t + lane / 32, dims DPL * (lane % 32) + e)
-  uint4 kr[NKS];
-  uint2 vr[kStep / 2];
   const int vcol = DPL * (lane & 31), vpar = lane >> 5;
   static_assert(DPL == 4 || DPL == 2, "head size 64 or 128");
   auto load_step = [&](int st, uint4 (&kk)[NKS], uint2 (&vv)[kStep / 2]) {
     const int j0 = base + (wave + 4 * st) * kStep;
+    const bool full = j0 >= sp_lo && j0 + kStep <= sp_hi;
+    if (full && (j0 >= s.past || j0 + kStep <= s.past)) {
+      // the whole step from one source: uniform base + 32-bit lane offsets
+      const bool from_new = j0 >= s.past;
+      const char *kb = (const char *)(from_new ? knew + (int64_t)(j0 - s.past) * p.k_ss
+                                               : kpast + (int64_t)j0 * D);
+      const char *vb = (const char *)(from_new ? vnew + (int64_t)(j0 - s.past) * p.v_ss
+                                               : vpast + (int64_t)j0 * D);
+      const uint32_t krs = (uint32_t)(from_new ? p.k_ss : D) * (uint32_t)sizeof(T);
+      const uint32_t vrs = (uint32_t)(from_new ? p.v_ss : D) * (uint32_t)sizeof(T);
+      const uint32_t koff = (uint32_t)n * krs + (uint32_t)kq * 16u;
+#pragma unroll
+      for (int s2 = 0; s2 < NKS; ++s2)
+        kk[s2] = ld_stream16(kb + koff + s2 * 64);
+      const uint32_t voff = (uint32_t)vpar * vrs + (uint32_t)vcol * (uint32_t)sizeof(T);
+#pragma unroll
+      for (int t = 0; t < kStep / 2; ++t) {
+        if constexpr (DPL == 4) vv[t] = ld_stream8(vb + voff + 2 * t * vrs);
+        else vv[t] = make_uint2(__builtin_nontemporal_load((const uint32_t *)(vb + voff + 2 * t * vrs)), 0u);
+      }
+      return;
+    }
     const int jk = j0 + n;  // this lane's K row (lane % 16)
     const bool kin = jk >= sp_lo && jk < sp_hi;
     const T *ks = krow(kin ? jk : sp_lo);
@@ -147,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p, DPlan pl) {
     for (int t = 0; t < kStep / 2; ++t) {
       const int jv = j0 + 2 * t + vpar;
       const bool vin = jv >= sp_lo && jv < sp_hi;
-      if (DPL == 4) {
+      if constexpr (DPL == 4) {
         vv[t] = vin ? *(const uint2 *)(vrow(vin ? jv : sp_lo) + vcol) : make_uint2(0, 0);
       } else {
         const uint32_t w = vin ? *(const uint32_t *)(vrow(vin ? jv : sp_lo) + vcol) : 0u;
@@ -165,11 +196,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p, DPlan pl) {
   const float sl = p.scale * kLog2e;
 
   const int my_steps = n_steps > wave ? (n_steps - wave + 3) / 4 : 0;
-  uint4 kn[NKS];
-  uint2 vn[kStep / 2];
-  if (my_steps > 0) load_step(0, kr, vr);
-  for (int it = 0; it < my_steps; ++it) {
-    if (it + 1 < my_steps) load_step(it + 1, kn, vn);
+  // Three register buffers rotate so the loads of step it + 2 are in flight
+  // while step it computes.
+  uint4 k0[NKS], k1[NKS], k2[NKS];
+  uint2 v0[kStep / 2], v1[kStep / 2], v2[kStep / 2];
+  auto body = [&](int it, uint4 (&kr)[NKS], uint2 (&vr)[kStep / 2], uint4 (&kf)[NKS],
+                  uint2 (&vf2)[kStep / 2]) {
+    if (it + 2 < my_steps) load_step(it + 2, kf, vf2);
     const int j0 = base + (wave + 4 * it) * kStep;
     // S^T (16 keys x 16 slots)
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
@@ -203,38 +236,44 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p, DPlan pl) {
       lsum += pv[r];
     }
     l = l * alpha + lsum;  // lane-local partial of slot n
-    // P of this step for the broadcast reads of the PV loop (same wavefront:
-    // LDS operations of one wave complete in order)
-    *(float4 *)&pbuf[wave][n * kStep + 4 * kq] = make_float4(pv[0], pv[1], pv[2], pv[3]);
+    // P of this step, parity-major (key k at (k & 1) * 8 + k / 2), for the
+    // broadcast reads of the PV loop (LDS operations of one wave complete in order)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int k = 4 * kq + r;
+      pbuf[wave][n * kStep + (k & 1) * 8 + (k >> 1)] = pv[r];
+    }
     // O rows scale by their slot's factor, which lane r holds
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-      const float ar = __builtin_amdgcn_readlane(__float_as_int(alpha), r);
+      const float ar = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), r));
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) o[r][e] *= __int_as_float(ar);
+      for (int e = 0; e < DPL; ++e) o[r][e] *= ar;
     }
     // PV: this lane accumulates keys 2t + vpar for its DPL dims
 #pragma unroll
     for (int t = 0; t < kStep / 2; ++t) {
-      const int kk = 2 * t + vpar;
       float vf[DPL];
-      if (DPL == 4) {
-        vf[0] = lo16<T>(vr[t].x); vf[1] = hi16<T>(vr[t].x);
-        vf[2] = lo16<T>(vr[t].y); vf[3] = hi16<T>(vr[t].y);
-      } else {
-        vf[0] = lo16<T>(vr[t].x); vf[1] = hi16<T>(vr[t].x);
+      vf[0] = lo16<T>(vr[t].x);
+      vf[1] = hi16<T>(vr[t].x);
+      if constexpr (DPL == 4) {
+        vf[2] = lo16<T>(vr[t].y);
+        vf[3] = hi16<T>(vr[t].y);
       }
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
-        const float w = pbuf[wave][r * kStep + kk];
+        const float w = pbuf[wave][r * kStep + vpar * 8 + t];
 #pragma unroll
         for (int e = 0; e < DPL; ++e) o[r][e] = __builtin_fmaf(w, vf[e], o[r][e]);
       }
     }
-#pragma unroll
-    for (int s2 = 0; s2 < NKS; ++s2) kr[s2] = kn[s2];
-#pragma unroll
-    for (int t = 0; t < kStep / 2; ++t) vr[t] = vn[t];
+  };
+  if (my_steps > 0) load_step(0, k0, v0);
+  if (my_steps > 1) load_step(1, k1, v1);
+  for (int it = 0; it < my_steps; it += 3) {
+    body(it, k0, v0, k2, v2);
+    if (it + 1 < my_steps) body(it + 1, k1, v1, k0, v0);
+    if (it + 2 < my_steps) body(it + 2, k2, v2, k1, v1);
   }
 
   // ---- wave partials -> LDS: m, l per slot (from the 4 lanes of each slot) ----

@@ -29,7 +29,8 @@
 //   FMA; per-key masks only on boundary tiles, written as -inf in place.  O is rescaled only when a row's running max grows by more
 //   than 2^8 (the final division uses the same max, so the result is unchanged).
 // * GroupQueryAttention present rows of the new keys are stored by the
-//   workgroup whose queries sit at those positions, while the rows pass
+//   workgroup whose queries sit at those positions: with causal masking from
+//   its last two LDS tiles after the loop, otherwise while the rows pass
 //   through registers.
 #include "olk_internal.h"
 
@@ -192,6 +193,12 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Params p, FPlan 
   const T *vnew = (const T *)p.v + b * p.v_sb + g * p.v_sh;
   const bool fuse = pl.fuse_present && hg == 0;
   const int own_lo = s.past + i0, own_hi = s.past + i_last + 1;
+  // Causal: the owned rows are the last keys the loop stages (at most BN of
+  // them), so both LDS buffers still hold them afterwards and present is
+  // written once the loop is done; stores inside the loop would make every
+  // later wait for tile loads also wait for the store acknowledgements.
+  const bool fuse_end = fuse && p.causal && pl.QW <= BN;
+  const bool fuse_loop = fuse && !fuse_end;
   T *pres_k = (T *)p.present_k + ((int64_t)b * p.Hkv + g) * p.T * D;
   T *pres_v = (T *)p.present_v + ((int64_t)b * p.Hkv + g) * p.T * D;
   uint4 kreg[4], vreg[4];
@@ -228,7 +235,7 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Params p, FPlan 
     T *kl = klds[buf];
 #pragma unroll
     for (int u = 0; u < 4; ++u) *(uint4 *)&kl[(4 * q + u) * KST + c * 8] = kreg[u];
-    if (fuse && kt * BN < own_hi && kt * BN + BN > own_lo) {
+    if (fuse_loop && kt * BN < own_hi && kt * BN + BN > own_lo) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int j = kt * BN + 4 * q + u;
@@ -253,7 +260,7 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Params p, FPlan 
         *(uint2 *)&vl[d * VST + vchunk_off] = kk;
       }
     }
-    if (fuse && kt * BN < own_hi && kt * BN + BN > own_lo) {
+    if (fuse_loop && kt * BN < own_hi && kt * BN + BN > own_lo) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int j = kt * BN + 4 * q + u;
@@ -378,29 +385,29 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Params p, FPlan 
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
     }
     const float mu = m == kNegInf ? 0.f : m;
-    vec8 pb[NST];
+    // P in 16-key steps, each feeding its PV MFMAs at once, so the matrix
+    // core starts while the VALU computes the next step's exponentials.
+    // Lane half h supplies keys 16st + {4h..4h+3, 8+4h..8+4h+3}.
     float lsum = 0.f;
 #pragma unroll
-    for (int st = 0; st < NST; ++st)
+    for (int st = 0; st < NST; ++st) {
+      vec8 pb;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float x = sacc[st >> 1][8 * (st & 1) + e];
         const float pv = GENERAL ? ex2(x - mu) : ex2(__builtin_fmaf(x, sl, -mu));
         lsum += pv;
-        pb[st][e] = (T)pv;
+        pb[e] = (T)pv;
       }
-    l += lsum;
-    // O^T += V^T P^T: lane half supplies keys 16st + {4h..4h+3, 8+4h..8+4h+3}
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int d = db * 32 + col;
-      const int swz = 2 * (db & (NCH_V / 2 - 1));  // uniform across the instruction
-#pragma unroll
-      for (int st = 0; st < NST; ++st) {
+      for (int db = 0; db < NDB; ++db) {
+        const int d = db * 32 + col;
+        const int swz = 2 * (db & (NCH_V / 2 - 1));  // uniform across the instruction
         const vec8 a = *(const vec8 *)&vl[d * VST + (((2 * st + half) ^ swz) * 8)];
-        o[db] = mma(a, pb[st], o[db]);
+        o[db] = mma(a, pb, o[db]);
       }
     }
+    l += lsum;
   };
 
   if (kt0 < kt1) {
@@ -442,6 +449,32 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Params p, FPlan 
       }
     }
     __syncthreads();
+  }
+
+  // ---- present rows of the owned keys, from the last two LDS tiles ----
+  if (fuse_end && kt0 < kt1) {
+    const int n_own = own_hi - own_lo;
+    for (int t = tid; t < n_own * CH; t += kThreads) {
+      const int j = own_lo + t / CH, cc = t % CH;
+      const int kt = j / BN, bi = (kt - kt0) & 1, r = j - kt * BN;
+      *(uint4 *)((char *)pres_k + ((uint32_t)j * D + cc * 8u) * sizeof(T)) =
+          *(const uint4 *)&klds[bi][r * KST + cc * 8];
+      // V row r from V^T: element d sits at its row's swizzled key slot
+      const int slot = 16 * (r >> 4) + 4 * quad_slot((r >> 2) & 3) + (r & 3);
+      uint16_t e8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = cc * 8 + e;
+        const int chunk = (slot >> 3) ^ (2 * ((d >> 5) & (NCH_V / 2 - 1)));
+        e8[e] = __builtin_bit_cast(uint16_t, vlds[bi][d * VST + chunk * 8 + (slot & 7)]);
+      }
+      uint4 row;
+      row.x = e8[0] | ((uint32_t)e8[1] << 16);
+      row.y = e8[2] | ((uint32_t)e8[3] << 16);
+      row.z = e8[4] | ((uint32_t)e8[5] << 16);
+      row.w = e8[6] | ((uint32_t)e8[7] << 16);
+      *(uint4 *)((char *)pres_v + ((uint32_t)j * D + cc * 8u) * sizeof(T)) = row;
+    }
   }
 
   // ---- epilogue: combine halves, sink, normalise, store ----
