@@ -105,9 +105,7 @@ template <typename T, int D, bool BIAS, bool SOFTCAP>
 __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Params p, FPlan pl) {
   typedef typename FV<T>::v8 vec8;
   constexpr int CH = D / 8;             // 16-byte chunks per K/V row
-  constexpr int QPW = 64 / CH;          // key quads per wavefront in the loader
   constexpr int BN = 64;                // keys per tile
-  constexpr int NQ = BN / 4;            // key quads per tile
   constexpr int KB = BN / 32;           // 32-key blocks per tile
   constexpr int NST = BN / 16;          // 16-key PV steps per tile
   constexpr int NKS = D / 16;           // QK^T k-steps
@@ -180,13 +178,23 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Params p, FPlan 
 
   // ---- staging: thread owns key quad q (4 keys) x 16-byte chunk c; at head
   // size 64 the upper half of the workgroup has no quad to stage ----
-  const int ql = lane % QPW, c = lane / QPW;
-  const int q = wave * QPW + ql;                 // quad index within the tile
-  const bool stager = q < NQ;
-  const int vslot = 16 * (q >> 2) + 4 * quad_slot(q & 3);  // V^T slot of the quad's key 0
-  // V^T column offset of the quad: chunk XOR-swizzled by (row / 32) = c / 4,
+  // ---- staging.  LDS writes are bank-conflict free on gfx950 when 16 lanes
+  // cover one contiguous row, so K and V use different lane maps:
+  //  K: lane -> 16-byte chunk lane % CH of row lane / CH; the workgroup covers
+  //     4 * RPI rows per pass, NUK passes per tile.
+  //  V: lane -> key quad vq = lane % 16 (4 keys) x chunk vc = 4 * wave + lane / 16;
+  //     after the 4x4 register transpose, 16 lanes write one full V^T row.
+  //     At head size 64 only waves 0-1 stage V. ----
+  constexpr int RPI = 64 / CH;              // K rows per wavefront pass
+  constexpr int NUK = BN / (4 * RPI);       // K passes per tile
+  const int kchunk = lane % CH;
+  const int krow0 = wave * RPI + lane / CH;  // row of pass 0; pass u adds 4 * RPI * u
+  const int vq = lane & 15, vc = 4 * wave + (lane >> 4);
+  const bool vstager = vc < CH;
+  const int vslot = 16 * (vq >> 2) + 4 * quad_slot(vq & 3);  // V^T slot of the quad's key 0
+  // V^T column offset of the quad: chunk XOR-swizzled by (row / 32) = vc / 4,
   // which is the same for all 8 rows a thread writes
-  const int vchunk_off = (((vslot >> 3) ^ (2 * ((c >> 2) & (NCH_V / 2 - 1)))) * 8) + (vslot & 7);
+  const int vchunk_off = (((vslot >> 3) ^ (2 * ((vc >> 2) & (NCH_V / 2 - 1)))) * 8) + (vslot & 7);
   const T *kpast = (const T *)p.past_k + ((int64_t)b * p.Hkv + g) * p.past_rows * D;
   const T *vpast = (const T *)p.past_v + ((int64_t)b * p.Hkv + g) * p.past_rows * D;
   const T *knew = (const T *)p.k + b * p.k_sb + g * p.k_sh;
@@ -201,71 +209,80 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Params p, FPlan 
   const bool fuse_loop = fuse && !fuse_end;
   T *pres_k = (T *)p.present_k + ((int64_t)b * p.Hkv + g) * p.T * D;
   T *pres_v = (T *)p.present_v + ((int64_t)b * p.Hkv + g) * p.T * D;
-  uint4 kreg[4], vreg[4];
 
-  // Source row of key j: the past buffer below past_b, the new K/V above.
+  uint4 rk[NUK], rv[4];  // staging registers: K of tile t+2, V of tile t+1
+
+  // Row j of K or V: the past buffer below past_b, the new input above; keys
+  // outside [lo, hi) read as zeros, never NaN.
+  auto load_row = [&](int j, const T *pastp, const T *newp, int64_t new_ss, int chunk) __attribute__((always_inline)) {
+    const T *src = j >= s.past ? newp + (int64_t)(j - s.past) * new_ss : pastp + (int64_t)j * D;
+    return j >= lo && j < hi ? *(const uint4 *)(src + chunk * 8) : make_uint4(0, 0, 0, 0);
+  };
   // Whole tiles inside one source use a uniform base plus 32-bit lane offsets.
-  auto load_rows = [&](int kt, const T *pastp, const T *newp, int64_t new_ss, uint4 *buf) {
-    if (!stager) return;
+  // first row r0 and row step of the NU rows a thread loads
+  auto load_rows = [&](int kt, const T *pastp, const T *newp, int64_t new_ss, int r0, int rstep,
+                       int chunk, auto &buf) __attribute__((always_inline)) {
+    constexpr int NU = sizeof(buf) / sizeof(buf[0]);
     const int j0 = kt * BN;
     const bool full = j0 >= lo && j0 + BN <= hi;
     if (full && j0 >= s.past) {
       const char *base = (const char *)(newp + (int64_t)(j0 - s.past) * new_ss);
       const uint32_t rs = (uint32_t)new_ss * (uint32_t)sizeof(T);
-      const uint32_t off = (uint32_t)(4 * q) * rs + (uint32_t)c * 16u;
+      const uint32_t off = (uint32_t)r0 * rs + (uint32_t)chunk * 16u;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) buf[u] = *(const uint4 *)(base + off + u * rs);
+      for (int u = 0; u < NU; ++u) buf[u] = *(const uint4 *)(base + off + u * rstep * rs);
     } else if (full && j0 + BN <= s.past) {
       const char *base = (const char *)(pastp + (int64_t)j0 * D);
-      const uint32_t off = ((uint32_t)(4 * q) * D + (uint32_t)c * 8u) * (uint32_t)sizeof(T);
+      const uint32_t rs = D * (uint32_t)sizeof(T);
+      const uint32_t off = (uint32_t)r0 * rs + (uint32_t)chunk * 16u;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) buf[u] = *(const uint4 *)(base + off + u * D * sizeof(T));
+      for (int u = 0; u < NU; ++u) buf[u] = *(const uint4 *)(base + off + u * rstep * rs);
     } else {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int j = j0 + 4 * q + u;
-        const T *src = j >= s.past ? newp + (int64_t)(j - s.past) * new_ss : pastp + (int64_t)j * D;
-        if (j >= lo && j < hi) buf[u] = *(const uint4 *)(src + c * 8);
-        else buf[u] = make_uint4(0, 0, 0, 0);  // outside the key range: zeros, never NaN
-      }
+      for (int u = 0; u < NU; ++u) buf[u] = load_row(j0 + r0 + u * rstep, pastp, newp, new_ss, chunk);
     }
   };
-  auto store_k = [&](int kt, int buf) {
-    if (!stager) return;
+  auto load_k = [&](int kt) __attribute__((always_inline)) {
+    load_rows(kt, kpast, knew, p.k_ss, krow0, 4 * RPI, kchunk, rk);
+  };
+  auto load_v = [&](int kt) __attribute__((always_inline)) {
+    if (vstager) load_rows(kt, vpast, vnew, p.v_ss, 4 * vq, 1, vc, rv);
+  };
+  auto store_k = [&](int kt, int buf) __attribute__((always_inline)) {
     T *kl = klds[buf];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) *(uint4 *)&kl[(4 * q + u) * KST + c * 8] = kreg[u];
+    for (int u = 0; u < NUK; ++u) *(uint4 *)&kl[(krow0 + 4 * RPI * u) * KST + kchunk * 8] = rk[u];
     if (fuse_loop && kt * BN < own_hi && kt * BN + BN > own_lo) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int j = kt * BN + 4 * q + u;
+      for (int u = 0; u < NUK; ++u) {
+        const int j = kt * BN + krow0 + 4 * RPI * u;
         if (j >= own_lo && j < own_hi)
-          *(uint4 *)((char *)pres_k + ((uint32_t)j * D + (uint32_t)c * 8u) * sizeof(T)) = kreg[u];
+          *(uint4 *)((char *)pres_k + ((uint32_t)j * D + (uint32_t)kchunk * 8u) * sizeof(T)) = rk[u];
       }
     }
   };
   // 4 keys x 8 dims -> 8 dims x 4 keys (V^T), 8 bytes per dim row
-  auto store_v = [&](int kt, int buf) {
-    if (!stager) return;
+  auto store_v = [&](int kt, int buf) __attribute__((always_inline)) {
+    if (!vstager) return;
     T *vl = vlds[buf];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const uint32_t r0 = ((const uint32_t *)&vreg[0])[w], r1 = ((const uint32_t *)&vreg[1])[w];
-      const uint32_t r2 = ((const uint32_t *)&vreg[2])[w], r3 = ((const uint32_t *)&vreg[3])[w];
+      const uint32_t r0 = ((const uint32_t *)&rv[0])[w], r1 = ((const uint32_t *)&rv[1])[w];
+      const uint32_t r2 = ((const uint32_t *)&rv[2])[w], r3 = ((const uint32_t *)&rv[3])[w];
 #pragma unroll
       for (int hl = 0; hl < 2; ++hl) {
         const uint32_t sel = hl ? 0x07060302u : 0x05040100u;
         const uint2 kk = make_uint2(__builtin_amdgcn_perm(r1, r0, sel), __builtin_amdgcn_perm(r3, r2, sel));
-        const int d = c * 8 + 2 * w + hl;
+        const int d = vc * 8 + 2 * w + hl;
         *(uint2 *)&vl[d * VST + vchunk_off] = kk;
       }
     }
     if (fuse_loop && kt * BN < own_hi && kt * BN + BN > own_lo) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int j = kt * BN + 4 * q + u;
+        const int j = kt * BN + 4 * vq + u;
         if (j >= own_lo && j < own_hi)
-          *(uint4 *)((char *)pres_v + ((uint32_t)j * D + (uint32_t)c * 8u) * sizeof(T)) = vreg[u];
+          *(uint4 *)((char *)pres_v + ((uint32_t)j * D + (uint32_t)vc * 8u) * sizeof(T)) = rv[u];
       }
     }
   };
@@ -311,9 +328,9 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Params p, FPlan 
     const T *kl = klds[buf];
     const f32x16 zero = {};
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
+    for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
+      for (int kb = 0; kb < KB; ++kb) {
         const vec8 a = *(const vec8 *)&kl[(kb * 32 + col) * KST + ks * 16 + half * 8];
         sacc[kb] = mma(a, qreg[ks], ks == 0 ? zero : sacc[kb]);
       }
@@ -411,8 +428,8 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Params p, FPlan 
   };
 
   if (kt0 < kt1) {
-    load_rows(kt0, kpast, knew, p.k_ss, kreg);
-    load_rows(kt0, vpast, vnew, p.v_ss, vreg);
+    load_k(kt0);
+    load_v(kt0);
     if (BPRE) load_bias(kt0, bcur);
     store_k(kt0, 0);
     store_v(kt0, 0);
@@ -425,8 +442,8 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Params p, FPlan 
     const int buf = (kt - kt0) & 1;
     const bool more = kt + 1 < kt1;
     if (more) {
-      load_rows(kt + 1, kpast, knew, p.k_ss, kreg);
-      load_rows(kt + 1, vpast, vnew, p.v_ss, vreg);
+      load_k(kt + 1);
+      load_v(kt + 1);
       if (BPRE) load_bias(kt + 1, bnext);
     }
     if (wave_active) {
