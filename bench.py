@@ -30,7 +30,7 @@ MFMA_PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}  # dense, MI355
 HBM_PEAK_GBS = 8000.0
 HEADLINE = "gqa_prefill_causal_bf16"
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
-TILED_SRC = os.path.join(ROOT, "transformer_attention_fwd_amd", "csrc", "olk_tiled.hip")
+FLASH_SRC = os.path.join(ROOT, "transformer_attention_fwd_amd", "csrc", "olk_flash.hip")
 
 
 def parse():
@@ -116,7 +116,7 @@ def traffic_for(workload: str):
     try:
         with open(PROFILE_TRAFFIC) as f:
             rec = json.load(f)
-        h = hashlib.sha256(open(TILED_SRC, "rb").read()).hexdigest()
+        h = hashlib.sha256(open(FLASH_SRC, "rb").read()).hexdigest()
         ent = rec.get(workload)
         if ent and ent.get("kernel_sha256") == h:
             return float(ent["fetch_bytes"]) + float(ent["write_bytes"])
@@ -219,7 +219,7 @@ def run_workload(name, steps, warmup, with_cpu, cpu_s, is_headline):
             peak = MFMA_PEAK_TFLOPS[p.dtype]
             res["roofline"] = {"bound": "mfma", "achieved": round(ach, 3), "peak": peak,
                                "unit": "TFLOP/s", "frac": round(ach / peak, 5),
-                               "traffic": traffic_for(name), "kernel": "tiled_kernel",
+                               "traffic": traffic_for(name), "kernel": "flash_fwd_kernel",
                                "kernel_ms": kms}
     if with_cpu:
         res["cpu_baseline"] = cpu_baseline(p, inputs, "bytes" if decode else "flops", cpu_s)

@@ -54,6 +54,8 @@ __device__ __forceinline__ f32x16 mma(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+// s_waitcnt immediate for vmcnt(0) only (gfx9 encoding: expcnt 7, lgkmcnt 15)
+constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr int kThreads = 256;
 constexpr int kSlots = 128;  // row slots per workgroup (4 wavefronts x 32)
 constexpr float kLog2e = 1.4426950408889634f;
@@ -175,6 +177,11 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Params p, FPlan 
       }
     }
   }
+  // Q is in registers from here on.  Waiting for its loads now, on every path,
+  // keeps the wait-count analysis from assuming they may still be in flight
+  // inside the loop, where it would otherwise hold the first MFMA of every
+  // tile until the next tile's prefetch loads have landed as well.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   // ---- staging: thread owns key quad q (4 keys) x 16-byte chunk c; at head
   // size 64 the upper half of the workgroup has no quad to stage ----
