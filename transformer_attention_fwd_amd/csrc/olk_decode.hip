@@ -132,13 +132,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p, DPlan pl) {
       qreg[ks] = __builtin_bit_cast(vec8, raw);
     }
   }
+  // Q is in registers from here on: wait for its loads on every path, so the
+  // wait-count analysis does not treat them as in flight inside the step loop
+  // (vmcnt(0) only; gfx9 encoding: expcnt 7, lgkmcnt 15).
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
   const T *kpast = (const T *)p.past_k + ((int64_t)b * p.Hkv + g) * p.past_rows * D;
   const T *vpast = (const T *)p.past_v + ((int64_t)b * p.Hkv + g) * p.past_rows * D;
   const T *knew = (const T *)p.k + b * p.k_sb + g * p.k_sh;
   const T *vnew = (const T *)p.v + b * p.v_sb + g * p.v_sh;
-  auto krow = [&](int j) { return j < s.past ? kpast + (int64_t)j * D : knew + (int64_t)(j - s.past) * p.k_ss; };
-  auto vrow = [&](int j) { return j < s.past ? vpast + (int64_t)j * D : vnew + (int64_t)(j - s.past) * p.v_ss; };
 
   // per-step registers: K (A operand: key lane % 16, dims 32 ks + 8 kq + e) and
   // V (key 2 t + lane / 32, dims DPL * (lane % 32) + e)
@@ -168,22 +170,25 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p, DPlan pl) {
       }
       return;
     }
-    const int jk = j0 + n;  // this lane's K row (lane % 16)
-    const bool kin = jk >= sp_lo && jk < sp_hi;
-    const T *ks = krow(kin ? jk : sp_lo);
+    // Steps that straddle the range or the past/new boundary: per-lane rows.
+    // Rows outside [sp_lo, sp_hi) load row sp_lo instead (valid memory, finite
+    // values; their scores are masked, so their P is exactly 0).  Both source
+    // offsets are computed and one selected: no branch, no select on loaded
+    // data, so the compiler's count of loads in flight stays exact.
+    auto row_ptr = [&](const T *pastp, const T *newp, int64_t new_ss, int j) {
+      const int jj = j >= sp_lo && j < sp_hi ? j : sp_lo;
+      const bool nw = jj >= s.past;
+      const int64_t off_new = (int64_t)(jj - s.past) * new_ss, off_past = (int64_t)jj * D;
+      return (nw ? newp : pastp) + (nw ? off_new : off_past);
+    };
+    const T *ks = row_ptr(kpast, knew, p.k_ss, j0 + n);
 #pragma unroll
-    for (int s2 = 0; s2 < NKS; ++s2)
-      kk[s2] = kin ? *(const uint4 *)(ks + s2 * 32 + kq * 8) : make_uint4(0, 0, 0, 0);
+    for (int s2 = 0; s2 < NKS; ++s2) kk[s2] = *(const uint4 *)(ks + s2 * 32 + kq * 8);
 #pragma unroll
     for (int t = 0; t < kStep / 2; ++t) {
-      const int jv = j0 + 2 * t + vpar;
-      const bool vin = jv >= sp_lo && jv < sp_hi;
-      if constexpr (DPL == 4) {
-        vv[t] = vin ? *(const uint2 *)(vrow(vin ? jv : sp_lo) + vcol) : make_uint2(0, 0);
-      } else {
-        const uint32_t w = vin ? *(const uint32_t *)(vrow(vin ? jv : sp_lo) + vcol) : 0u;
-        vv[t] = make_uint2(w, 0);
-      }
+      const T *vs = row_ptr(vpast, vnew, p.v_ss, j0 + 2 * t + vpar) + vcol;
+      if constexpr (DPL == 4) vv[t] = *(const uint2 *)vs;
+      else vv[t] = make_uint2(*(const uint32_t *)vs, 0u);
     }
   };
 
