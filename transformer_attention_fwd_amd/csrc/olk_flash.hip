@@ -342,6 +342,15 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Params p, FPlan 
         sacc[kb] = mma(a, qreg[ks], ks == 0 ? zero : sacc[kb]);
       }
     }
+    // schedule: four operand reads in flight ahead of the MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // 0x100: LDS reads
+#pragma unroll
+    for (int i = 0; i < NKS * KB - 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 0x008: MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
   };
 
   // Softmax and PV of one tile.  With bias or softcap (GENERAL) the scores
