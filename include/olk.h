@@ -100,6 +100,23 @@ typedef struct {
                                 valid past at [0, past_b) (past_k/v NULL or equal to
                                 present_k/v); only the new positions are written. */
   int32_t kernel;            /* olk_kernel */
+  /* Rotary position embedding fused into GroupQueryAttention (the operator's
+   * do_rotary / rotary_interleaved attributes; the rotation itself is the
+   * RotaryEmbedding kernel of the onnx-light reference kernels header page,
+   * "class RotaryEmbedding", after arXiv 2104.09864).  Q and the new K rows are
+   * rotated at their absolute positions (query i and new key i of batch b at
+   * past_b + i); the past is used as stored; V is not rotated.  present_key
+   * receives the rotated keys.  Each rotated pair (x1, x2) with cosine c and
+   * sine s becomes (x1*c - x2*s, x2*c + x1*s), computed in float32 as
+   * fma(x1, c, -(x2*s)) and fma(x2, c, x1*s) and rounded once to the element
+   * type.  Requires op = GQA, D == Dv and present_k/present_v (the rotated
+   * keys are written there and read back).  Positions at or beyond
+   * rotary_max_pos use the last cache row (memory-safe; values unspecified). */
+  int32_t do_rotary;         /* 0/1 */
+  int32_t rotary_interleaved;/* 1: pairs (2k, 2k+1); 0: pairs (k, k + R/2) */
+  int32_t rotary_dim;        /* R: channels rotated, even, 0 < R <= D; 0 = D.  Channels >= R
+                                are copied unchanged. */
+  int32_t rotary_max_pos;    /* rows of cos_cache / sin_cache (> 0 when do_rotary) */
 } olk_attn_desc;
 
 /* Device pointers (caller-owned); NULL = absent. */
@@ -117,6 +134,8 @@ typedef struct {
   void *y;                   /* required output; see q_rank */
   void *present_k;           /* (B,Hkv,T,D) output, or NULL = not requested */
   void *present_v;           /* (B,Hkv,T,Dv) output, or NULL = not requested */
+  const void *cos_cache;     /* do_rotary: (rotary_max_pos, R/2) element type, row = position */
+  const void *sin_cache;     /* do_rotary: (rotary_max_pos, R/2) element type */
 } olk_attn_io;
 
 /*

@@ -40,7 +40,19 @@
  *       they stay in the softmax.
  *   R10 a row with no allowed key outputs 0.
  *   R11 MHA projection bias layout is [q (N*H) | k (N*H) | v (N*Hv)].
- * Intermediate values are not rounded; Y is returned in float64.
+ *   R18 rotary embedding (GroupQueryAttention do_rotary): Q and the new K rows
+ *       are rotated at their absolute positions (past_b + i), the past is used
+ *       as stored, V is not rotated, and present_key holds the rotated keys.
+ *       The rotation follows the RotaryEmbedding kernel of the reference
+ *       kernels header page ("class RotaryEmbedding": rank-2 cos/sin caches
+ *       indexed by position, rotary_embedding_dim, interleaved pairing), i.e.
+ *       each pair (x1, x2) becomes (x1 cos - x2 sin, x2 cos + x1 sin) as in
+ *       arXiv 2104.09864.  The rotated values are tensors of the element type:
+ *       computed in float32 as fmaf(x1, c, -(x2*s)) and fmaf(x2, c, x1*s) and
+ *       rounded once (RNE), so present holds exactly these bits.  Positions
+ *       beyond the cache use its last row.
+ * Intermediate values are not rounded (apart from R18's rotated Q/K); Y is
+ * returned in float64.
  */
 #include <math.h>
 #include <stdint.h>
@@ -62,12 +74,14 @@ typedef struct {
   int32_t has_scale;
   float scale, softcap, mask_filter_value;
   int32_t bias_b, bias_h;
+  int32_t do_rotary, rotary_interleaved, rotary_dim, rotary_max_pos;
 } ref_desc;
 
 typedef struct {
   const void *q, *k, *v, *past_k, *past_v;
   const int32_t *lens;
   const void *bias, *sink, *proj_bias;
+  const void *cos_cache, *sin_cache;
 } ref_inputs;
 
 /* ---- element decoding (format definitions, not attention arithmetic) ---- */
@@ -97,6 +111,79 @@ static double elem(const void *base, int dtype, size_t idx) {
 }
 
 static size_t esize(int dtype) { return dtype == REF_F32 ? 4 : 2; }
+
+/* float32 -> binary16, round to nearest even (IEEE 754 conversion). */
+static uint16_t float_to_half(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+  uint32_t e = (u >> 23) & 0xff, m = u & 0x7fffffu;
+  if (e == 0xff) return sign | 0x7c00u | (m ? 0x200u : 0u);   /* inf / NaN */
+  int ex = (int)e - 127 + 15;
+  if (ex >= 31) return sign | 0x7c00u;                         /* overflow */
+  if (ex <= 0) {                                               /* subnormal or zero */
+    if (ex < -10) return sign;
+    uint32_t mant = m | 0x800000u;
+    int shift = 14 - ex;                                       /* 24-bit mantissa -> 10 - ex bits */
+    uint32_t q = mant >> shift, rem = mant & ((1u << shift) - 1), halfway = 1u << (shift - 1);
+    if (rem > halfway || (rem == halfway && (q & 1))) ++q;
+    return sign | (uint16_t)q;
+  }
+  uint32_t q = ((uint32_t)ex << 10) | (m >> 13), rem = m & 0x1fffu;
+  if (rem > 0x1000u || (rem == 0x1000u && (q & 1))) ++q;     /* may carry into the exponent */
+  return sign | (uint16_t)q;
+}
+
+/* float32 -> bfloat16 (upper half), round to nearest even. */
+static uint16_t float_to_bf16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x7fffffu)) return (uint16_t)((u >> 16) | 0x40u);
+  uint32_t lsb = (u >> 16) & 1u;
+  u += 0x7fffu + lsb;
+  return (uint16_t)(u >> 16);
+}
+
+/* ---- R18: rotary embedding of one channel ---- */
+
+static int rot_dim(const ref_desc *d) { return d->rotary_dim > 0 ? d->rotary_dim : d->head_size; }
+
+/* Channel c of a row (element 0 at index base of src) after the rotation at
+ * position pos, as the element type's bits (f32: the float's bits). */
+static uint32_t rot_bits(const ref_desc *d, const ref_inputs *in, const void *src, size_t base,
+                         int c, long pos) {
+  const int R = rot_dim(d), half = R / 2;
+  float out;
+  if (c >= R) {
+    out = (float)elem(src, d->dtype, base + c);
+  } else {
+    int k, first, partner;
+    if (d->rotary_interleaved) { k = c / 2; first = (c % 2) == 0; partner = c ^ 1; }
+    else { k = c % half; first = c < half; partner = first ? c + half : c - half; }
+    const float x1 = (float)elem(src, d->dtype, base + (first ? c : partner));
+    const float x2 = (float)elem(src, d->dtype, base + (first ? partner : c));
+    if (pos < 0) pos = 0;
+    if (pos >= d->rotary_max_pos) pos = d->rotary_max_pos - 1;
+    const float cs = (float)elem(in->cos_cache, d->dtype, (size_t)pos * half + k);
+    const float sn = (float)elem(in->sin_cache, d->dtype, (size_t)pos * half + k);
+    if (first) {
+      const float t = x2 * sn;
+      out = fmaf(x1, cs, -t);
+    } else {
+      const float t = x1 * sn;
+      out = fmaf(x2, cs, t);
+    }
+  }
+  if (d->dtype == REF_F32) { uint32_t u; memcpy(&u, &out, 4); return u; }
+  return d->dtype == REF_F16 ? float_to_half(out) : float_to_bf16(out);
+}
+
+static double rot_elem(const ref_desc *d, const ref_inputs *in, const void *src, size_t base,
+                       int c, long pos) {
+  const uint32_t bits = rot_bits(d, in, src, base, c, pos);
+  if (d->dtype == REF_F32) { float f; memcpy(&f, &bits, 4); return (double)f; }
+  return d->dtype == REF_F16 ? half_to_double((uint16_t)bits) : bf16_to_double((uint16_t)bits);
+}
 
 /* ---- index helpers ---- */
 
@@ -159,7 +246,9 @@ static double key_elem(const ref_desc *d, const ref_inputs *in, const seqinfo *s
   const void *past = value ? in->past_v : in->past_k;
   const void *cur = value ? in->v : in->k;
   if (j < s->past_b) return elem(past, d->dtype, past_index(d, b, g, (int)j, c, width));
-  return elem(cur, d->dtype, new_kv_index(d, b, g, (int)(j - s->past_b), c, width));
+  const size_t base = new_kv_index(d, b, g, (int)(j - s->past_b), 0, width);
+  if (d->do_rotary && !value) return rot_elem(d, in, cur, base, c, j); /* R18: new key at position j */
+  return elem(cur, d->dtype, base + c);
 }
 
 static double scale_of(const ref_desc *d) {
@@ -181,7 +270,8 @@ static long row_weights(const ref_desc *d, const ref_inputs *in, int b, int h, i
   const int G = d->q_heads / d->kv_heads;
   const int g = h / G; /* R5 */
   for (int c = 0; c < D; ++c) {
-    double x = elem(in->q, d->dtype, q_index(d, b, h, i, c));
+    double x = d->do_rotary ? rot_elem(d, in, in->q, q_index(d, b, h, i, 0), c, s.q_off + i) /* R18 */
+                            : elem(in->q, d->dtype, q_index(d, b, h, i, c));
     /* MHA projection bias: the query segment is added to q (R11). */
     if (d->op == REF_MHA && in->proj_bias) x += elem(in->proj_bias, d->dtype, (size_t)h * D + c);
     qbuf[c] = x;
@@ -240,6 +330,11 @@ static int check_desc(const ref_desc *d, const ref_inputs *in) {
   if (d->head_size <= 0 || d->v_head_size <= 0 || d->batch < 0 || d->q_seq < 0) return -1;
   if (d->op == REF_GQA && (!in->lens || d->kv_seq != d->q_seq)) return -1;
   if (d->past_seq > 0 && (!in->past_k || !in->past_v)) return -1;
+  if (d->do_rotary) {
+    const int R = rot_dim(d);
+    if (d->op != REF_GQA || !in->cos_cache || !in->sin_cache) return -1;
+    if (R <= 0 || R % 2 || R > d->head_size || d->rotary_max_pos <= 0) return -1;
+  }
   return 0;
 }
 
@@ -342,9 +437,18 @@ int olk_ref_present(const ref_desc *d, const ref_inputs *in, void *pk, void *pv)
         const void *cur = which ? in->v : in->k;
         for (long j = 0; j < s.total_b && j < Tp; ++j) {
           const char *src;
+          char *o = (char *)dst + ((((size_t)b * d->kv_heads + g) * Tp + j) * width) * es;
+          if (j >= s.past_b && d->do_rotary && !which) { /* R18: rotated new key */
+            const size_t base = new_kv_index(d, b, g, (int)(j - s.past_b), 0, width);
+            for (int c = 0; c < width; ++c) {
+              const uint32_t bits = rot_bits(d, in, cur, base, c, j);
+              if (es == 4) memcpy(o + 4 * (size_t)c, &bits, 4);
+              else { const uint16_t h16 = (uint16_t)bits; memcpy(o + 2 * (size_t)c, &h16, 2); }
+            }
+            continue;
+          }
           if (j < s.past_b) src = (const char *)past + past_index(d, b, g, (int)j, 0, width) * es;
           else src = (const char *)cur + new_kv_index(d, b, g, (int)(j - s.past_b), 0, width) * es;
-          char *o = (char *)dst + ((((size_t)b * d->kv_heads + g) * Tp + j) * width) * es;
           memcpy(o, src, (size_t)width * es);
         }
       }

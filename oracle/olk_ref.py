@@ -30,19 +30,24 @@ class _Desc(ctypes.Structure):
         "window", "has_scale")] + [
         ("scale", ctypes.c_float), ("softcap", ctypes.c_float),
         ("mask_filter_value", ctypes.c_float),
-        ("bias_b", ctypes.c_int32), ("bias_h", ctypes.c_int32)]
+        ("bias_b", ctypes.c_int32), ("bias_h", ctypes.c_int32)] + [
+        (n, ctypes.c_int32) for n in ("do_rotary", "rotary_interleaved", "rotary_dim",
+                                      "rotary_max_pos")]
 
 
 class _Inputs(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
-        "q", "k", "v", "past_k", "past_v", "lens", "bias", "sink", "proj_bias")]
+        "q", "k", "v", "past_k", "past_v", "lens", "bias", "sink", "proj_bias",
+        "cos_cache", "sin_cache")]
 
 
 def build(force: bool = False) -> str:
     """Compile the oracle with gcc (float64, OpenMP)."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", tmp,
+        # -ffp-contract=off: the rotary arithmetic (R18) is float32 with exactly
+        # the roundings written in the source
+        subprocess.run(["gcc", "-O2", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared", "-o", tmp,
                         _SRC, "-lm"], check=True)
         os.replace(tmp, _LIB)
     return _LIB
@@ -74,7 +79,9 @@ def _desc(p) -> _Desc:
                  causal=p.causal, window=p.window,
                  has_scale=0 if p.scale is None else 1,
                  scale=0.0 if p.scale is None else p.scale, softcap=p.softcap,
-                 mask_filter_value=p.mask_filter_value, bias_b=bb, bias_h=bh)
+                 mask_filter_value=p.mask_filter_value, bias_b=bb, bias_h=bh,
+                 do_rotary=p.rotary, rotary_interleaved=p.rotary_interleaved,
+                 rotary_dim=p.rotary_dim, rotary_max_pos=p.max_pos)
 
 
 class _Bound:
@@ -83,7 +90,8 @@ class _Bound:
     def __init__(self, inputs: Dict[str, torch.Tensor]):
         self.keep = {}
         ptrs = {}
-        for name in ("q", "k", "v", "past_k", "past_v", "lens", "bias", "sink", "proj_bias"):
+        for name in ("q", "k", "v", "past_k", "past_v", "lens", "bias", "sink", "proj_bias",
+                     "cos_cache", "sin_cache"):
             t = inputs.get(name)
             if t is None:
                 ptrs[name] = None

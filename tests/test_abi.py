@@ -65,7 +65,7 @@ _BASE = 1 << 40
 
 def fake_io(p: Problem, **over):
     names = ["q", "k", "v", "past_k", "past_v", "seqlens", "attn_bias", "head_sink",
-             "proj_bias", "y", "present_k", "present_v"]
+             "proj_bias", "y", "present_k", "present_v", "cos_cache", "sin_cache"]
     ptr = {n: _BASE + (i + 1) * (1 << 36) for i, n in enumerate(names)}
     if p.P == 0:
         ptr["past_k"] = ptr["past_v"] = None
@@ -77,6 +77,8 @@ def fake_io(p: Problem, **over):
         ptr["proj_bias"] = None
     if p.op != "gqa" and not p.has_lens:
         ptr["seqlens"] = None
+    if not p.rotary:
+        ptr["cos_cache"] = ptr["sin_cache"] = None
     ptr.update(over)
     return olk.olk_attn_io(**ptr)
 
@@ -190,3 +192,27 @@ def test_status_strings():
     for s in range(7):
         assert olk.olk_status_str(s)
     assert olk.olk_last_kernel_name() == ""
+
+
+def test_rotary_rules():
+    rope = GQA.with_(rotary=1)
+    assert status(rope) == olk.OLK_OK
+    assert status(rope.with_(rotary_dim=64, rotary_interleaved=1)) == olk.OLK_OK
+    assert status(rope.with_(rotary_dim=63)) == olk.OLK_E_ATTR     # odd R
+    assert status(rope.with_(rotary_dim=130)) == olk.OLK_E_ATTR    # R > D
+    assert status(rope, cos_cache=None) == olk.OLK_E_NULL
+    # the rotated keys live in present: present outputs are required
+    assert status(rope, present_k=None, present_v=None) == olk.OLK_E_UNSUPPORTED
+    # GroupQueryAttention only
+    mha = MHA.with_(rotary=1)
+    assert status(mha) == olk.OLK_E_ATTR
+    d = olk.make_desc(rope)
+    d.do_rotary = 2
+    assert olk.olk_validate(d, fake_io(rope)) == olk.OLK_E_ATTR
+    d = olk.make_desc(rope)
+    d.rotary_max_pos = 0
+    assert olk.olk_validate(d, fake_io(rope)) == olk.OLK_E_SHAPE
+    # caches are inputs: they must not overlap the outputs
+    io = fake_io(rope)
+    io.cos_cache = io.y
+    assert olk.olk_validate(olk.make_desc(rope), io) == olk.OLK_E_SHAPE

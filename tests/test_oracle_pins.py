@@ -454,3 +454,122 @@ def test_window_2048_attends_current_and_2047_preceding():
         nz = np.nonzero(w)[0]
         assert len(nz) == case["attended"]
         assert nz[0] == case["first_key"] and nz[-1] == case["last_key"]
+
+
+# ---------------------------------------------------------------------------
+# Rotary embedding (GroupQueryAttention do_rotary; RotaryEmbedding of the
+# reference kernels header page, after arXiv 2104.09864).
+# ---------------------------------------------------------------------------
+
+def _rope_problem(**kw):
+    base = dict(op="gqa", dtype="f32", B=2, S=6, L=6, P=9, Hq=4, Hkv=2, D=16, Dv=16,
+                causal=1, lens_range=(0, 9), rotary=1)
+    base.update(kw)
+    return Problem(**base)
+
+
+def _with_tables(p, inp, cos, sin):
+    out = dict(inp)
+    out["cos_cache"] = torch.as_tensor(cos, dtype=p.torch_dtype).contiguous()
+    out["sin_cache"] = torch.as_tensor(sin, dtype=p.torch_dtype).contiguous()
+    return out
+
+
+def test_rotary_with_identity_tables_is_plain_attention():
+    # cos = 1, sin = 0 rotates nothing: Y and present equal the plain call
+    p = _rope_problem(dtype="bf16")
+    inp = make_inputs(p, 41)
+    half = p.R // 2
+    ident = _with_tables(p, inp, np.ones((p.max_pos, half)), np.zeros((p.max_pos, half)))
+    plain = p.with_(rotary=0)
+    assert np.array_equal(olk_ref.attention(p, ident), olk_ref.attention(plain, inp))
+    for a, b in zip(olk_ref.present(p, ident, fill=0.0), olk_ref.present(plain, inp, fill=0.0)):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("interleaved", [0, 1])
+def test_rotary_is_the_textbook_plane_rotation(interleaved):
+    # One pair per head (D = 2): key (1, 0) at position j becomes (cos_j, sin_j)
+    # and (0, 1) becomes (-sin_j, cos_j), as the rotation matrix
+    # [[cos, -sin], [sin, cos]] of the RoPE paper; positions count the past.
+    p = _rope_problem(B=1, S=2, L=2, P=3, Hq=1, Hkv=1, D=2, Dv=2, lens_range=None,
+                      rotary_interleaved=interleaved)
+    inp = make_inputs(p, 42, lens=np.array([3 + 2 - 1]))  # past_b = 3
+    inp["k"] = torch.tensor([[[1.0, 0.0], [0.0, 1.0]]], dtype=torch.float32)
+    ang = 0.3 * np.arange(p.max_pos)[:, None]
+    tab = _with_tables(p, inp, np.cos(ang), np.sin(ang))
+    pk, _ = olk_ref.present(p, tab, fill=0.0)
+    c3, s3 = np.float32(np.cos(0.9)), np.float32(np.sin(0.9))
+    c4, s4 = np.float32(np.cos(1.2)), np.float32(np.sin(1.2))
+    assert np.array_equal(pk[0, 0, 3].numpy(), np.array([c3, s3], dtype=np.float32))
+    assert np.array_equal(pk[0, 0, 4].numpy(), np.array([-s4, c4], dtype=np.float32))
+    # the past rows are used as stored
+    assert torch.equal(pk[0, 0, :3], inp["past_k"][0, 0])
+
+
+def test_rotary_pairs_split_halves_and_keeps_tail_channels():
+    # R = 8 of D = 16, split halves: channel k pairs with k + 4; channels >= 8 are copied
+    p = _rope_problem(B=1, S=1, L=1, P=0, Hq=1, Hkv=1, lens_range=None, rotary_dim=8)
+    inp = make_inputs(p, 43)
+    x = torch.zeros(1, 1, 16)
+    x[0, 0, 1] = 1.0                 # channel 1 pairs with channel 5
+    x[0, 0, 8:] = torch.arange(8.0)  # beyond R: untouched
+    inp["k"] = x
+    ang = np.full((p.max_pos, 4), 0.5)
+    pk, _ = olk_ref.present(p, _with_tables(p, inp, np.cos(ang), np.sin(ang)), fill=0.0)
+    row = pk[0, 0, 0].numpy()
+    want = np.zeros(16, dtype=np.float32)
+    want[1], want[5] = np.float32(np.cos(0.5)), np.float32(np.sin(0.5))
+    want[8:] = np.arange(8.0)
+    assert np.array_equal(row, want)
+
+
+def test_rotary_preserves_norms():
+    p = _rope_problem()
+    inp = make_inputs(p, 44)
+    pk, _ = olk_ref.present(p, inp, fill=0.0)
+    lens = inp["lens"].numpy()
+    for b in range(p.B):
+        past = int(lens[b]) + 1 - p.S
+        new = inp["k"][b].view(p.S, p.Hkv, p.D).permute(1, 0, 2).double()
+        rot = pk[b, :, past: past + p.S].double()
+        np.testing.assert_allclose(rot.norm(dim=-1).numpy(), new.norm(dim=-1).numpy(),
+                                   rtol=1e-6)
+
+
+def test_rotary_scores_depend_only_on_relative_position():
+    # Same q at every query position and same k at every key position, no mask:
+    # after rotation the score of (query at m, key at n) depends on m - n only,
+    # so within two rows one position apart the weight ratios of keys shifted by
+    # one position agree.
+    p = _rope_problem(B=1, S=8, L=8, P=0, Hq=1, Hkv=1, D=16, Dv=16, causal=0, lens_range=None)
+    inp = make_inputs(p, 45)
+    rng = np.random.default_rng(0)
+    qv = torch.tensor(rng.standard_normal(16), dtype=torch.float32)
+    kv = torch.tensor(rng.standard_normal(16), dtype=torch.float32)
+    inp["q"] = qv.repeat(1, 8, 1)
+    inp["k"] = kv.repeat(1, 8, 1)
+    w3, _ = olk_ref.row_weights(p, inp, 0, 0, 3)
+    w4, _ = olk_ref.row_weights(p, inp, 0, 0, 4)
+    r3 = np.log(w3[1:7] / w3[0])    # keys 1..6 against key 0, query at 3
+    r4 = np.log(w4[2:8] / w4[1])    # keys 2..7 against key 1, query at 4
+    np.testing.assert_allclose(r3, r4, atol=2e-5)
+
+
+def test_interleaved_equals_split_halves_under_channel_permutation():
+    # Interleaved pairs (2k, 2k+1) are split-half pairs (k, k + R/2) after the
+    # channel permutation that moves 2k -> k and 2k+1 -> k + R/2.
+    p = _rope_problem(rotary_interleaved=1)
+    inp = make_inputs(p, 46)
+    D = p.D
+    perm = np.concatenate([np.arange(0, D, 2), np.arange(1, D, 2)])  # interleaved -> split order
+    split = p.with_(rotary_interleaved=0)
+    sp = dict(inp)
+    sp["q"] = inp["q"].view(p.B, p.S, p.Hq, D)[..., perm].reshape(p.B, p.S, p.Hq * D).contiguous()
+    sp["k"] = inp["k"].view(p.B, p.L, p.Hkv, D)[..., perm].reshape(p.B, p.L, p.Hkv * D).contiguous()
+    sp["past_k"] = inp["past_k"][..., perm].contiguous()
+    pk_i, _ = olk_ref.present(p, inp, fill=0.0)
+    pk_s, _ = olk_ref.present(split, sp, fill=0.0)
+    assert torch.equal(pk_i[..., perm], pk_s)
+    np.testing.assert_allclose(olk_ref.attention(p, inp), olk_ref.attention(split, sp),
+                               rtol=0, atol=1e-12)

@@ -1,6 +1,6 @@
 """GPU parity: the HIP path through the C ABI against the oracle.
 
-Small problems are compared element by element over every output; the five
+Small problems are compared element by element over every output; the
 full-size workloads are compared on sampled rows (in the launch configuration
 the benchmark times) and present_key/present_value bit for bit.
 """
@@ -64,6 +64,20 @@ SMALL = {
                                      scale=0.05),
     "gqa_headsize256_f32": Problem(op="gqa", dtype="f32", B=1, S=20, L=20, Hq=2, Hkv=1,
                                    D=256, Dv=256, causal=1),
+    # rotary embedding (do_rotary): split halves, interleaved with a partial
+    # rotary dimension and a past, and the fp32 path
+    "gqa_rope_bf16": Problem(op="gqa", dtype="bf16", B=2, S=130, L=130, Hq=8, Hkv=2, D=128,
+                             Dv=128, causal=1, rotary=1),
+    "gqa_rope_past_interleaved_f16": Problem(op="gqa", dtype="f16", B=3, S=20, L=20, P=100,
+                                             Hq=4, Hkv=2, D=64, Dv=64, causal=1,
+                                             lens_range=(0, 100), rotary=1,
+                                             rotary_interleaved=1, rotary_dim=32),
+    "gqa_rope_window_f32": Problem(op="gqa", dtype="f32", B=2, S=17, L=17, P=40, Hq=4, Hkv=1,
+                                   D=48, Dv=48, causal=1, window=9, lens_range=(5, 40),
+                                   rotary=1, rotary_dim=16, rotary_max_pos=50),
+    "gqa_rope_dim12_f16": Problem(op="gqa", dtype="f16", B=2, S=33, L=33, P=8, Hq=4, Hkv=2,
+                                  D=64, Dv=64, causal=1, lens_range=(0, 8), rotary=1,
+                                  rotary_dim=12),
 }
 
 
@@ -206,5 +220,24 @@ def test_first_token_decode_and_full_cache():
     inp = make_inputs(p, 8, lens=np.array([0, 256]))
     for mode in ("fwd", "decode"):
         c = _run(p, to_dev(inp), mode=mode)
+        assert_close(p, y_logical(p, c.y), olk_ref.attention(p, inp))
+        assert_present_exact(p, inp, c.present_k, c.present_v)
+
+
+def test_rotary_decode_inplace_cache_append():
+    # KV-cache decode with rotary: the cache holds rotated keys; the new key is
+    # rotated at position past_b and appended in place
+    p = Problem(op="gqa", dtype="bf16", B=4, S=1, L=1, P=300, Hq=8, Hkv=2, D=128, Dv=128,
+                causal=1, lens_range=(0, 300), rotary=1)
+    inp = make_inputs(p, 123)
+    dev = to_dev(inp)
+    pk = dev["past_k"].new_empty((p.B, p.Hkv, p.P + 1, p.D))
+    pv = dev["past_v"].new_empty((p.B, p.Hkv, p.P + 1, p.Dv))
+    pk[:, :, : p.P] = dev.pop("past_k")
+    pv[:, :, : p.P] = dev.pop("past_v")
+    for mode in ("decode", "fwd"):
+        k0, v0 = pk.clone(), pv.clone()
+        c = _run(p, dev, mode=mode, kv_inplace=True, present_k=k0, present_v=v0)
+        _say(f"[parity] rotary inplace {mode} kernel={olk.olk_last_kernel_name()}")
         assert_close(p, y_logical(p, c.y), olk_ref.attention(p, inp))
         assert_present_exact(p, inp, c.present_k, c.present_v)

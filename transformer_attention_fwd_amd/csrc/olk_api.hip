@@ -47,7 +47,7 @@ bool overlaps(Range a, Range b) {
 
 // Sizes of every tensor in bytes (int64 arithmetic, checked by the caller).
 struct Sizes {
-  size_t q, k, v, past_k, past_v, bias, sink, proj, y, pres_k, pres_v;
+  size_t q, k, v, past_k, past_v, bias, sink, proj, y, pres_k, pres_v, rot;
 };
 
 Sizes sizes_of(const olk_attn_desc *d) {
@@ -68,6 +68,8 @@ Sizes sizes_of(const olk_attn_desc *d) {
   s.y = B * S * Hq * Dv * es;
   s.pres_k = B * Hkv * T * D * es;
   s.pres_v = B * Hkv * T * Dv * es;
+  const size_t R = d->rotary_dim > 0 ? d->rotary_dim : D;
+  s.rot = d->do_rotary ? (size_t)(d->rotary_max_pos > 0 ? d->rotary_max_pos : 0) * (R / 2) * es : 0;
   return s;
 }
 
@@ -87,6 +89,14 @@ olk_status validate(const olk_attn_desc *d, const olk_attn_io *io) {
   if (w == 0 || w < -1) return OLK_E_ATTR;
   if (w > 0 && (d->op != OLK_OP_GQA || !d->causal)) return OLK_E_ATTR;
   if (d->softcap > 0.f && d->op == OLK_OP_MHA) return OLK_E_ATTR;
+  // rotary embedding: GroupQueryAttention only; R even, 0 < R <= D
+  if (d->do_rotary != 0 && d->do_rotary != 1) return OLK_E_ATTR;
+  if (d->rotary_interleaved != 0 && d->rotary_interleaved != 1) return OLK_E_ATTR;
+  if (d->do_rotary) {
+    const int R = d->rotary_dim > 0 ? d->rotary_dim : d->head_size;
+    if (d->op != OLK_OP_GQA || d->rotary_dim < 0 || R % 2 || R > d->head_size) return OLK_E_ATTR;
+    if (d->rotary_max_pos <= 0) return OLK_E_SHAPE;
+  }
 
   if (d->batch < 0 || d->q_seq < 0 || d->kv_seq < 0 || d->past_seq < 0) return OLK_E_SHAPE;
   if (d->q_num_heads <= 0 || d->kv_num_heads <= 0) return OLK_E_SHAPE;
@@ -131,13 +141,20 @@ olk_status validate(const olk_attn_desc *d, const olk_attn_io *io) {
     if ((!io->past_k && sz.past_k) || (!io->past_v && sz.past_v)) return OLK_E_NULL;
   }
   if (d->head_size > 256 || d->v_head_size > 256) return OLK_E_UNSUPPORTED;
+  if (d->do_rotary && sz.q) {
+    if (!io->cos_cache || !io->sin_cache) return OLK_E_NULL;
+    // the rotated keys are written to present and read back; rotated Q is
+    // staged in Y, which needs Y rows of Q's width
+    if (!io->present_k || !io->present_v) return OLK_E_UNSUPPORTED;
+    if (d->v_head_size != d->head_size) return OLK_E_UNSUPPORTED;
+  }
   if (d->q_num_heads > 65535 || d->batch > 65535) return OLK_E_UNSUPPORTED;
 
   // Outputs must not overlap inputs or each other (kv_inplace: present is the past).
   const Range outs[3] = {{(const char *)io->y, sz.y},
                          {(const char *)io->present_k, sz.pres_k},
                          {(const char *)io->present_v, sz.pres_v}};
-  const Range ins[8] = {{(const char *)io->q, sz.q},
+  const Range ins[10] = {{(const char *)io->q, sz.q},
                         {(const char *)io->k, sz.k},
                         {(const char *)io->v, sz.v},
                         {d->kv_inplace ? nullptr : (const char *)io->past_k,
@@ -146,9 +163,11 @@ olk_status validate(const olk_attn_desc *d, const olk_attn_io *io) {
                          d->past_seq ? sz.past_v : 0},
                         {(const char *)io->attn_bias, io->attn_bias ? sz.bias : 0},
                         {(const char *)io->head_sink, io->head_sink ? sz.sink : 0},
-                        {(const char *)io->proj_bias, io->proj_bias ? sz.proj : 0}};
+                        {(const char *)io->proj_bias, io->proj_bias ? sz.proj : 0},
+                        {(const char *)io->cos_cache, sz.rot},
+                        {(const char *)io->sin_cache, sz.rot}};
   for (int a = 0; a < 3; ++a) {
-    for (int b = 0; b < 8; ++b)
+    for (int b = 0; b < 10; ++b)
       if (overlaps(outs[a], ins[b])) return OLK_E_SHAPE;
     for (int b = a + 1; b < 3; ++b)
       if (overlaps(outs[a], outs[b])) return OLK_E_SHAPE;
@@ -209,7 +228,33 @@ olk::Params make_params(const olk_attn_desc *d, const olk_attn_io *io) {
   p.softcap = d->softcap;
   p.mfv = d->mask_filter_value;
   p.pad_add = (d->op == OLK_OP_MHA && io->seqlens) ? 1 : 0;
+  p.cos_cache = io->cos_cache;
+  p.sin_cache = io->sin_cache;
+  p.rot_dim = d->rotary_dim > 0 ? d->rotary_dim : d->head_size;
+  p.rot_inter = d->rotary_interleaved;
+  p.rot_max = d->rotary_max_pos;
   return p;
+}
+
+// do_rotary: copy the past rows into present (out of place), run the rotary
+// pre-pass (rotated Q into Y, rotated new K and new V into present), and
+// return the parameters of the attention proper: Q read from Y, every key read
+// from present, nothing left for the attention kernels to write into present.
+hipError_t rotary_prepass(olk::Params &p, int dtype, hipStream_t st) {
+  olk::Params pp = p;
+  pp.present_past_only = 1;
+  hipError_t e = olk::launch_present(pp, dtype, st);
+  if (e != hipSuccess) return e;
+  e = olk::launch_rope(p, dtype, st);
+  if (e != hipSuccess) return e;
+  p.q = p.y;
+  p.q_sb = p.y_sb; p.q_ss = p.y_ss; p.q_sh = p.y_sh;
+  p.past_k = p.present_k;
+  p.past_v = p.present_v;
+  p.past_rows = p.T;
+  p.keys_in_past = 1;
+  p.present_k = p.present_v = nullptr;
+  return hipSuccess;
 }
 
 int n_splits(const olk_attn_desc *d, int split_keys = kSplitKeys) {
@@ -240,18 +285,27 @@ olk_status olk_attention_fwd(const olk_attn_desc *desc, const olk_attn_io *io, v
   if (st != OLK_OK) return st;
   olk::Params p = make_params(desc, io);
   hipStream_t s = (hipStream_t)stream;
-  const bool tiled_ok = olk::tiled_supports(p, desc->dtype);
+  // the kernel choice is made on the parameters the attention kernel gets (with
+  // do_rotary, Q is read from Y); check it before anything is launched
+  olk::Params pa = p;
+  if (desc->do_rotary) { pa.q = pa.y; pa.q_sb = pa.y_sb; pa.q_ss = pa.y_ss; pa.q_sh = pa.y_sh; }
+  const bool tiled_ok = olk::tiled_supports(pa, desc->dtype);
   if (desc->kernel == OLK_KERNEL_TILED && !tiled_ok) return OLK_E_UNSUPPORTED;
   const bool use_tiled = desc->kernel != OLK_KERNEL_GENERIC && tiled_ok;
-  if (use_tiled && olk::flash_fuses_present(p)) p.present_past_only = 1;
-  hipError_t e = olk::launch_present(p, desc->dtype, s);
+  hipError_t e = hipSuccess;
+  if (desc->do_rotary) {
+    e = rotary_prepass(p, desc->dtype, s);
+  } else {
+    if (use_tiled && olk::flash_fuses_present(p)) p.present_past_only = 1;
+    e = olk::launch_present(p, desc->dtype, s);
+  }
   if (e != hipSuccess) return OLK_E_HIP;
   if (use_tiled) {
     e = olk::launch_flash(p, desc->dtype, s);
-    g_last_kernel = "olk_tiled_fwd";
+    g_last_kernel = desc->do_rotary ? "olk_rope+olk_tiled_fwd" : "olk_tiled_fwd";
   } else {
     e = olk::launch_generic(p, desc->dtype, s);
-    g_last_kernel = "olk_generic_fwd";
+    g_last_kernel = desc->do_rotary ? "olk_rope+olk_generic_fwd" : "olk_generic_fwd";
   }
   return e == hipSuccess ? OLK_OK : OLK_E_HIP;
 }
@@ -265,13 +319,16 @@ olk_status olk_attention_decode(const olk_attn_desc *desc, const olk_attn_io *io
   const size_t need = olk_workspace_bytes(desc);
   if (need && (!workspace || workspace_bytes < need)) return OLK_E_WORKSPACE;
   if (((uintptr_t)workspace & 15) != 0) return OLK_E_WORKSPACE;
-  const olk::Params p = make_params(desc, io);
+  olk::Params p = make_params(desc, io);
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = olk::launch_present(p, desc->dtype, s);
+  olk::Params pa = p;
+  if (desc->do_rotary) { pa.q = pa.y; pa.q_sb = pa.y_sb; pa.q_ss = pa.y_ss; pa.q_sh = pa.y_sh; }
+  const bool tiled_ok = olk::tiled_supports(pa, desc->dtype);
+  if (desc->kernel == OLK_KERNEL_TILED && !tiled_ok) return OLK_E_UNSUPPORTED;
+  hipError_t e = desc->do_rotary ? rotary_prepass(p, desc->dtype, s)
+                                 : olk::launch_present(p, desc->dtype, s);
   if (e != hipSuccess) return OLK_E_HIP;
   const int n_split = n_splits(desc);
-  const bool tiled_ok = olk::tiled_supports(p, desc->dtype);
-  if (desc->kernel == OLK_KERNEL_TILED && !tiled_ok) return OLK_E_UNSUPPORTED;
   int n_comb = n_split;
   if (desc->kernel != OLK_KERNEL_GENERIC && tiled_ok && olk::decode_supports(p, desc->dtype)) {
     n_comb = n_splits(desc, kDecodeSplitKeys);

@@ -149,12 +149,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p, DPlan pl) {
   auto load_step = [&](int st, uint4 (&kk)[NKS], uint2 (&vv)[kStep / 2]) {
     const int j0 = base + (wave + 4 * st) * kStep;
     const bool full = j0 >= sp_lo && j0 + kStep <= sp_hi;
-    if (full && (j0 >= s.past || j0 + kStep <= s.past)) {
+    if (full && (j0 >= s.src || j0 + kStep <= s.src)) {
       // the whole step from one source: uniform base + 32-bit lane offsets
-      const bool from_new = j0 >= s.past;
-      const char *kb = (const char *)(from_new ? knew + (int64_t)(j0 - s.past) * p.k_ss
+      const bool from_new = j0 >= s.src;
+      const char *kb = (const char *)(from_new ? knew + (int64_t)(j0 - s.src) * p.k_ss
                                                : kpast + (int64_t)j0 * D);
-      const char *vb = (const char *)(from_new ? vnew + (int64_t)(j0 - s.past) * p.v_ss
+      const char *vb = (const char *)(from_new ? vnew + (int64_t)(j0 - s.src) * p.v_ss
                                                : vpast + (int64_t)j0 * D);
       const uint32_t krs = (uint32_t)(from_new ? p.k_ss : D) * (uint32_t)sizeof(T);
       const uint32_t vrs = (uint32_t)(from_new ? p.v_ss : D) * (uint32_t)sizeof(T);
@@ -177,8 +177,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p, DPlan pl) {
     // data, so the compiler's count of loads in flight stays exact.
     auto row_ptr = [&](const T *pastp, const T *newp, int64_t new_ss, int j) {
       const int jj = j >= sp_lo && j < sp_hi ? j : sp_lo;
-      const bool nw = jj >= s.past;
-      const int64_t off_new = (int64_t)(jj - s.past) * new_ss, off_past = (int64_t)jj * D;
+      const bool nw = jj >= s.src;
+      const int64_t off_new = (int64_t)(jj - s.src) * new_ss, off_past = (int64_t)jj * D;
       return (nw ? newp : pastp) + (nw ? off_new : off_past);
     };
     const T *ks = row_ptr(kpast, knew, p.k_ss, j0 + n);

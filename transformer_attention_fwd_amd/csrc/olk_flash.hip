@@ -222,7 +222,7 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Params p, FPlan 
   // Row j of K or V: the past buffer below past_b, the new input above; keys
   // outside [lo, hi) read as zeros, never NaN.
   auto load_row = [&](int j, const T *pastp, const T *newp, int64_t new_ss, int chunk) __attribute__((always_inline)) {
-    const T *src = j >= s.past ? newp + (int64_t)(j - s.past) * new_ss : pastp + (int64_t)j * D;
+    const T *src = j >= s.src ? newp + (int64_t)(j - s.src) * new_ss : pastp + (int64_t)j * D;
     return j >= lo && j < hi ? *(const uint4 *)(src + chunk * 8) : make_uint4(0, 0, 0, 0);
   };
   // Whole tiles inside one source use a uniform base plus 32-bit lane offsets.
@@ -232,13 +232,13 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Params p, FPlan 
     constexpr int NU = sizeof(buf) / sizeof(buf[0]);
     const int j0 = kt * BN;
     const bool full = j0 >= lo && j0 + BN <= hi;
-    if (full && j0 >= s.past) {
-      const char *base = (const char *)(newp + (int64_t)(j0 - s.past) * new_ss);
+    if (full && j0 >= s.src) {
+      const char *base = (const char *)(newp + (int64_t)(j0 - s.src) * new_ss);
       const uint32_t rs = (uint32_t)new_ss * (uint32_t)sizeof(T);
       const uint32_t off = (uint32_t)r0 * rs + (uint32_t)chunk * 16u;
 #pragma unroll
       for (int u = 0; u < NU; ++u) buf[u] = *(const uint4 *)(base + off + u * rstep * rs);
-    } else if (full && j0 + BN <= s.past) {
+    } else if (full && j0 + BN <= s.src) {
       const char *base = (const char *)(pastp + (int64_t)j0 * D);
       const uint32_t rs = D * (uint32_t)sizeof(T);
       const uint32_t off = (uint32_t)r0 * rs + (uint32_t)chunk * 16u;

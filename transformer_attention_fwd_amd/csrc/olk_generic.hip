@@ -33,14 +33,14 @@ template <typename T>
 __device__ __forceinline__ const T *kv_row(const Params &p, const Seq &s, int b, int g, int j,
                                            bool value) {
   const int width = value ? p.Dv : p.D;
-  if (j < s.past) {
+  if (j < s.src) {
     const T *past = (const T *)(value ? p.past_v : p.past_k);
     return past + (((int64_t)b * p.Hkv + g) * p.past_rows + j) * width;
   }
   const T *cur = (const T *)(value ? p.v : p.k);
   const int64_t sb = value ? p.v_sb : p.k_sb, ss = value ? p.v_ss : p.k_ss,
                 sh = value ? p.v_sh : p.k_sh;
-  return cur + b * sb + (int64_t)(j - s.past) * ss + g * sh;
+  return cur + b * sb + (int64_t)(j - s.src) * ss + g * sh;
 }
 
 struct RowState {

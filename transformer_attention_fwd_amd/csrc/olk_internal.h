@@ -34,6 +34,11 @@ struct Params {
   float scale;     // score multiplier
   float softcap;   // > 0: softcap * tanh(s / softcap)
   float mfv;       // mask_filter_value
+  int keys_in_past;  // every key j < total_b is read from past_k/past_v (the rotary
+                     // path has already written the rotated new keys into present)
+  // rotary embedding (used by the rotary pre-pass only)
+  const void *cos_cache, *sin_cache;
+  int rot_dim, rot_inter, rot_max;
 };
 
 // Per-batch sequence bookkeeping (integer; read once per workgroup).
@@ -43,6 +48,7 @@ struct Seq {
   int valid;  // keys j < valid may be attended
   int pad;    // keys j >= pad get mfv added (MultiHeadAttention, additive mode)
   int qoff;   // absolute position of query 0 (bottom-right causal alignment)
+  int src;    // keys j < src are read from the past buffer, the rest from the new K/V
 };
 
 __device__ __forceinline__ Seq seq_info(const Params &p, int b) {
@@ -73,6 +79,7 @@ __device__ __forceinline__ Seq seq_info(const Params &p, int b) {
       }
     }
   }
+  s.src = p.keys_in_past ? s.total : s.past;
   return s;
 }
 
@@ -86,5 +93,6 @@ hipError_t launch_generic_split(const Params &p, int dtype, int chunk, int n_spl
 hipError_t launch_combine(const Params &p, int dtype, int n_split, const float *ws,
                           hipStream_t st);
 hipError_t launch_present(const Params &p, int dtype, hipStream_t st);
+hipError_t launch_rope(const Params &p, int dtype, hipStream_t st);
 
 }  // namespace olk

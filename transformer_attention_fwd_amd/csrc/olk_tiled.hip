@@ -192,12 +192,12 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_kernel(Params p, Plan pl) {
       const int j = kt * kBN + ld_row + u * ROW_STEP;
       const int c = ld_chunk * 8;
       if (j >= lo && j < hi) {
-        if (j < s.past) {
+        if (j < s.src) {
           kbuf[u] = *(const uint4 *)(kpast + (int64_t)j * D + c);
           vbuf[u] = *(const uint4 *)(vpast + (int64_t)j * D + c);
         } else {
-          kbuf[u] = *(const uint4 *)(knew + (int64_t)(j - s.past) * p.k_ss + c);
-          vbuf[u] = *(const uint4 *)(vnew + (int64_t)(j - s.past) * p.v_ss + c);
+          kbuf[u] = *(const uint4 *)(knew + (int64_t)(j - s.src) * p.k_ss + c);
+          vbuf[u] = *(const uint4 *)(vnew + (int64_t)(j - s.src) * p.v_ss + c);
         }
       } else {  // outside the workgroup's key range: zeros (never NaN garbage)
         kbuf[u] = make_uint4(0, 0, 0, 0);

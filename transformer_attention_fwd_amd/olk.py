@@ -43,13 +43,15 @@ class olk_attn_desc(ctypes.Structure):
         ("scale", ctypes.c_float), ("softcap", ctypes.c_float),
         ("mask_filter_value", ctypes.c_float),
         ("bias_b", ctypes.c_int32), ("bias_h", ctypes.c_int32),
-        ("kv_inplace", ctypes.c_int32), ("kernel", ctypes.c_int32)]
+        ("kv_inplace", ctypes.c_int32), ("kernel", ctypes.c_int32)] + [
+        (n, ctypes.c_int32) for n in ("do_rotary", "rotary_interleaved", "rotary_dim",
+                                      "rotary_max_pos")]
 
 
 class olk_attn_io(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "q", "k", "v", "past_k", "past_v", "seqlens", "attn_bias", "head_sink",
-        "proj_bias", "y", "present_k", "present_v")]
+        "proj_bias", "y", "present_k", "present_v", "cos_cache", "sin_cache")]
 
 
 _P = ctypes.POINTER
@@ -120,7 +122,9 @@ def make_desc(p: Problem, kernel: str = "auto", kv_inplace: bool = False) -> olk
         local_window_size=p.window, has_scale=0 if p.scale is None else 1,
         scale=0.0 if p.scale is None else p.scale, softcap=p.softcap,
         mask_filter_value=p.mask_filter_value, bias_b=bb, bias_h=bh,
-        kv_inplace=1 if kv_inplace else 0, kernel=KERNELS[kernel])
+        kv_inplace=1 if kv_inplace else 0, kernel=KERNELS[kernel],
+        do_rotary=p.rotary, rotary_interleaved=p.rotary_interleaved,
+        rotary_dim=p.rotary_dim, rotary_max_pos=p.max_pos if p.rotary else 0)
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -139,7 +143,8 @@ def make_io(tensors: Dict[str, torch.Tensor], y: torch.Tensor,
                        past_k=_ptr(g("past_k")), past_v=_ptr(g("past_v")),
                        seqlens=_ptr(g("lens")), attn_bias=_ptr(g("bias")),
                        head_sink=_ptr(g("sink")), proj_bias=_ptr(g("proj_bias")),
-                       y=_ptr(y), present_k=_ptr(present_k), present_v=_ptr(present_v))
+                       y=_ptr(y), present_k=_ptr(present_k), present_v=_ptr(present_v),
+                       cos_cache=_ptr(g("cos_cache")), sin_cache=_ptr(g("sin_cache")))
 
 
 def current_stream() -> int:

@@ -15,6 +15,8 @@ Tensor layouts (all row-major, element type = ``dtype`` unless stated):
 * ``bias``  (bias_b, bias_h, S, P+L) additive attention bias
 * ``sink``  (Hq,) per-head virtual logit (GroupQueryAttention ``head_sink``)
 * ``proj_bias`` (2*Hq*D + Hq*Dv,) MultiHeadAttention projection bias [q | k | v]
+* ``cos_cache``/``sin_cache`` (max_pos, R/2) rotary tables (GroupQueryAttention
+  with ``rotary``); deterministic, not drawn
 
 Draw order inside one problem is fixed: q, k, v, past_k, past_v, lens, bias,
 sink, proj_bias (absent tensors are skipped).  Normals are drawn as float32 from
@@ -66,11 +68,26 @@ class Problem:
     sigma_bias: float = 0.1
     sigma_sink: float = 1.0
     sigma_proj: float = 0.02
+    # rotary embedding (GroupQueryAttention do_rotary): cos/sin caches of
+    # rotary_max_pos rows (0: P + L) and R/2 columns, R = rotary_dim (0: D)
+    rotary: int = 0
+    rotary_interleaved: int = 0
+    rotary_dim: int = 0
+    rotary_max_pos: int = 0
+    rotary_base: float = 10000.0
 
     @property
     def T(self) -> int:
         """Present length / key columns of the bias: P + L."""
         return self.P + self.L
+
+    @property
+    def R(self) -> int:
+        return self.rotary_dim if self.rotary_dim > 0 else self.D
+
+    @property
+    def max_pos(self) -> int:
+        return self.rotary_max_pos if self.rotary_max_pos > 0 else self.P + self.L
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -80,7 +97,7 @@ class Problem:
         return replace(self, **kw)
 
 
-# The five workloads.  Sizes and distributions follow the workload list of the
+# The workloads.  Sizes and distributions follow the workload list of the
 # attention-forward study; each is named by what it is.
 WORKLOADS: Dict[str, Problem] = {
     # fp32 GQA prefill, tiny: B=1 S=16, 4 q heads / 2 kv heads, D=32, causal
@@ -104,6 +121,11 @@ WORKLOADS: Dict[str, Problem] = {
         op="mha", dtype="f16", B=8, S=448, L=1500, P=0, Hq=20, Hkv=20, D=64,
         Dv=64, kv_rank=4, causal=0, window=-1, bias_bh=(1, 20),
         has_lens=True, lens_range=(1000, 1500), has_proj_bias=True),
+    # the bf16 causal prefill with rotary embedding fused in (do_rotary, split
+    # halves over the full head): Q/K rotated at positions 0..S-1
+    "gqa_prefill_rope_bf16": Problem(
+        op="gqa", dtype="bf16", B=4, S=2048, L=2048, P=0, Hq=32, Hkv=8, D=128,
+        Dv=128, causal=1, window=-1, rotary=1),
 }
 
 WORKLOAD_ORDER = [
@@ -112,6 +134,7 @@ WORKLOAD_ORDER = [
     "gqa_prefill_window_sink_bf16",
     "gqa_decode_f16",
     "mha_cross_f16",
+    "gqa_prefill_rope_bf16",
 ]
 
 
@@ -198,7 +221,21 @@ def make_inputs(p: Problem, seed: int, lens: Optional[np.ndarray] = None
     if p.has_proj_bias:
         out["proj_bias"] = _normal(rng, (2 * p.Hq * p.D + p.Hq * p.Dv,),
                                    p.sigma_proj, dt, 1)
+    if p.rotary:
+        out["cos_cache"], out["sin_cache"] = rotary_tables(p)
     return out
+
+
+def rotary_tables(p: Problem) -> Tuple[torch.Tensor, torch.Tensor]:
+    """cos/sin caches (max_pos, R/2) with the usual frequency schedule
+    base^(-2k/R), computed in float64 and rounded to the element type.  They
+    are inputs of the operator (no random draws)."""
+    half = p.R // 2
+    pos = np.arange(p.max_pos, dtype=np.float64)[:, None]
+    inv = p.rotary_base ** (-2.0 * np.arange(half, dtype=np.float64) / p.R)
+    ang = pos * inv[None, :]
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a.astype(np.float32))).to(p.torch_dtype)
+    return to(np.cos(ang)), to(np.sin(ang))
 
 
 def workload(name: str) -> Tuple[Problem, Dict[str, torch.Tensor]]:
