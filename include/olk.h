@@ -68,6 +68,14 @@ typedef enum {
   OLK_KERNEL_TILED = 2    /* MFMA tiled kernel (f16/bf16, head size 64 or 128) */
 } olk_kernel;
 
+typedef enum {
+  OLK_MASK_NONE = 0,
+  OLK_MASK_BOOL = 1,         /* uint8, nonzero = attend (ai.onnx Attention) */
+  OLK_MASK_BINARY_I32 = 2    /* int32, nonzero = attend, zero = key padding: the score gets
+                                mask_filter_value added (MultiHeadAttention; excludes the
+                                key-padding lengths in seqlens) */
+} olk_mask_kind;
+
 /*
  * Attributes and sizes of one call.
  *  B = batch, S = q_seq, L = kv_seq (new keys), P = past_seq (past buffer
@@ -117,6 +125,29 @@ typedef struct {
   int32_t rotary_dim;        /* R: channels rotated, even, 0 < R <= D; 0 = D.  Channels >= R
                                 are copied unchanged. */
   int32_t rotary_max_pos;    /* rows of cos_cache / sin_cache (> 0 when do_rotary) */
+  /* Further attn_bias extents (the ai.onnx Attention FLOAT attn_mask is an
+   * attn_bias: onnx-light reference kernels header page, "class Attention",
+   * rank 2-4 masks broadcast to (B, Hq, S, T) and added; a mask whose last
+   * dimension is shorter than T is padded with -inf). */
+  int32_t bias_s;            /* 0 or S: one bias row per query; 1: broadcast over queries */
+  int32_t bias_t;            /* 0 or T: full rows; 0 < bias_t < T (Attention only): keys
+                                j >= bias_t are excluded (-inf padding) */
+  /* attn_mask (the same page: BOOL rank 2-4, true = attend, false = -inf,
+   * short masks padded with false; onnx-light-cpu Python API "Custom
+   * operators", MultiHeadAttention: binary key-padding masks (B,T) / (B,S,T)).
+   * Broadcast extents as for attn_bias; element (b, h, i, j) at
+   * ((b'*mask_h + h')*mask_s' + i')*mask_t + j with b', h', i' = 0 on broadcast
+   * dimensions. */
+  int32_t mask_kind;         /* olk_mask_kind */
+  int32_t mask_b, mask_h;    /* 1 or B, 1 or Hq */
+  int32_t mask_s;            /* 0 or S: per query row; 1: broadcast */
+  int32_t mask_t;            /* 0 or T: full; BOOL may be shorter (keys beyond are false) */
+  int32_t seqlens_i64;       /* ai.onnx Attention: 1 = seqlens points at int64
+                                nonpad_kv_seqlen values */
+  int32_t qk_mode;           /* ai.onnx Attention qk_matmul_output_mode when qk_out != NULL:
+                                0 (Q.K^T)*scale for every (i, j); 1 + attn_bias, excluded
+                                keys (causal, masks, nonpad, short padding) -inf; 2 after
+                                softcap (excluded -inf); 3 softmax weights (excluded 0) */
 } olk_attn_desc;
 
 /* Device pointers (caller-owned); NULL = absent. */
@@ -127,7 +158,7 @@ typedef struct {
   const void *past_v;        /* (B,Hkv,P,Dv) or NULL */
   const int32_t *seqlens;    /* (B) int32.  GQA: seqlens_k = total length - 1 (required);
                                 MHA: key-padding lengths; Attention: non-padding lengths */
-  const void *attn_bias;     /* (bias_b, bias_h, S, T) additive, or NULL */
+  const void *attn_bias;     /* (bias_b, bias_h, S or 1, T or bias_t) additive, or NULL */
   const void *head_sink;     /* (Hq) GroupQueryAttention virtual logits, or NULL */
   const void *proj_bias;     /* MultiHeadAttention (2*Hq*D + Hq*Dv) = [q | k | v], or NULL;
                                 with rank-4 K/V only the q segment applies */
@@ -136,6 +167,8 @@ typedef struct {
   void *present_v;           /* (B,Hkv,T,Dv) output, or NULL = not requested */
   const void *cos_cache;     /* do_rotary: (rotary_max_pos, R/2) element type, row = position */
   const void *sin_cache;     /* do_rotary: (rotary_max_pos, R/2) element type */
+  const void *attn_mask;     /* see mask_kind, or NULL */
+  float *qk_out;             /* ai.onnx Attention: (B, Hq, S, T) float32 output, or NULL */
 } olk_attn_io;
 
 /*

@@ -51,6 +51,19 @@
  *       computed in float32 as fmaf(x1, c, -(x2*s)) and fmaf(x2, c, x1*s) and
  *       rounded once (RNE), so present holds exactly these bits.  Positions
  *       beyond the cache use its last row.
+ *   R19 masks (reference kernels header page, "class Attention": FLOAT masks
+ *       rank 2-4 broadcast to (B, Hq, S, T) and added as a bias, BOOL masks
+ *       with false = -inf, a last dimension shorter than T padded with
+ *       -inf/false, INT64 nonpad_kv_seqlen; Python API page,
+ *       MultiHeadAttention: binary key-padding masks (B,T)/(B,S,T)).  A FLOAT
+ *       mask is the additive bias; keys beyond its columns, BOOL-false keys
+ *       and keys at or beyond nonpad are excluded after the score pipeline
+ *       (R6); a zero in a MultiHeadAttention binary mask adds
+ *       mask_filter_value like key padding (R9).
+ *   R20 qk_matmul_output (modes 0-3): mode 0 is (Q K^T) * scale for every
+ *       (i, j); modes 1 and 2 add the bias and apply the softcap to allowed
+ *       keys and hold -inf for excluded ones; mode 3 is the softmax weight
+ *       (0 for excluded keys).
  * Intermediate values are not rounded (apart from R18's rotated Q/K); Y is
  * returned in float64.
  */
@@ -75,6 +88,9 @@ typedef struct {
   float scale, softcap, mask_filter_value;
   int32_t bias_b, bias_h;
   int32_t do_rotary, rotary_interleaved, rotary_dim, rotary_max_pos;
+  int32_t bias_s, bias_t;                      /* bias rows: 1 = broadcast; columns (0 = T) */
+  int32_t mask_kind, mask_b, mask_h, mask_s, mask_t;
+  int32_t seqlens_i64;
 } ref_desc;
 
 typedef struct {
@@ -82,6 +98,7 @@ typedef struct {
   const int32_t *lens;
   const void *bias, *sink, *proj_bias;
   const void *cos_cache, *sin_cache;
+  const void *mask;
 } ref_inputs;
 
 /* ---- element decoding (format definitions, not attention arithmetic) ---- */
@@ -230,7 +247,7 @@ static int seq_info(const ref_desc *d, const ref_inputs *in, int b, seqinfo *s) 
     s->valid_b = T;
     s->pad_b = T;
     if (in->lens) {
-      long n = in->lens[b];
+      long n = d->seqlens_i64 ? (long)((const int64_t *)in->lens)[b] : (long)in->lens[b];
       if (n < 0) n = 0;
       if (n > T) n = T;
       if (d->op == REF_ATTENTION) s->valid_b = n; /* -inf beyond nonpad length */
@@ -249,6 +266,29 @@ static double key_elem(const ref_desc *d, const ref_inputs *in, const seqinfo *s
   const size_t base = new_kv_index(d, b, g, (int)(j - s->past_b), 0, width);
   if (d->do_rotary && !value) return rot_elem(d, in, cur, base, c, j); /* R18: new key at position j */
   return elem(cur, d->dtype, base + c);
+}
+
+/* R19: bias rows / columns and the attn_mask element of (b, h, i, j) */
+static long bias_cols(const ref_desc *d) {
+  long T = (long)d->past_seq + d->kv_seq;
+  return d->bias_t > 0 ? d->bias_t : T;
+}
+
+static double bias_at(const ref_desc *d, const ref_inputs *in, int b, int h, int i, long j) {
+  size_t bb = d->bias_b > 1 ? (size_t)b : 0, bh = d->bias_h > 1 ? (size_t)h : 0;
+  size_t rows = d->bias_s == 1 ? 1 : (size_t)d->q_seq, bi = d->bias_s == 1 ? 0 : (size_t)i;
+  return elem(in->bias, d->dtype, ((bb * d->bias_h + bh) * rows + bi) * (size_t)bias_cols(d) + j);
+}
+
+static int mask_at(const ref_desc *d, const ref_inputs *in, int b, int h, int i, long j) {
+  long T = (long)d->past_seq + d->kv_seq;
+  long cols = d->mask_t > 0 ? d->mask_t : T;
+  if (j >= cols) return 0;
+  size_t mb = d->mask_b > 1 ? (size_t)b : 0, mh = d->mask_h > 1 ? (size_t)h : 0;
+  size_t rows = d->mask_s == 1 ? 1 : (size_t)d->q_seq, mi = d->mask_s == 1 ? 0 : (size_t)i;
+  size_t e = ((mb * d->mask_h + mh) * rows + mi) * (size_t)cols + j;
+  if (d->mask_kind == 1) return ((const uint8_t *)in->mask)[e] != 0;
+  return ((const int32_t *)in->mask)[e] != 0;
 }
 
 static double scale_of(const ref_desc *d) {
@@ -282,21 +322,22 @@ static long row_weights(const ref_desc *d, const ref_inputs *in, int b, int h, i
   long n_allowed = 0;
   double m = -INFINITY;
   unsigned char *ok = (unsigned char *)malloc((size_t)s.total_b + 1);
+  (void)T;
   for (long j = 0; j < s.total_b; ++j) {
     int allowed = j < s.valid_b;
     if (d->causal && j > pos) allowed = 0;
     if (d->window > 0 && j < pos - d->window + 1) allowed = 0;
+    if (in->bias && j >= bias_cols(d)) allowed = 0;                     /* R19: short mask */
+    if (d->mask_kind == 1 && !mask_at(d, in, b, h, i, j)) allowed = 0;  /* R19: BOOL false */
     ok[j] = (unsigned char)allowed;
     if (!allowed) { w[j] = 0.0; continue; }
     double dot = 0.0;
     for (int c = 0; c < D; ++c) dot += qbuf[c] * key_elem(d, in, &s, b, g, j, c, 0);
     double sc = dot * scale;
-    if (in->bias) {
-      size_t bb = d->bias_b > 1 ? (size_t)b : 0, bh = d->bias_h > 1 ? (size_t)h : 0;
-      sc += elem(in->bias, d->dtype, ((bb * d->bias_h + bh) * d->q_seq + i) * (size_t)T + j);
-    }
+    if (in->bias) sc += bias_at(d, in, b, h, i, j);
     if (d->softcap > 0.0f) sc = (double)d->softcap * tanh(sc / (double)d->softcap);
     if (d->op == REF_MHA && j >= s.pad_b) sc += (double)d->mask_filter_value;
+    if (d->mask_kind == 2 && !mask_at(d, in, b, h, i, j)) sc += (double)d->mask_filter_value; /* R19 */
     w[j] = sc;
     if (sc > m) m = sc;
     ++n_allowed;
@@ -330,6 +371,7 @@ static int check_desc(const ref_desc *d, const ref_inputs *in) {
   if (d->head_size <= 0 || d->v_head_size <= 0 || d->batch < 0 || d->q_seq < 0) return -1;
   if (d->op == REF_GQA && (!in->lens || d->kv_seq != d->q_seq)) return -1;
   if (d->past_seq > 0 && (!in->past_k || !in->past_v)) return -1;
+  if (d->mask_kind && !in->mask) return -1;
   if (d->do_rotary) {
     const int R = rot_dim(d);
     if (d->op != REF_GQA || !in->cos_cache || !in->sin_cache) return -1;
@@ -455,4 +497,53 @@ int olk_ref_present(const ref_desc *d, const ref_inputs *in, void *pk, void *pv)
     }
   }
   return 0;
+}
+
+/* R20: qk_matmul_output of every row, float64 (B, Hq, S, T). */
+int olk_ref_qk(const ref_desc *d, const ref_inputs *in, int mode, double *out, int threads) {
+  if (check_desc(d, in) != 0 || !out || mode < 0 || mode > 3) return -1;
+  const long T = (long)d->past_seq + d->kv_seq;
+  const long rows = (long)d->batch * d->q_heads * d->q_seq;
+  int err = 0;
+#ifdef _OPENMP
+  if (threads > 0) omp_set_num_threads(threads);
+#endif
+#pragma omp parallel reduction(|| : err)
+  {
+    double *w = (double *)malloc(sizeof(double) * (size_t)max_keys(d));
+    double *qbuf = (double *)malloc(sizeof(double) * (size_t)d->head_size);
+#pragma omp for schedule(dynamic, 4)
+    for (long r = 0; r < rows; ++r) {
+      int i = (int)(r % d->q_seq);
+      int h = (int)((r / d->q_seq) % d->q_heads);
+      int b = (int)(r / ((long)d->q_heads * d->q_seq));
+      double *o = out + (size_t)r * T;
+      double sink_w;
+      seqinfo s;
+      long n = row_weights(d, in, b, h, i, w, &sink_w, qbuf, &s); /* fills qbuf, weights */
+      if (n < 0) { err = 1; continue; }
+      const int g = h / (d->q_heads / d->kv_heads);
+      const long pos = s.q_off + i;
+      for (long j = 0; j < T; ++j) {
+        if (mode == 3) { o[j] = j < s.total_b ? w[j] : 0.0; continue; }
+        double dot = 0.0;
+        if (j < s.total_b)
+          for (int c = 0; c < d->head_size; ++c) dot += qbuf[c] * key_elem(d, in, &s, b, g, j, c, 0);
+        double sc = dot * scale_of(d);
+        if (mode == 0) { o[j] = sc; continue; }
+        int allowed = j < s.valid_b && j < s.total_b;
+        if (d->causal && j > pos) allowed = 0;
+        if (d->window > 0 && j < pos - d->window + 1) allowed = 0;
+        if (in->bias && j >= bias_cols(d)) allowed = 0;
+        if (d->mask_kind == 1 && !mask_at(d, in, b, h, i, j)) allowed = 0;
+        if (!allowed) { o[j] = -INFINITY; continue; }
+        if (in->bias) sc += bias_at(d, in, b, h, i, j);
+        if (mode == 2 && d->softcap > 0.0f) sc = (double)d->softcap * tanh(sc / (double)d->softcap);
+        o[j] = sc;
+      }
+    }
+    free(w);
+    free(qbuf);
+  }
+  return err ? -1 : 0;
 }

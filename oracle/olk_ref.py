@@ -32,13 +32,14 @@ class _Desc(ctypes.Structure):
         ("mask_filter_value", ctypes.c_float),
         ("bias_b", ctypes.c_int32), ("bias_h", ctypes.c_int32)] + [
         (n, ctypes.c_int32) for n in ("do_rotary", "rotary_interleaved", "rotary_dim",
-                                      "rotary_max_pos")]
+                                      "rotary_max_pos", "bias_s", "bias_t", "mask_kind",
+                                      "mask_b", "mask_h", "mask_s", "mask_t", "seqlens_i64")]
 
 
 class _Inputs(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "q", "k", "v", "past_k", "past_v", "lens", "bias", "sink", "proj_bias",
-        "cos_cache", "sin_cache")]
+        "cos_cache", "sin_cache", "mask")]
 
 
 def build(force: bool = False) -> str:
@@ -68,6 +69,8 @@ def lib():
                                              ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
         _lib.olk_ref_row_weights.restype = ctypes.c_long
         _lib.olk_ref_present.argtypes = [P(_Desc), P(_Inputs), ctypes.c_void_p, ctypes.c_void_p]
+        _lib.olk_ref_qk.argtypes = [P(_Desc), P(_Inputs), ctypes.c_int, ctypes.c_void_p,
+                                    ctypes.c_int]
     return _lib
 
 
@@ -81,7 +84,13 @@ def _desc(p) -> _Desc:
                  scale=0.0 if p.scale is None else p.scale, softcap=p.softcap,
                  mask_filter_value=p.mask_filter_value, bias_b=bb, bias_h=bh,
                  do_rotary=p.rotary, rotary_interleaved=p.rotary_interleaved,
-                 rotary_dim=p.rotary_dim, rotary_max_pos=p.max_pos)
+                 rotary_dim=p.rotary_dim, rotary_max_pos=p.max_pos,
+                 bias_s=1 if p.bias_s_bcast else 0, bias_t=p.bias_cols,
+                 mask_kind={"": 0, "bool": 1, "int32": 2}[p.mask_kind],
+                 mask_b=p.mask_bhs[0] if p.mask_bhs else 1,
+                 mask_h=p.mask_bhs[1] if p.mask_bhs else 1,
+                 mask_s=(1 if p.mask_bhs[2] == 1 else 0) if p.mask_bhs else 0,
+                 mask_t=p.mask_cols, seqlens_i64=1 if p.lens_i64 else 0)
 
 
 class _Bound:
@@ -91,7 +100,7 @@ class _Bound:
         self.keep = {}
         ptrs = {}
         for name in ("q", "k", "v", "past_k", "past_v", "lens", "bias", "sink", "proj_bias",
-                     "cos_cache", "sin_cache"):
+                     "cos_cache", "sin_cache", "mask"):
             t = inputs.get(name)
             if t is None:
                 ptrs[name] = None
@@ -157,3 +166,14 @@ def present(p, inputs: Dict[str, torch.Tensor], fill: Optional[float] = None
     if rc != 0:
         raise ValueError("oracle rejected the problem")
     return pk, pv
+
+
+def qk(p, inputs: Dict[str, torch.Tensor], mode: int, threads: int = 0) -> np.ndarray:
+    """qk_matmul_output of ai.onnx Attention in float64, (B, Hq, S, T)."""
+    b = _Bound(inputs)
+    out = np.zeros((p.B, p.Hq, p.S, p.T), dtype=np.float64)
+    rc = lib().olk_ref_qk(ctypes.byref(_desc(p)), ctypes.byref(b.s), mode, out.ctypes.data,
+                          threads)
+    if rc != 0:
+        raise ValueError("oracle rejected the problem")
+    return out

@@ -216,3 +216,42 @@ def test_rotary_rules():
     io = fake_io(rope)
     io.cos_cache = io.y
     assert olk.olk_validate(olk.make_desc(rope), io) == olk.OLK_E_SHAPE
+
+
+def test_mask_rules():
+    att = Problem(op="attention", dtype="bf16", B=2, S=8, L=8, Hq=4, Hkv=2, D=64, Dv=64,
+                  has_lens=False)
+    mha = MHA.with_(has_lens=False)
+
+    def st(p, **io):
+        d = olk.make_desc(p)
+        f = fake_io(p, **io)
+        if p.mask_kind:
+            f.attn_mask = _BASE + 40 * (1 << 36)
+        return olk.olk_validate(d, f)
+
+    assert st(att.with_(mask_kind="bool", mask_bhs=(1, 1, 8))) == olk.OLK_OK
+    assert st(att.with_(mask_kind="bool", mask_bhs=(2, 4, 1), mask_cols=5)) == olk.OLK_OK
+    assert st(att.with_(mask_kind="bool", mask_bhs=(3, 1, 1))) == olk.OLK_E_SHAPE
+    assert st(att.with_(mask_kind="bool", mask_bhs=(1, 1, 8), mask_cols=9)) == olk.OLK_E_SHAPE
+    assert st(GQA.with_(mask_kind="bool", mask_bhs=(1, 1, 1))) == olk.OLK_E_ATTR  # GQA: none
+    assert st(mha.with_(mask_kind="int32", mask_bhs=(8, 1, 1))) == olk.OLK_OK
+    assert st(mha.with_(mask_kind="bool", mask_bhs=(8, 1, 1))) == olk.OLK_E_ATTR
+    # one key-padding input: lengths or a binary mask
+    assert st(MHA.with_(mask_kind="int32", mask_bhs=(8, 1, 1))) == olk.OLK_E_ATTR
+    assert st(mha.with_(mask_kind="int32", mask_bhs=(8, 1, 1), mask_cols=7)) == olk.OLK_E_SHAPE
+    d = olk.make_desc(att.with_(mask_kind="bool", mask_bhs=(1, 1, 8)))
+    assert olk.olk_validate(d, fake_io(att)) == olk.OLK_E_NULL          # mask pointer missing
+    # short FLOAT masks and query-broadcast bias rows
+    assert status(att.with_(bias_bh=(1, 1), bias_s_bcast=True, bias_cols=3)) == olk.OLK_OK
+    assert status(MHA.with_(bias_bh=(1, 20), bias_cols=10)) == olk.OLK_E_SHAPE
+    # int64 nonpad lengths and the qk output are ai.onnx Attention features
+    assert status(att.with_(has_lens=True, lens_i64=True)) == olk.OLK_OK
+    assert status(GQA.with_(lens_i64=True)) == olk.OLK_E_ATTR
+    qk = _BASE + 41 * (1 << 36)
+    assert status(att.with_(qk_mode=3), qk_out=qk) == olk.OLK_OK
+    assert status(att.with_(qk_mode=4), qk_out=qk) == olk.OLK_E_ATTR
+    assert status(GQA.with_(qk_mode=0), qk_out=qk) == olk.OLK_E_ATTR
+    io = fake_io(att)
+    io.qk_out = io.q
+    assert olk.olk_validate(olk.make_desc(att.with_(qk_mode=0)), io) == olk.OLK_E_SHAPE

@@ -573,3 +573,119 @@ def test_interleaved_equals_split_halves_under_channel_permutation():
     assert torch.equal(pk_i[..., perm], pk_s)
     np.testing.assert_allclose(olk_ref.attention(p, inp), olk_ref.attention(split, sp),
                                rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Mask surface (ai.onnx Attention attn_mask / nonpad_kv_seqlen / qk output;
+# MultiHeadAttention binary masks).
+# ---------------------------------------------------------------------------
+
+def _att(**kw):
+    base = dict(op="attention", dtype="f32", B=2, S=7, L=11, Hq=4, Hkv=2, D=16, Dv=16,
+                causal=0, has_lens=False)
+    base.update(kw)
+    return Problem(**base)
+
+
+def _sdpa_masked(p, inp, allow=None, add=None):
+    """torch SDPA in float64 with an explicit (B, Hq, S, T) boolean or additive mask."""
+    q = _bnsh_q(p, inp["q"])
+    k = _bnsh_kv(p, inp["k"], p.D).repeat_interleave(p.Hq // p.Hkv, dim=1)
+    v = _bnsh_kv(p, inp["v"], p.Dv).repeat_interleave(p.Hq // p.Hkv, dim=1)
+    m = allow if allow is not None else add
+    y = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=m)
+    return y.permute(0, 2, 1, 3).numpy()
+
+
+def test_bool_mask_matches_torch_sdpa_boolean_mask():
+    p = _att(mask_kind="bool", mask_bhs=(2, 1, 7))
+    inp = make_inputs(p, 61)
+    allow = inp["mask"].expand(p.B, p.Hq, p.S, p.T)
+    assert allow.any(dim=-1).all()
+    np.testing.assert_allclose(olk_ref.attention(p, inp), _sdpa_masked(p, inp, allow=allow),
+                               rtol=1e-10, atol=1e-12)
+
+
+def test_float_mask_broadcast_equals_expanded_bias():
+    # a (1, 1, 1, T) mask broadcast over batch, heads and queries is the expanded bias
+    p = _att(bias_bh=(1, 1), bias_s_bcast=True)
+    inp = make_inputs(p, 62)
+    full = p.with_(bias_bh=(2, 4), bias_s_bcast=False)
+    fi = dict(inp)
+    fi["bias"] = inp["bias"].expand(2, 4, p.S, p.T).contiguous()
+    assert np.array_equal(olk_ref.attention(p, inp), olk_ref.attention(full, fi))
+
+
+def test_short_masks_are_padded_with_exclusion():
+    # BOOL mask of 6 < T columns == the full mask padded with false
+    p = _att(mask_kind="bool", mask_bhs=(1, 4, 7), mask_cols=6)
+    inp = make_inputs(p, 63)
+    full = p.with_(mask_cols=0)
+    fi = dict(inp)
+    pad = torch.zeros(1, 4, 7, p.T, dtype=torch.bool)
+    pad[..., :6] = inp["mask"]
+    fi["mask"] = pad
+    assert np.array_equal(olk_ref.attention(p, inp), olk_ref.attention(full, fi))
+    # FLOAT mask of 6 columns == SDPA with the mask padded by -inf
+    q = _att(bias_bh=(2, 1), bias_cols=6)
+    qi = make_inputs(q, 64)
+    add = torch.full((2, 1, 7, q.T), -math.inf, dtype=torch.float64)
+    add[..., :6] = qi["bias"].double()
+    np.testing.assert_allclose(olk_ref.attention(q, qi), _sdpa_masked(q, qi, add=add),
+                               rtol=1e-10, atol=1e-12)
+
+
+def test_int64_nonpad_lengths_equal_int32():
+    p = _att(has_lens=True, lens_range=(1, 11))
+    inp = make_inputs(p, 65)
+    p64 = p.with_(lens_i64=True)
+    i64 = dict(inp)
+    i64["lens"] = inp["lens"].to(torch.int64)
+    assert np.array_equal(olk_ref.attention(p64, i64), olk_ref.attention(p, inp))
+
+
+def test_mha_binary_prefix_mask_equals_key_padding_lengths():
+    # a (B, T) binary mask of n_b leading ones == key-padding length n_b (both add mfv)
+    p = Problem(op="mha", dtype="f32", B=3, S=5, L=12, Hq=2, Hkv=2, D=8, Dv=8, kv_rank=3,
+                causal=0, has_lens=True, lens_range=(2, 12))
+    inp = make_inputs(p, 66)
+    lens = inp["lens"].numpy()
+    bm = p.with_(has_lens=False, mask_kind="int32", mask_bhs=(3, 1, 1))
+    bi = {k: v for k, v in inp.items() if k != "lens"}
+    m = np.zeros((3, 1, 1, p.T), dtype=np.int32)
+    for b in range(3):
+        m[b, 0, 0, : lens[b]] = 1
+    bi["mask"] = torch.from_numpy(m)
+    assert np.array_equal(olk_ref.attention(bm, bi), olk_ref.attention(p, inp))
+
+
+def test_mha_binary_mask_matches_sdpa_with_additive_filter_value():
+    p = Problem(op="mha", dtype="f32", B=2, S=5, L=9, Hq=2, Hkv=2, D=8, Dv=8, kv_rank=3,
+                causal=0, has_lens=False, mask_kind="int32", mask_bhs=(2, 1, 5),
+                mask_filter_value=-3.0)
+    inp = make_inputs(p, 67)
+    add = (1 - inp["mask"].double()).expand(2, 2, 5, 9) * -3.0
+    np.testing.assert_allclose(olk_ref.attention(p, inp), _sdpa_masked(p, inp, add=add),
+                               rtol=1e-10, atol=1e-12)
+
+
+def test_qk_output_modes():
+    p = _att(causal=1, P=3, mask_kind="bool", mask_bhs=(1, 1, 7), bias_bh=(2, 4),
+             softcap=2.0, has_lens=True, lens_range=(5, 14))
+    inp = make_inputs(p, 68)
+    q = _bnsh_q(p, inp["q"])
+    kt = torch.cat([_f64(inp["past_k"]), _bnsh_kv(p, inp["k"], p.D)], dim=2)
+    kt = kt.repeat_interleave(p.Hq // p.Hkv, dim=1)
+    raw = (q @ kt.transpose(-1, -2)).numpy() / math.sqrt(p.D)
+    m0 = olk_ref.qk(p, inp, 0)
+    np.testing.assert_allclose(m0, raw, rtol=1e-12, atol=1e-12)       # library matmul
+    m1, m2, m3 = (olk_ref.qk(p, inp, m) for m in (1, 2, 3))
+    allowed = m3 > 0
+    assert np.array_equal(np.isfinite(m1), allowed)                   # excluded: -inf
+    bias = inp["bias"].double().numpy()
+    np.testing.assert_allclose(m1[allowed], (raw + bias)[allowed], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(m2[allowed], 2.0 * np.tanh(m1[allowed] / 2.0), rtol=1e-12)
+    np.testing.assert_allclose(m3.sum(-1), 1.0, rtol=1e-12)
+    for (b, h, i) in ((0, 0, 0), (1, 3, 6), (0, 2, 4)):
+        w, _ = olk_ref.row_weights(p, inp, b, h, i)
+        np.testing.assert_allclose(m3[b, h, i, : len(w)], w, rtol=0, atol=0)

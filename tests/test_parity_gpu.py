@@ -78,6 +78,26 @@ SMALL = {
     "gqa_rope_dim12_f16": Problem(op="gqa", dtype="f16", B=2, S=33, L=33, P=8, Hq=4, Hkv=2,
                                   D=64, Dv=64, causal=1, lens_range=(0, 8), rotary=1,
                                   rotary_dim=12),
+    # mask surface: BOOL masks (broadcast, short), FLOAT masks broadcast over
+    # queries with a short last dimension (tiled path), int64 nonpad lengths,
+    # MultiHeadAttention binary masks
+    "attention_bool_mask_bf16": Problem(op="attention", dtype="bf16", B=2, S=65, L=130, Hq=4,
+                                        Hkv=2, D=64, Dv=64, causal=0, has_lens=False,
+                                        mask_kind="bool", mask_bhs=(2, 1, 1), mask_cols=100),
+    "attention_bool_mask_full_f32": Problem(op="attention", dtype="f32", B=2, S=20, L=37, P=5,
+                                            Hq=4, Hkv=1, D=32, Dv=32, causal=1, has_lens=True,
+                                            lens_range=(10, 42), lens_i64=True,
+                                            mask_kind="bool", mask_bhs=(1, 4, 20), softcap=3.0),
+    "attention_float_mask_short_bf16": Problem(op="attention", dtype="bf16", B=2, S=70, L=200,
+                                               Hq=8, Hkv=2, D=128, Dv=128, causal=0,
+                                               has_lens=False, bias_bh=(1, 1),
+                                               bias_s_bcast=True, bias_cols=170),
+    "mha_binary_mask_bt_f16": Problem(op="mha", dtype="f16", B=3, S=30, L=90, Hq=4, Hkv=4,
+                                      D=64, Dv=64, kv_rank=4, causal=0, has_lens=False,
+                                      mask_kind="int32", mask_bhs=(3, 1, 1), bias_bh=(1, 4)),
+    "mha_binary_mask_bst_f16": Problem(op="mha", dtype="f16", B=2, S=17, L=40, Hq=2, Hkv=2,
+                                       D=64, Dv=64, kv_rank=4, causal=0, has_lens=False,
+                                       mask_kind="int32", mask_bhs=(2, 1, 17)),
 }
 
 
@@ -89,7 +109,9 @@ def _run(p, dev, **kw):
 
 
 def tiled_capable(p):
-    return p.dtype in ("f16", "bf16") and p.D == p.Dv and p.D in (64, 128)
+    # attention masks and the qk output go to the generic kernels
+    return (p.dtype in ("f16", "bf16") and p.D == p.Dv and p.D in (64, 128)
+            and not p.mask_kind and p.qk_mode is None)
 
 
 @pytest.mark.parametrize("name", list(SMALL))
@@ -241,3 +263,24 @@ def test_rotary_decode_inplace_cache_append():
         _say(f"[parity] rotary inplace {mode} kernel={olk.olk_last_kernel_name()}")
         assert_close(p, y_logical(p, c.y), olk_ref.attention(p, inp))
         assert_present_exact(p, inp, c.present_k, c.present_v)
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2, 3])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_qk_matmul_output(mode, dtype):
+    # every stage of the score pipeline, with past, causal, nonpad lengths, a
+    # BOOL mask, a FLOAT mask and softcap; Y must not change with the qk output
+    p = Problem(op="attention", dtype=dtype, B=2, S=24, L=40, P=9, Hq=4, Hkv=2, D=64, Dv=64,
+                causal=1, has_lens=True, lens_range=(20, 49), mask_kind="bool",
+                mask_bhs=(2, 1, 24), bias_bh=(1, 4), softcap=4.0, qk_mode=mode)
+    inp = make_inputs(p, 700 + mode)
+    _say(f"[parity] qk mode={mode} dtype={dtype}")
+    for run in ("fwd", "decode"):
+        c = _run(p, to_dev(inp), mode=run)
+        got = c.qk.detach().cpu().double().numpy()
+        want = olk_ref.qk(p, inp, mode)
+        fin = np.isfinite(want)
+        assert np.array_equal(np.isfinite(got), fin)
+        tol = 1e-4 if mode == 3 else (2e-4 if dtype == "f32" else 2e-3)
+        np.testing.assert_allclose(got[fin], want[fin], rtol=0, atol=tol)
+        assert_close(p, y_logical(p, c.y), olk_ref.attention(p, inp))

@@ -47,8 +47,12 @@ bool overlaps(Range a, Range b) {
 
 // Sizes of every tensor in bytes (int64 arithmetic, checked by the caller).
 struct Sizes {
-  size_t q, k, v, past_k, past_v, bias, sink, proj, y, pres_k, pres_v, rot;
+  size_t q, k, v, past_k, past_v, bias, sink, proj, y, pres_k, pres_v, rot, mask, qk;
 };
+
+// attn_bias / attn_mask extents: rows per (b, h) and columns
+int64_t rows_of(int32_t ext_s, int64_t S) { return ext_s == 1 ? 1 : S; }
+int64_t cols_of(int32_t ext_t, int64_t T) { return ext_t > 0 ? ext_t : T; }
 
 Sizes sizes_of(const olk_attn_desc *d) {
   const size_t es = esize_of(d->dtype);
@@ -62,7 +66,11 @@ Sizes sizes_of(const olk_attn_desc *d) {
   s.past_k = B * Hkv * P * D * es;
   s.past_v = B * Hkv * P * Dv * es;
   s.bias = (size_t)(d->bias_b > 0 ? d->bias_b : 0) * (size_t)(d->bias_h > 0 ? d->bias_h : 0) *
-           S * T * es;
+           (size_t)rows_of(d->bias_s, S) * (size_t)cols_of(d->bias_t, T) * es;
+  s.mask = (size_t)(d->mask_b > 0 ? d->mask_b : 0) * (size_t)(d->mask_h > 0 ? d->mask_h : 0) *
+           (size_t)rows_of(d->mask_s, S) * (size_t)cols_of(d->mask_t, T) *
+           (d->mask_kind == OLK_MASK_BINARY_I32 ? 4 : 1);
+  s.qk = B * Hq * S * T * 4;
   s.sink = Hq * es;
   s.proj = (2 * Hq * D + Hq * Dv) * es;
   s.y = B * S * Hq * Dv * es;
@@ -105,10 +113,32 @@ olk_status validate(const olk_attn_desc *d, const olk_attn_io *io) {
   if (d->q_rank != 3 && d->q_rank != 4) return OLK_E_SHAPE;
   if (d->kv_rank != 3 && d->kv_rank != 4) return OLK_E_SHAPE;
   if ((int64_t)d->past_seq + d->kv_seq > INT32_MAX) return OLK_E_SHAPE;
+  const int64_t T_all = (int64_t)d->past_seq + d->kv_seq;
   if (io->attn_bias) {
     if (d->bias_b != 1 && d->bias_b != d->batch) return OLK_E_SHAPE;
     if (d->bias_h != 1 && d->bias_h != d->q_num_heads) return OLK_E_SHAPE;
+    if (d->bias_s != 0 && d->bias_s != 1 && d->bias_s != d->q_seq) return OLK_E_SHAPE;
+    if (d->bias_t < 0 || d->bias_t > T_all) return OLK_E_SHAPE;
+    // a shorter last dimension (padded with -inf) is an ai.onnx Attention mask
+    if (d->bias_t > 0 && d->bias_t < T_all && d->op != OLK_OP_ATTENTION) return OLK_E_SHAPE;
   }
+  if (d->mask_kind < OLK_MASK_NONE || d->mask_kind > OLK_MASK_BINARY_I32) return OLK_E_ATTR;
+  if (d->mask_kind == OLK_MASK_BOOL && d->op != OLK_OP_ATTENTION) return OLK_E_ATTR;
+  if (d->mask_kind == OLK_MASK_BINARY_I32) {
+    // one key-padding input: lengths or a binary mask
+    if (d->op != OLK_OP_MHA || io->seqlens) return OLK_E_ATTR;
+    if (d->mask_t != 0 && d->mask_t != T_all) return OLK_E_SHAPE;
+  }
+  if (d->mask_kind != OLK_MASK_NONE) {
+    if (d->mask_b != 1 && d->mask_b != d->batch) return OLK_E_SHAPE;
+    if (d->mask_h != 1 && d->mask_h != d->q_num_heads) return OLK_E_SHAPE;
+    if (d->mask_s != 0 && d->mask_s != 1 && d->mask_s != d->q_seq) return OLK_E_SHAPE;
+    if (d->mask_t < 0 || d->mask_t > T_all) return OLK_E_SHAPE;
+  }
+  if (d->seqlens_i64 != 0 && d->seqlens_i64 != 1) return OLK_E_ATTR;
+  if (d->seqlens_i64 && d->op != OLK_OP_ATTENTION) return OLK_E_ATTR;
+  if (io->qk_out && (d->op != OLK_OP_ATTENTION || d->qk_mode < 0 || d->qk_mode > 3))
+    return OLK_E_ATTR;
 
   switch (d->op) {
     case OLK_OP_GQA:
@@ -133,6 +163,7 @@ olk_status validate(const olk_attn_desc *d, const olk_attn_io *io) {
   if (!io->q && sz.q) return OLK_E_NULL;
   if ((!io->k && sz.k) || (!io->v && sz.v)) return OLK_E_NULL;
   if (!io->y && sz.y) return OLK_E_NULL;
+  if (d->mask_kind != OLK_MASK_NONE && !io->attn_mask && sz.mask) return OLK_E_NULL;
   if (d->kv_inplace) {
     if ((!io->present_k && sz.pres_k) || (!io->present_v && sz.pres_v)) return OLK_E_NULL;
     if (io->past_k && io->past_k != io->present_k) return OLK_E_SHAPE;
@@ -151,10 +182,11 @@ olk_status validate(const olk_attn_desc *d, const olk_attn_io *io) {
   if (d->q_num_heads > 65535 || d->batch > 65535) return OLK_E_UNSUPPORTED;
 
   // Outputs must not overlap inputs or each other (kv_inplace: present is the past).
-  const Range outs[3] = {{(const char *)io->y, sz.y},
+  const Range outs[4] = {{(const char *)io->y, sz.y},
                          {(const char *)io->present_k, sz.pres_k},
-                         {(const char *)io->present_v, sz.pres_v}};
-  const Range ins[10] = {{(const char *)io->q, sz.q},
+                         {(const char *)io->present_v, sz.pres_v},
+                         {(const char *)io->qk_out, io->qk_out ? sz.qk : 0}};
+  const Range ins[11] = {{(const char *)io->q, sz.q},
                         {(const char *)io->k, sz.k},
                         {(const char *)io->v, sz.v},
                         {d->kv_inplace ? nullptr : (const char *)io->past_k,
@@ -165,11 +197,12 @@ olk_status validate(const olk_attn_desc *d, const olk_attn_io *io) {
                         {(const char *)io->head_sink, io->head_sink ? sz.sink : 0},
                         {(const char *)io->proj_bias, io->proj_bias ? sz.proj : 0},
                         {(const char *)io->cos_cache, sz.rot},
-                        {(const char *)io->sin_cache, sz.rot}};
-  for (int a = 0; a < 3; ++a) {
-    for (int b = 0; b < 10; ++b)
+                        {(const char *)io->sin_cache, sz.rot},
+                        {(const char *)io->attn_mask, d->mask_kind ? sz.mask : 0}};
+  for (int a = 0; a < 4; ++a) {
+    for (int b = 0; b < 11; ++b)
       if (overlaps(outs[a], ins[b])) return OLK_E_SHAPE;
-    for (int b = a + 1; b < 3; ++b)
+    for (int b = a + 1; b < 4; ++b)
       if (overlaps(outs[a], outs[b])) return OLK_E_SHAPE;
   }
   return OLK_OK;
@@ -218,8 +251,25 @@ olk::Params make_params(const olk_attn_desc *d, const olk_attn_io *io) {
     p.v_sb = Hkv * L * Dv; p.v_sh = L * Dv; p.v_ss = Dv;
   }
   const int64_t T = p.T;
-  p.bias_sh = d->bias_h > 1 ? S * T : 0;
-  p.bias_sb = d->bias_b > 1 ? (int64_t)d->bias_h * S * T : 0;
+  {
+    const int64_t rs = rows_of(d->bias_s, S), cs = cols_of(d->bias_t, T);
+    p.bias_si = rs > 1 ? cs : 0;
+    p.bias_sh = d->bias_h > 1 ? rs * cs : 0;
+    p.bias_sb = d->bias_b > 1 ? (int64_t)d->bias_h * rs * cs : 0;
+    p.bias_cols = (int)cs;
+  }
+  if (d->mask_kind != OLK_MASK_NONE) {
+    const int64_t rs = rows_of(d->mask_s, S), cs = cols_of(d->mask_t, T);
+    p.mask = io->attn_mask;
+    p.mask_kind = d->mask_kind;
+    p.mask_si = rs > 1 ? cs : 0;
+    p.mask_sh = d->mask_h > 1 ? rs * cs : 0;
+    p.mask_sb = d->mask_b > 1 ? (int64_t)d->mask_h * rs * cs : 0;
+    p.mask_cols = (int)cs;
+  }
+  p.seqlens64 = d->seqlens_i64;
+  p.qk_out = io->qk_out;
+  p.qk_mode = d->qk_mode;
   p.op = d->op;
   p.causal = d->causal;
   p.window = d->local_window_size > 0 ? d->local_window_size : -1;
@@ -307,6 +357,7 @@ olk_status olk_attention_fwd(const olk_attn_desc *desc, const olk_attn_io *io, v
     e = olk::launch_generic(p, desc->dtype, s);
     g_last_kernel = desc->do_rotary ? "olk_rope+olk_generic_fwd" : "olk_generic_fwd";
   }
+  if (e == hipSuccess && p.qk_out) e = olk::launch_qk(p, desc->dtype, s);
   return e == hipSuccess ? OLK_OK : OLK_E_HIP;
 }
 
@@ -343,6 +394,7 @@ olk_status olk_attention_decode(const olk_attn_desc *desc, const olk_attn_io *io
   }
   if (e != hipSuccess) return OLK_E_HIP;
   e = olk::launch_combine(p, desc->dtype, n_comb, (const float *)workspace, s);
+  if (e == hipSuccess && p.qk_out) e = olk::launch_qk(p, desc->dtype, s);
   return e == hipSuccess ? OLK_OK : OLK_E_HIP;
 }
 

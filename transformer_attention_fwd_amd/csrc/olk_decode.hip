@@ -340,7 +340,8 @@ hipError_t launch_nr(const Params &p, const DPlan &pl, int nr, dim3 grid, hipStr
 // The decode kernel takes every (query, head) row of one KV head in 16 slots.
 bool decode_supports(const Params &p, int dtype) {
   return (dtype == DT_F16 || dtype == DT_BF16) && p.D == p.Dv && (p.D == 64 || p.D == 128) &&
-         p.G * p.S <= 16 && !p.bias && !(p.softcap > 0.f) && p.scale > 0.f && !p.proj_bias;
+         p.G * p.S <= 16 && !p.bias && !p.mask && !(p.softcap > 0.f) && p.scale > 0.f &&
+         !p.proj_bias && !p.qk_out;
 }
 
 hipError_t launch_decode(const Params &p, int dtype, int split_keys, int n_split, float *ws,

@@ -143,6 +143,7 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Params p, FPlan 
   const int pos_min = s.qoff + i0, pos_max = s.qoff + i_last;
   int hi = p.pad_add ? s.total : s.valid;
   if (p.causal) hi = min(hi, pos_max + 1);
+  if (BIAS) hi = min(hi, p.bias_cols);  // a short mask excludes the keys beyond it
   const int lo = p.window > 0 ? max(0, pos_min - p.window + 1) : 0;
   const int kt0 = lo / BN, kt1 = (hi + BN - 1) / BN;
 
@@ -301,16 +302,16 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Params p, FPlan 
   const float mfv_l2 = p.mfv * kLog2e;
   const float mfv_raw = p.mfv / p.scale;  // the same offset before the scale (scale > 0)
   const T *bias_row = BIAS ? (const T *)p.bias + b * p.bias_sb + row_h * p.bias_sh +
-                                 (int64_t)(row_ok ? row_i : 0) * p.T
+                                 (int64_t)(row_ok ? row_i : 0) * p.bias_si
                            : nullptr;
 
-  // 4 bias values of keys jb..jb+3 as raw 16-bit pairs (zeros past T)
+  // 4 bias values of keys jb..jb+3 as raw 16-bit pairs (zeros past the bias columns)
   auto bias4 = [&](int jb) {
-    if (pl.bias_vec && jb + 3 < p.T) return *(const uint2 *)(bias_row + jb);
+    if (pl.bias_vec && jb + 3 < p.bias_cols) return *(const uint2 *)(bias_row + jb);
     uint16_t e4[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      e4[e] = jb + e < p.T ? __builtin_bit_cast(uint16_t, bias_row[jb + e]) : (uint16_t)0;
+      e4[e] = jb + e < p.bias_cols ? __builtin_bit_cast(uint16_t, bias_row[jb + e]) : (uint16_t)0;
     return make_uint2(e4[0] | ((uint32_t)e4[1] << 16), e4[2] | ((uint32_t)e4[3] << 16));
   };
   // At head size 64 the bias of the next tile is prefetched with its K/V.
@@ -578,7 +579,8 @@ hipError_t launch_flash(const Params &p, int dtype, hipStream_t st) {
   pl.n_qt = (p.S + pl.QW - 1) / pl.QW;
   const int n_bg = p.B * p.Hkv * pl.n_hg;
   pl.xcd_remap = n_bg % 8 == 0 ? 1 : 0;
-  pl.bias_vec = (p.T % 4 == 0 && ((uintptr_t)p.bias & 7) == 0) ? 1 : 0;
+  pl.bias_vec = (p.bias_si % 4 == 0 && p.bias_sh % 4 == 0 && p.bias_sb % 4 == 0 &&
+                 ((uintptr_t)p.bias & 7) == 0) ? 1 : 0;
   pl.fuse_present = flash_fuses_present(p) ? 1 : 0;
   if (dtype == DT_BF16)
     return p.D == 64 ? launch_td<bf16, 64>(p, pl, st) : launch_td<bf16, 128>(p, pl, st);

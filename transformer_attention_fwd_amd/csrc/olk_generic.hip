@@ -64,16 +64,19 @@ __device__ void row_range(const Params &p, const Seq &s, int b, int h, int i, in
       float dot = 0.f;
       for (int c = 0; c < p.D; ++c) dot = fmaf(qs[c], to_f32(kr[c]), dot);
       sc = dot * p.scale;
-      if (p.bias) {
-        const T *br = (const T *)p.bias + b * p.bias_sb + h * p.bias_sh + (int64_t)i * p.T;
+      if (p.bias) {  // j < bias_cols: the caller's range stops there
+        const T *br = (const T *)p.bias + b * p.bias_sb + h * p.bias_sh + (int64_t)i * p.bias_si;
         sc += to_f32(br[j]);
       }
       if (p.softcap > 0.f) sc = p.softcap * tanhf(sc / p.softcap);
       if (p.op == OP_MHA && j >= s.pad) sc += p.mfv;
+      // MultiHeadAttention binary mask: a zero marks key padding (+mfv)
+      if (p.mask_kind == 2 && !mask_at(p, b, h, i, j)) sc += p.mfv;
       // masks (exclusion) after the score pipeline
       bool ok = j < s.valid;
       if (p.causal && j > pos) ok = false;
       if (p.window > 0 && j < pos - p.window + 1) ok = false;
+      if (p.mask_kind == 1 && !mask_at(p, b, h, i, j)) ok = false;  // BOOL false: -inf
       if (!ok) sc = kNegInf;
     }
     const float cmax = wave_max(sc);
@@ -119,6 +122,7 @@ __device__ __forceinline__ void key_range(const Params &p, const Seq &s, int i, 
   const int pos = s.qoff + i;
   hi = s.valid;
   if (p.causal) hi = min(hi, pos + 1);
+  if (p.bias) hi = min(hi, p.bias_cols);  // a short mask excludes the keys beyond it
   lo = 0;
   if (p.window > 0) lo = max(0, pos - p.window + 1);
 }
@@ -229,7 +233,78 @@ __global__ __launch_bounds__(kWave) void combine_kernel(Params p, int n_split, c
   }
 }
 
+// qk_matmul_output of ai.onnx Attention (onnx-light reference kernels header
+// page, "class Attention": qk_matmul_output_mode 0 raw (Q K^T) * scale, 1 with
+// the bias, 2 after softcap, 3 after softmax; Result: rank-4 FLOAT
+// (B, Hq, S, T)).  One wavefront per (b, h, i) row, lanes over keys.  The bias
+// of modes 1-3 is attn_bias plus the masks derived from is_causal, BOOL
+// attn_mask, nonpad_kv_seqlen and short-mask padding: excluded keys read -inf
+// in modes 1 and 2 and 0 in mode 3; mode 0 covers every key.
+template <typename T>
+__global__ __launch_bounds__(kWave) void qk_kernel(Params p) {
+  __shared__ float qs[256];
+  const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x;
+  const Seq s = seq_info(p, b);
+  load_q<T>(p, b, h, i, qs);
+  const int g = h / p.G, pos = s.qoff + i;
+  int lo, hi;
+  key_range(p, s, i, lo, hi);
+  // score of key j at the output stage (modes 0-2; mode 3 uses stage 2)
+  auto score = [&](int j, bool &ok) {
+    const T *kr = kv_row<T>(p, s, b, g, j, false);
+    float dot = 0.f;
+    for (int c = 0; c < p.D; ++c) dot = fmaf(qs[c], to_f32(kr[c]), dot);
+    float sc = dot * p.scale;
+    ok = j >= lo && j < hi;
+    if (p.causal && j > pos) ok = false;
+    if (p.mask_kind == 1 && !mask_at(p, b, h, i, j)) ok = false;
+    if (p.qk_mode == 0) return sc;
+    if (!ok) return kNegInf;
+    if (p.bias)
+      sc += to_f32(((const T *)p.bias)[b * p.bias_sb + h * p.bias_sh + (int64_t)i * p.bias_si + j]);
+    if (p.qk_mode >= 2 && p.softcap > 0.f) sc = p.softcap * tanhf(sc / p.softcap);
+    return sc;
+  };
+  float *out = p.qk_out + (((int64_t)b * p.Hq + h) * p.S + i) * p.T;
+  if (p.qk_mode < 3) {
+    for (int j = lane; j < p.T; j += kWave) {
+      bool ok;
+      out[j] = score(j, ok);
+    }
+    return;
+  }
+  float m = kNegInf;
+  for (int j = lane; j < p.T; j += kWave) {
+    bool ok;
+    const float v = score(j, ok);
+    if (ok) m = fmaxf(m, v);
+  }
+  m = wave_max(m);
+  float l = 0.f;
+  for (int j = lane; j < p.T; j += kWave) {
+    bool ok;
+    const float v = score(j, ok);
+    if (ok) l += expf(v - m);
+  }
+  l = wave_sum(l);
+  for (int j = lane; j < p.T; j += kWave) {
+    bool ok;
+    const float v = score(j, ok);
+    out[j] = (ok && m != kNegInf) ? expf(v - m) / l : 0.f;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_qk(const Params &p, int dtype, hipStream_t st) {
+  if (p.B == 0 || p.S == 0 || p.Hq == 0 || p.T == 0) return hipSuccess;
+  dim3 grid(p.S, p.Hq, p.B);
+  if (dtype == DT_F32) hipLaunchKernelGGL(qk_kernel<float>, grid, dim3(kWave), 0, st, p);
+  else if (dtype == DT_F16) hipLaunchKernelGGL(qk_kernel<f16>, grid, dim3(kWave), 0, st, p);
+  else hipLaunchKernelGGL(qk_kernel<bf16>, grid, dim3(kWave), 0, st, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_generic(const Params &p, int dtype, hipStream_t st) {
   if (p.B == 0 || p.S == 0 || p.Hq == 0) return hipSuccess;

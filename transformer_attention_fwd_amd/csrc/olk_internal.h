@@ -23,7 +23,15 @@ struct Params {
   int64_t k_sb, k_ss, k_sh;   // new K
   int64_t v_sb, v_ss, v_sh;   // new V
   int64_t y_sb, y_ss, y_sh;   // Y
-  int64_t bias_sb, bias_sh;   // bias batch / head strides (0 when broadcast); row stride T
+  int64_t bias_sb, bias_sh, bias_si;  // bias batch / head / query-row strides (0 when broadcast)
+  int bias_cols;              // keys j >= bias_cols are excluded (short mask padding); T otherwise
+  const void *mask;           // attn_mask (mask_kind != 0)
+  int mask_kind;              // 1: uint8 bool (exclusion), 2: int32 binary (+mfv on zero)
+  int64_t mask_sb, mask_sh, mask_si;  // element strides (0 when broadcast)
+  int mask_cols;              // keys j >= mask_cols: false
+  int seqlens64;              // seqlens points at int64 values
+  float *qk_out;              // (B, Hq, S, T) float32 or null
+  int qk_mode;
   int B, S, L, P, T, Hq, Hkv, G, D, Dv;
   int past_rows;   // rows per (b, g) of the past buffer: P, or T when the past lives in present
   int op, causal, window;
@@ -69,8 +77,8 @@ __device__ __forceinline__ Seq seq_info(const Params &p, int b) {
     s.valid = p.T;
     s.pad = p.T;
     if (p.seqlens) {
-      int n = p.seqlens[b];
-      n = n < 0 ? 0 : (n > p.T ? p.T : n);
+      long long n64 = p.seqlens64 ? ((const long long *)p.seqlens)[b] : (long long)p.seqlens[b];
+      int n = (int)(n64 < 0 ? 0 : (n64 > p.T ? p.T : n64));
       if (p.op == OP_ATTENTION) {
         s.valid = n;
       } else if (n > 0) {  // MHA: a fully padded row is a uniform shift = no mask
@@ -81,6 +89,14 @@ __device__ __forceinline__ Seq seq_info(const Params &p, int b) {
   }
   s.src = p.keys_in_past ? s.total : s.past;
   return s;
+}
+
+// attn_mask element of (b, h, i, j): true = attend.  BOOL masks are uint8,
+// binary masks int32; keys beyond the mask's columns read false.
+__device__ __forceinline__ bool mask_at(const Params &p, int b, int h, int i, int j) {
+  if (j >= p.mask_cols) return false;
+  const int64_t e = b * p.mask_sb + h * p.mask_sh + i * p.mask_si + j;
+  return p.mask_kind == 1 ? ((const uint8_t *)p.mask)[e] != 0 : ((const int32_t *)p.mask)[e] != 0;
 }
 
 template <typename T> __device__ __forceinline__ float to_f32(T x) { return (float)x; }
@@ -94,5 +110,6 @@ hipError_t launch_combine(const Params &p, int dtype, int n_split, const float *
                           hipStream_t st);
 hipError_t launch_present(const Params &p, int dtype, hipStream_t st);
 hipError_t launch_rope(const Params &p, int dtype, hipStream_t st);
+hipError_t launch_qk(const Params &p, int dtype, hipStream_t st);
 
 }  // namespace olk

@@ -133,6 +133,7 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_kernel(Params p, Plan pl) {
   const int pos_min = s.qoff + i0, pos_max = s.qoff + i_last;
   int hi = p.pad_add ? s.total : s.valid;
   if (p.causal) hi = min(hi, pos_max + 1);
+  if (BIAS) hi = min(hi, p.bias_cols);  // a short mask excludes the keys beyond it
   int lo = 0;
   if (p.window > 0) lo = max(0, pos_min - p.window + 1);
   int kt0 = lo / kBN, kt1 = (hi + kBN - 1) / kBN;
@@ -226,7 +227,7 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_kernel(Params p, Plan pl) {
   const float cap_log2 = p.softcap * kLog2e;
   const float mfv_log2 = p.mfv * kLog2e;
   const T *bias_row = nullptr;
-  if (BIAS) bias_row = (const T *)p.bias + b * p.bias_sb + h * p.bias_sh + (int64_t)(row_ok ? i : 0) * p.T;
+  if (BIAS) bias_row = (const T *)p.bias + b * p.bias_sb + h * p.bias_sh + (int64_t)(row_ok ? i : 0) * p.bias_si;
 
   if (kt0 < kt1) {
     load_tile(kt0);
@@ -277,14 +278,14 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_kernel(Params p, Plan pl) {
           const int jb = j0 + kb * 32 + 8 * q4 + 4 * half;  // 4 consecutive keys
           float bv[4] = {0.f, 0.f, 0.f, 0.f};
           if (BIAS) {
-            if (pl.bias_vec && jb + 3 < p.T) {
+            if (pl.bias_vec && jb + 3 < p.bias_cols) {
               const uint2 raw = *(const uint2 *)(bias_row + jb);
               bv[0] = lo_f<T>(raw.x); bv[1] = hi_f<T>(raw.x);
               bv[2] = lo_f<T>(raw.y); bv[3] = hi_f<T>(raw.y);
             } else {
 #pragma unroll
               for (int e = 0; e < 4; ++e)
-                bv[e] = jb + e < p.T ? (float)bias_row[jb + e] : 0.f;
+                bv[e] = jb + e < p.bias_cols ? (float)bias_row[jb + e] : 0.f;
             }
           }
 #pragma unroll
@@ -437,7 +438,8 @@ Plan make_plan(const Params &p, int partial, int n_split, int split_tiles, float
   pl.split_tiles = split_tiles;
   const int n_bg = p.B * p.Hkv * pl.n_hg;
   pl.xcd_remap = (n_bg % 8 == 0) ? 1 : 0;
-  pl.bias_vec = (p.T % 4 == 0 && ((uintptr_t)p.bias & 7) == 0) ? 1 : 0;
+  pl.bias_vec = (p.bias_si % 4 == 0 && p.bias_sh % 4 == 0 && p.bias_sb % 4 == 0 &&
+                 ((uintptr_t)p.bias & 7) == 0) ? 1 : 0;
   pl.ws = ws;
   return pl;
 }
@@ -469,6 +471,8 @@ hipError_t launch_plan(const Params &p, int dtype, const Plan &pl, hipStream_t s
 bool tiled_supports(const Params &p, int dtype) {
   if (dtype != DT_F16 && dtype != DT_BF16) return false;
   if (p.D != p.Dv || (p.D != 64 && p.D != 128)) return false;
+  // attention masks and the qk output are served by the generic kernels
+  if (p.mask || p.qk_out) return false;
   if (!aligned16(p.q) || !aligned16(p.k) || !aligned16(p.v) || !aligned16(p.y)) return false;
   if (p.P > 0 && (!aligned16(p.past_k) || !aligned16(p.past_v))) return false;
   if (p.proj_bias && !aligned16(p.proj_bias)) return false;

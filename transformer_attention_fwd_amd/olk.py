@@ -45,13 +45,16 @@ class olk_attn_desc(ctypes.Structure):
         ("bias_b", ctypes.c_int32), ("bias_h", ctypes.c_int32),
         ("kv_inplace", ctypes.c_int32), ("kernel", ctypes.c_int32)] + [
         (n, ctypes.c_int32) for n in ("do_rotary", "rotary_interleaved", "rotary_dim",
-                                      "rotary_max_pos")]
+                                      "rotary_max_pos", "bias_s", "bias_t", "mask_kind",
+                                      "mask_b", "mask_h", "mask_s", "mask_t", "seqlens_i64",
+                                      "qk_mode")]
 
 
 class olk_attn_io(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "q", "k", "v", "past_k", "past_v", "seqlens", "attn_bias", "head_sink",
-        "proj_bias", "y", "present_k", "present_v", "cos_cache", "sin_cache")]
+        "proj_bias", "y", "present_k", "present_v", "cos_cache", "sin_cache", "attn_mask",
+        "qk_out")]
 
 
 _P = ctypes.POINTER
@@ -124,7 +127,12 @@ def make_desc(p: Problem, kernel: str = "auto", kv_inplace: bool = False) -> olk
         mask_filter_value=p.mask_filter_value, bias_b=bb, bias_h=bh,
         kv_inplace=1 if kv_inplace else 0, kernel=KERNELS[kernel],
         do_rotary=p.rotary, rotary_interleaved=p.rotary_interleaved,
-        rotary_dim=p.rotary_dim, rotary_max_pos=p.max_pos if p.rotary else 0)
+        rotary_dim=p.rotary_dim, rotary_max_pos=p.max_pos if p.rotary else 0,
+        bias_s=1 if p.bias_s_bcast else 0, bias_t=p.bias_cols,
+        mask_kind={"": 0, "bool": 1, "int32": 2}[p.mask_kind],
+        mask_b=p.mask_bhs[0] if p.mask_bhs else 0, mask_h=p.mask_bhs[1] if p.mask_bhs else 0,
+        mask_s=(1 if p.mask_bhs[2] == 1 else 0) if p.mask_bhs else 0, mask_t=p.mask_cols,
+        seqlens_i64=1 if p.lens_i64 else 0, qk_mode=p.qk_mode if p.qk_mode is not None else 0)
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -137,14 +145,16 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
 
 def make_io(tensors: Dict[str, torch.Tensor], y: torch.Tensor,
             present_k: Optional[torch.Tensor] = None,
-            present_v: Optional[torch.Tensor] = None) -> olk_attn_io:
+            present_v: Optional[torch.Tensor] = None,
+            qk_out: Optional[torch.Tensor] = None) -> olk_attn_io:
     g = tensors.get
     return olk_attn_io(q=_ptr(g("q")), k=_ptr(g("k")), v=_ptr(g("v")),
                        past_k=_ptr(g("past_k")), past_v=_ptr(g("past_v")),
                        seqlens=_ptr(g("lens")), attn_bias=_ptr(g("bias")),
                        head_sink=_ptr(g("sink")), proj_bias=_ptr(g("proj_bias")),
                        y=_ptr(y), present_k=_ptr(present_k), present_v=_ptr(present_v),
-                       cos_cache=_ptr(g("cos_cache")), sin_cache=_ptr(g("sin_cache")))
+                       cos_cache=_ptr(g("cos_cache")), sin_cache=_ptr(g("sin_cache")),
+                       attn_mask=_ptr(g("mask")), qk_out=_ptr(qk_out))
 
 
 def current_stream() -> int:
@@ -179,8 +189,10 @@ class Call:
         if kv_inplace:
             self.dev.pop("past_k", None)
             self.dev.pop("past_v", None)
+        self.qk = (torch.empty((p.B, p.Hq, p.S, p.T), dtype=torch.float32, device=device)
+                   if p.qk_mode is not None else None)
         self.desc = make_desc(p, kernel=kernel, kv_inplace=kv_inplace)
-        self.io = make_io(self.dev, self.y, self.present_k, self.present_v)
+        self.io = make_io(self.dev, self.y, self.present_k, self.present_v, self.qk)
         self.ws_bytes = olk_workspace_bytes(self.desc) if mode == "decode" else 0
         self.ws = (torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
                    if self.ws_bytes else None)

@@ -17,6 +17,8 @@ Tensor layouts (all row-major, element type = ``dtype`` unless stated):
 * ``proj_bias`` (2*Hq*D + Hq*Dv,) MultiHeadAttention projection bias [q | k | v]
 * ``cos_cache``/``sin_cache`` (max_pos, R/2) rotary tables (GroupQueryAttention
   with ``rotary``); deterministic, not drawn
+* ``mask`` (mask_b, mask_h, mask_s, cols) bool or int32 attention mask, drawn
+  after ``proj_bias`` as uniform [0, 1) < mask_p
 
 Draw order inside one problem is fixed: q, k, v, past_k, past_v, lens, bias,
 sink, proj_bias (absent tensors are skipped).  Normals are drawn as float32 from
@@ -75,6 +77,19 @@ class Problem:
     rotary_dim: int = 0
     rotary_max_pos: int = 0
     rotary_base: float = 10000.0
+    # attn_bias extents beyond (bias_b, bias_h): one row for every query
+    # (bias_s_bcast) and a short last dimension (bias_cols < P+L, ai.onnx Attention)
+    bias_s_bcast: bool = False
+    bias_cols: int = 0
+    # attn_mask: "" none, "bool" (ai.onnx Attention, uint8, true = attend) or
+    # "int32" (MultiHeadAttention binary key-padding mask, nonzero = attend);
+    # extents (mask_b, mask_h, mask_s) with mask_s 1 or S, mask_cols 0 = P+L
+    mask_kind: str = ""
+    mask_bhs: Optional[Tuple[int, int, int]] = None
+    mask_cols: int = 0
+    mask_p: float = 0.8          # probability that a mask element attends
+    lens_i64: bool = False       # ai.onnx Attention nonpad_kv_seqlen as int64
+    qk_mode: Optional[int] = None  # ai.onnx Attention qk_matmul_output_mode
 
     @property
     def T(self) -> int:
@@ -215,14 +230,26 @@ def make_inputs(p: Problem, seed: int, lens: Optional[np.ndarray] = None
         out["lens"] = torch.from_numpy(np.ascontiguousarray(l32))
     if p.bias_bh is not None:
         bb, bh = p.bias_bh
-        out["bias"] = _normal(rng, (bb, bh, p.S, p.T), p.sigma_bias, dt, 1)
+        rows = 1 if p.bias_s_bcast else p.S
+        cols = p.bias_cols if p.bias_cols > 0 else p.T
+        out["bias"] = _normal(rng, (bb, bh, rows, cols), p.sigma_bias, dt, 1)
     if p.has_sink:
         out["sink"] = _normal(rng, (p.Hq,), p.sigma_sink, dt, 1)
     if p.has_proj_bias:
         out["proj_bias"] = _normal(rng, (2 * p.Hq * p.D + p.Hq * p.Dv,),
                                    p.sigma_proj, dt, 1)
+    if p.mask_kind:
+        mb, mh, ms = p.mask_bhs
+        cols = p.mask_cols if p.mask_cols > 0 else p.T
+        bits = rng.random(size=(mb, mh, ms, cols)) < p.mask_p
+        out["mask"] = torch.from_numpy(bits.astype(np.uint8 if p.mask_kind == "bool"
+                                                    else np.int32))
+        if p.mask_kind == "bool":
+            out["mask"] = out["mask"].to(torch.bool)
     if p.rotary:
         out["cos_cache"], out["sin_cache"] = rotary_tables(p)
+    if p.lens_i64 and "lens" in out:
+        out["lens"] = out["lens"].to(torch.int64)
     return out
 
 
