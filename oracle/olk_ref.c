@@ -40,6 +40,9 @@
  *       they stay in the softmax.
  *   R10 a row with no allowed key outputs 0.
  *   R11 MHA projection bias layout is [q (N*H) | k (N*H) | v (N*Hv)].
+ *   R21 with rank-3 K/V (self-attention) the k and v segments are added to
+ *       the new K/V rows; the biased rows are element-type tensors (float32
+ *       add, rounded once) and present holds them.
  *   R18 rotary embedding (GroupQueryAttention do_rotary): Q and the new K rows
  *       are rotated at their absolute positions (past_b + i), the past is used
  *       as stored, V is not rotated, and present_key holds the rotated keys.
@@ -257,6 +260,27 @@ static int seq_info(const ref_desc *d, const ref_inputs *in, int b, seqinfo *s) 
   return 0;
 }
 
+/* R21: new K/V element with its projection-bias segment, as the element type */
+static int kv_biased(const ref_desc *d, const ref_inputs *in) {
+  return d->op == REF_MHA && d->kv_rank == 3 && in->proj_bias != NULL;
+}
+
+static uint32_t biased_bits(const ref_desc *d, const ref_inputs *in, const void *cur, size_t idx,
+                            int g, int c, int value) {
+  const size_t seg = value ? (size_t)2 * d->q_heads * d->head_size + (size_t)g * d->v_head_size
+                           : (size_t)d->q_heads * d->head_size + (size_t)g * d->head_size;
+  const float x = (float)elem(cur, d->dtype, idx);
+  const float bb = (float)elem(in->proj_bias, d->dtype, seg + c);
+  const float r = x + bb;
+  if (d->dtype == REF_F32) { uint32_t u; memcpy(&u, &r, 4); return u; }
+  return d->dtype == REF_F16 ? float_to_half(r) : float_to_bf16(r);
+}
+
+static double bits_to_double(int dtype, uint32_t bits) {
+  if (dtype == REF_F32) { float f; memcpy(&f, &bits, 4); return (double)f; }
+  return dtype == REF_F16 ? half_to_double((uint16_t)bits) : bf16_to_double((uint16_t)bits);
+}
+
 static double key_elem(const ref_desc *d, const ref_inputs *in, const seqinfo *s,
                        int b, int g, long j, int c, int value) {
   int width = value ? d->v_head_size : d->head_size;
@@ -265,6 +289,7 @@ static double key_elem(const ref_desc *d, const ref_inputs *in, const seqinfo *s
   if (j < s->past_b) return elem(past, d->dtype, past_index(d, b, g, (int)j, c, width));
   const size_t base = new_kv_index(d, b, g, (int)(j - s->past_b), 0, width);
   if (d->do_rotary && !value) return rot_elem(d, in, cur, base, c, j); /* R18: new key at position j */
+  if (kv_biased(d, in)) return bits_to_double(d->dtype, biased_bits(d, in, cur, base + c, g, c, value));
   return elem(cur, d->dtype, base + c);
 }
 
@@ -480,6 +505,15 @@ int olk_ref_present(const ref_desc *d, const ref_inputs *in, void *pk, void *pv)
         for (long j = 0; j < s.total_b && j < Tp; ++j) {
           const char *src;
           char *o = (char *)dst + ((((size_t)b * d->kv_heads + g) * Tp + j) * width) * es;
+          if (j >= s.past_b && kv_biased(d, in)) { /* R21: biased new K/V */
+            const size_t base = new_kv_index(d, b, g, (int)(j - s.past_b), 0, width);
+            for (int c = 0; c < width; ++c) {
+              const uint32_t bits = biased_bits(d, in, cur, base + c, g, c, which);
+              if (es == 4) memcpy(o + 4 * (size_t)c, &bits, 4);
+              else { const uint16_t h16 = (uint16_t)bits; memcpy(o + 2 * (size_t)c, &h16, 2); }
+            }
+            continue;
+          }
           if (j >= s.past_b && d->do_rotary && !which) { /* R18: rotated new key */
             const size_t base = new_kv_index(d, b, g, (int)(j - s.past_b), 0, width);
             for (int c = 0; c < width; ++c) {

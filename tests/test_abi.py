@@ -123,7 +123,9 @@ def test_operator_specific_rejections():
     assert status(GQA, seqlens=None) == olk.OLK_E_NULL               # seqlens_k required
     assert status(MHA.with_(has_sink=True)) == olk.OLK_E_ATTR        # sink is GQA-only
     assert status(MHA.with_(softcap=5.0)) == olk.OLK_E_ATTR
-    assert status(MHA.with_(kv_rank=3)) == olk.OLK_E_UNSUPPORTED     # rank-3 K/V bias segments
+    assert status(MHA.with_(kv_rank=3)) == olk.OLK_OK                # rank-3 K/V bias segments
+    # their biased rows are written to present: present is required then
+    assert status(MHA.with_(kv_rank=3), present_k=None, present_v=None) == olk.OLK_E_UNSUPPORTED
     att = Problem(op="attention", dtype="bf16", B=2, S=8, L=8, Hq=4, Hkv=2, D=64, Dv=64)
     assert status(att) == olk.OLK_OK
     assert status(att.with_(has_proj_bias=True)) == olk.OLK_E_ATTR

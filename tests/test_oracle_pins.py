@@ -689,3 +689,37 @@ def test_qk_output_modes():
     for (b, h, i) in ((0, 0, 0), (1, 3, 6), (0, 2, 4)):
         w, _ = olk_ref.row_weights(p, inp, b, h, i)
         np.testing.assert_allclose(m3[b, h, i, : len(w)], w, rtol=0, atol=0)
+
+
+def test_mha_rank3_projection_bias_is_added_to_new_kv_rows():
+    # R21: rank-3 self-attention adds the k / v segments to the new rows (element
+    # type, one rounding); the same call with pre-added K/V and zero k / v
+    # segments gives identical Y and present
+    p = Problem(op="mha", dtype="bf16", B=2, S=6, L=6, P=4, Hq=3, Hkv=3, D=8, Dv=8,
+                kv_rank=3, causal=1, has_lens=False, has_proj_bias=True, sigma_proj=0.5)
+    inp = make_inputs(p, 71)
+    pb = inp["proj_bias"]
+    qn, kn = p.Hq * p.D, p.Hq * p.D
+    bk, bv = pb[qn: qn + kn], pb[qn + kn:]
+    pre = dict(inp)
+    pre["k"] = (inp["k"].float() + bk.float()).to(torch.bfloat16)
+    pre["v"] = (inp["v"].float() + bv.float()).to(torch.bfloat16)
+    zb = pb.clone()
+    zb[qn:] = 0
+    pre["proj_bias"] = zb
+    assert np.array_equal(olk_ref.attention(p, inp), olk_ref.attention(p, pre))
+    for a, b in zip(olk_ref.present(p, inp, fill=0.0), olk_ref.present(p, pre, fill=0.0)):
+        assert torch.equal(a, b)
+
+
+def test_mha_rank3_projection_bias_matches_sdpa():
+    p = Problem(op="mha", dtype="f32", B=2, S=5, L=5, Hq=2, Hkv=2, D=8, Dv=8, kv_rank=3,
+                causal=0, has_lens=False, has_proj_bias=True, sigma_proj=0.3)
+    inp = make_inputs(p, 72)
+    pb = _f64(inp["proj_bias"])
+    n = p.Hq * p.D
+    q = _bnsh_q(p, inp["q"]) + pb[:n].view(1, p.Hq, 1, p.D)
+    k = _bnsh_kv(p, inp["k"], p.D) + pb[n: 2 * n].view(1, p.Hq, 1, p.D)
+    v = _bnsh_kv(p, inp["v"], p.Dv) + pb[2 * n:].view(1, p.Hq, 1, p.Dv)
+    want = torch.nn.functional.scaled_dot_product_attention(q, k, v).permute(0, 2, 1, 3)
+    np.testing.assert_allclose(olk_ref.attention(p, inp), want.numpy(), rtol=0, atol=1e-6)

@@ -98,6 +98,15 @@ SMALL = {
     "mha_binary_mask_bst_f16": Problem(op="mha", dtype="f16", B=2, S=17, L=40, Hq=2, Hkv=2,
                                        D=64, Dv=64, kv_rank=4, causal=0, has_lens=False,
                                        mask_kind="int32", mask_bhs=(2, 1, 17)),
+    # MultiHeadAttention rank-3 self-attention with k / v projection-bias
+    # segments, unidirectional with a past
+    "mha_self_projbias_past_f16": Problem(op="mha", dtype="f16", B=2, S=40, L=40, P=30, Hq=4,
+                                          Hkv=4, D=64, Dv=64, kv_rank=3, causal=1,
+                                          has_lens=True, lens_range=(20, 70),
+                                          has_proj_bias=True, sigma_proj=0.3),
+    "mha_self_projbias_bf16": Problem(op="mha", dtype="bf16", B=2, S=100, L=100, Hq=4, Hkv=4,
+                                      D=128, Dv=128, kv_rank=3, causal=0, has_lens=False,
+                                      has_proj_bias=True, sigma_proj=0.3, bias_bh=(2, 1)),
 }
 
 

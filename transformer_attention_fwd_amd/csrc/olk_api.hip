@@ -151,8 +151,11 @@ olk_status validate(const olk_attn_desc *d, const olk_attn_io *io) {
       if (d->q_rank != 3) return OLK_E_SHAPE;
       if (d->kv_num_heads != d->q_num_heads) return OLK_E_SHAPE;
       if (io->head_sink || d->kv_inplace) return OLK_E_ATTR;
-      // rank-3 K/V with their projection-bias segments: not implemented
-      if (io->proj_bias && d->kv_rank == 3) return OLK_E_UNSUPPORTED;
+      // rank-3 K/V with their projection-bias segments: the biased rows are
+      // written to present and read back, so present is required
+      if (io->proj_bias && d->kv_rank == 3 && d->batch > 0 && d->kv_seq > 0 &&
+          (!io->present_k || !io->present_v))
+        return OLK_E_UNSUPPORTED;
       break;
     default:  // ai.onnx::Attention
       if (io->head_sink || io->proj_bias || d->kv_inplace) return OLK_E_ATTR;
@@ -286,6 +289,28 @@ olk::Params make_params(const olk_attn_desc *d, const olk_attn_io *io) {
   return p;
 }
 
+// MultiHeadAttention rank-3 K/V with a projection bias: the past rows and the
+// biased new rows go to present, and the attention reads every key from there
+// (Q keeps its bias segment in the kernels).
+bool kv_bias_path(const olk_attn_desc *d, const olk_attn_io *io) {
+  return d->op == OLK_OP_MHA && d->kv_rank == 3 && io->proj_bias != nullptr;
+}
+
+hipError_t kv_bias_prepass(olk::Params &p, int dtype, hipStream_t st) {
+  olk::Params pp = p;
+  pp.present_past_only = 1;
+  hipError_t e = olk::launch_present(pp, dtype, st);
+  if (e != hipSuccess) return e;
+  e = olk::launch_kv_bias(p, dtype, st);
+  if (e != hipSuccess) return e;
+  p.past_k = p.present_k;
+  p.past_v = p.present_v;
+  p.past_rows = p.T;
+  p.keys_in_past = 1;
+  p.present_k = p.present_v = nullptr;
+  return hipSuccess;
+}
+
 // do_rotary: copy the past rows into present (out of place), run the rotary
 // pre-pass (rotated Q into Y, rotated new K and new V into present), and
 // return the parameters of the attention proper: Q read from Y, every key read
@@ -345,6 +370,8 @@ olk_status olk_attention_fwd(const olk_attn_desc *desc, const olk_attn_io *io, v
   hipError_t e = hipSuccess;
   if (desc->do_rotary) {
     e = rotary_prepass(p, desc->dtype, s);
+  } else if (kv_bias_path(desc, io)) {
+    e = kv_bias_prepass(p, desc->dtype, s);
   } else {
     if (use_tiled && olk::flash_fuses_present(p)) p.present_past_only = 1;
     e = olk::launch_present(p, desc->dtype, s);
@@ -376,8 +403,9 @@ olk_status olk_attention_decode(const olk_attn_desc *desc, const olk_attn_io *io
   if (desc->do_rotary) { pa.q = pa.y; pa.q_sb = pa.y_sb; pa.q_ss = pa.y_ss; pa.q_sh = pa.y_sh; }
   const bool tiled_ok = olk::tiled_supports(pa, desc->dtype);
   if (desc->kernel == OLK_KERNEL_TILED && !tiled_ok) return OLK_E_UNSUPPORTED;
-  hipError_t e = desc->do_rotary ? rotary_prepass(p, desc->dtype, s)
-                                 : olk::launch_present(p, desc->dtype, s);
+  hipError_t e = desc->do_rotary        ? rotary_prepass(p, desc->dtype, s)
+                 : kv_bias_path(desc, io) ? kv_bias_prepass(p, desc->dtype, s)
+                                          : olk::launch_present(p, desc->dtype, s);
   if (e != hipSuccess) return OLK_E_HIP;
   const int n_split = n_splits(desc);
   int n_comb = n_split;

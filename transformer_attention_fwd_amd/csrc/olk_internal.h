@@ -111,5 +111,6 @@ hipError_t launch_combine(const Params &p, int dtype, int n_split, const float *
 hipError_t launch_present(const Params &p, int dtype, hipStream_t st);
 hipError_t launch_rope(const Params &p, int dtype, hipStream_t st);
 hipError_t launch_qk(const Params &p, int dtype, hipStream_t st);
+hipError_t launch_kv_bias(const Params &p, int dtype, hipStream_t st);
 
 }  // namespace olk

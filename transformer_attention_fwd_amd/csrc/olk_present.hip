@@ -51,7 +51,38 @@ __global__ __launch_bounds__(kThreads) void present_kernel(Params p, int esize, 
   }
 }
 
+// MultiHeadAttention with rank-3 K/V and a projection bias: new row i of
+// (b = blockIdx.z, g = blockIdx.y) gets its k / v bias segment added (float32
+// add, rounded once to the element type) and lands in present at P + i; the
+// attention kernels then read every key from present.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void kv_bias_kernel(Params p) {
+  const int i = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int j = p.P + i;
+  const T *bias = (const T *)p.proj_bias;
+  for (int t = threadIdx.x; t < p.D + p.Dv; t += kThreads) {
+    const bool value = t >= p.D;
+    const int c = value ? t - p.D : t;
+    const int width = value ? p.Dv : p.D;
+    const T *src = (const T *)(value ? p.v : p.k) + b * (value ? p.v_sb : p.k_sb) +
+                   (int64_t)i * (value ? p.v_ss : p.k_ss) + (int64_t)g * (value ? p.v_sh : p.k_sh);
+    const int64_t seg = value ? (int64_t)2 * p.Hq * p.D + (int64_t)g * p.Dv
+                              : (int64_t)p.Hq * p.D + (int64_t)g * p.D;
+    T *dst = (T *)(value ? p.present_v : p.present_k) + (((int64_t)b * p.Hkv + g) * p.T + j) * width;
+    dst[c] = (T)((float)src[c] + (float)bias[seg + c]);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_kv_bias(const Params &p, int dtype, hipStream_t st) {
+  if (p.B == 0 || p.L == 0 || p.Hkv == 0) return hipSuccess;
+  const dim3 grid(p.L, p.Hkv, p.B);
+  if (dtype == DT_BF16) hipLaunchKernelGGL(kv_bias_kernel<bf16>, grid, dim3(kThreads), 0, st, p);
+  else if (dtype == DT_F16) hipLaunchKernelGGL(kv_bias_kernel<f16>, grid, dim3(kThreads), 0, st, p);
+  else hipLaunchKernelGGL(kv_bias_kernel<float>, grid, dim3(kThreads), 0, st, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_present(const Params &p, int dtype, hipStream_t st) {
   if ((!p.present_k && !p.present_v) || p.B == 0 || p.T == 0) return hipSuccess;
