@@ -72,6 +72,19 @@ def allowed_pairs(p, inputs) -> np.ndarray:
         lo = np.zeros(p.S, dtype=np.int64)
         if p.window > 0:
             lo = np.maximum(0, pos - p.window + 1)
+        if p.bias_bh is not None and p.bias_cols > 0:
+            hi = np.minimum(hi, p.bias_cols)
+        if p.mask_kind == "bool":
+            # attended keys of each row under a head-broadcast BOOL mask
+            m = inputs["mask"].numpy().astype(bool)
+            assert m.shape[1] == 1, "head-broadcast masks only"
+            mb = m[b if m.shape[0] > 1 else 0, 0]
+            cols = mb.shape[-1]
+            for i in range(p.S):
+                row = mb[i if mb.shape[0] > 1 else 0]
+                h_i = min(int(hi[i]), cols)
+                out[b, i] = int(row[int(lo[i]):h_i].sum()) if h_i > lo[i] else 0
+            continue
         out[b] = np.maximum(0, hi - lo)
     return out
 

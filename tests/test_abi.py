@@ -79,6 +79,8 @@ def fake_io(p: Problem, **over):
         ptr["seqlens"] = None
     if not p.rotary:
         ptr["cos_cache"] = ptr["sin_cache"] = None
+    if p.mask_kind:
+        ptr["attn_mask"] = _BASE + 50 * (1 << 36)
     ptr.update(over)
     return olk.olk_attn_io(**ptr)
 

@@ -117,10 +117,14 @@ def _run(p, dev, **kw):
     return c
 
 
-def tiled_capable(p):
-    # attention masks and the qk output go to the generic kernels
-    return (p.dtype in ("f16", "bf16") and p.D == p.Dv and p.D in (64, 128)
-            and not p.mask_kind and p.qk_mode is None)
+def tiled_capable(p, mode="fwd"):
+    # BOOL masks run in the prefill kernel (not in the split-KV partials);
+    # binary masks and the qk output go to the generic kernels
+    if p.mask_kind == "int32" or p.qk_mode is not None:
+        return False
+    if p.mask_kind == "bool" and mode == "decode":
+        return False
+    return p.dtype in ("f16", "bf16") and p.D == p.Dv and p.D in (64, 128)
 
 
 @pytest.mark.parametrize("name", list(SMALL))
@@ -129,13 +133,14 @@ def tiled_capable(p):
                                          ("fwd", "auto")])
 def test_small_parity(name, mode, kernel):
     p = SMALL[name]
-    if kernel == "tiled" and not tiled_capable(p):
-        pytest.skip("the tiled kernel covers f16/bf16 with head size 64 or 128")
+    if kernel == "tiled" and not tiled_capable(p, mode):
+        pytest.skip("the tiled kernels cover f16/bf16 with head size 64 or 128 (no "
+                    "binary masks or qk output; BOOL masks in prefill only)")
     inp = make_inputs(p, 500 + list(SMALL).index(name))
     _say(f"[parity] {name} mode={mode} kernel={kernel}")
     c = _run(p, to_dev(inp), mode=mode, kernel=kernel)
     name_ran = olk.olk_last_kernel_name()
-    if kernel != "generic" and tiled_capable(p):
+    if kernel != "generic" and tiled_capable(p, mode):
         assert "generic" not in name_ran, name_ran
     want = olk_ref.attention(p, inp)
     assert_close(p, y_logical(p, c.y), want)
@@ -150,7 +155,7 @@ def test_workload_parity(name):
     dev = to_dev(inp)
     c = _run(p, dev, mode=mode)
     _say(f"[parity] {name} kernel={olk.olk_last_kernel_name()}")
-    if tiled_capable(p):
+    if tiled_capable(p, mode):
         assert "generic" not in olk.olk_last_kernel_name()
     if p.B * p.S * p.Hq <= 4096:
         assert_close(p, y_logical(p, c.y), olk_ref.attention(p, inp))

@@ -401,7 +401,8 @@ olk_status olk_attention_decode(const olk_attn_desc *desc, const olk_attn_io *io
   hipStream_t s = (hipStream_t)stream;
   olk::Params pa = p;
   if (desc->do_rotary) { pa.q = pa.y; pa.q_sb = pa.y_sb; pa.q_ss = pa.y_ss; pa.q_sh = pa.y_sh; }
-  const bool tiled_ok = olk::tiled_supports(pa, desc->dtype);
+  // the split-KV partial kernels take no attn_mask: masks go to the generic split
+  const bool tiled_ok = olk::tiled_supports(pa, desc->dtype) && !pa.mask;
   if (desc->kernel == OLK_KERNEL_TILED && !tiled_ok) return OLK_E_UNSUPPORTED;
   hipError_t e = desc->do_rotary        ? rotary_prepass(p, desc->dtype, s)
                  : kv_bias_path(desc, io) ? kv_bias_prepass(p, desc->dtype, s)

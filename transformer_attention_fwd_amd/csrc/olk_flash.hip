@@ -100,12 +100,16 @@ struct FPlan {
   int GH, n_hg, QW, n_qt;
   int xcd_remap;
   int bias_vec;
+  int mask_vec;      // BOOL mask rows are 4-byte aligned
   int fuse_present;
 };
 
-template <typename T, int D, bool BIAS, bool SOFTCAP>
+// BM: 0 no bias, 1 attn_bias, 2 BOOL attn_mask (with or without attn_bias)
+template <typename T, int D, int BM, bool SOFTCAP>
 __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Params p, FPlan pl) {
   typedef typename FV<T>::v8 vec8;
+  constexpr bool BIAS = BM != 0;   // the score epilogue reads a bias row
+  constexpr bool MASK = BM == 2;
   constexpr int CH = D / 8;             // 16-byte chunks per K/V row
   constexpr int BN = 64;                // keys per tile
   constexpr int KB = BN / 32;           // 32-key blocks per tile
@@ -143,7 +147,10 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Params p, FPlan 
   const int pos_min = s.qoff + i0, pos_max = s.qoff + i_last;
   int hi = p.pad_add ? s.total : s.valid;
   if (p.causal) hi = min(hi, pos_max + 1);
-  if (BIAS) hi = min(hi, p.bias_cols);  // a short mask excludes the keys beyond it
+  // short masks exclude the keys beyond their columns (BIAS instantiations
+  // also serve BOOL attn_mask, with or without a bias)
+  if (BM == 1 || (MASK && p.bias)) hi = min(hi, p.bias_cols);
+  if (MASK) hi = min(hi, p.mask_cols);
   const int lo = p.window > 0 ? max(0, pos_min - p.window + 1) : 0;
   const int kt0 = lo / BN, kt1 = (hi + BN - 1) / BN;
 
@@ -307,12 +314,26 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Params p, FPlan 
 
   // 4 bias values of keys jb..jb+3 as raw 16-bit pairs (zeros past the bias columns)
   auto bias4 = [&](int jb) {
+    if (MASK && !p.bias) return make_uint2(0, 0);
     if (pl.bias_vec && jb + 3 < p.bias_cols) return *(const uint2 *)(bias_row + jb);
     uint16_t e4[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       e4[e] = jb + e < p.bias_cols ? __builtin_bit_cast(uint16_t, bias_row[jb + e]) : (uint16_t)0;
     return make_uint2(e4[0] | ((uint32_t)e4[1] << 16), e4[2] | ((uint32_t)e4[3] << 16));
+  };
+  // BOOL attn_mask: bytes of keys jb..jb+3 of this row slot (0 past the mask's columns)
+  const uint8_t *mask_row = MASK ? (const uint8_t *)p.mask + b * p.mask_sb +
+                                                 row_h * p.mask_sh +
+                                                 (int64_t)(row_ok ? row_i : 0) * p.mask_si
+                                           : nullptr;
+  auto mask4 = [&](int jb) {
+    if (pl.mask_vec && jb + 3 < p.mask_cols) return *(const uint32_t *)(mask_row + jb);
+    uint32_t w = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (jb + e < p.mask_cols) w |= (uint32_t)mask_row[jb + e] << (8 * e);
+    return w;
   };
   // At head size 64 the bias of the next tile is prefetched with its K/V.
   constexpr bool BPRE = BIAS && D == 64;
@@ -380,12 +401,15 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Params p, FPlan 
             bv[0] = lo16<T>(raw.x); bv[1] = hi16<T>(raw.x);
             bv[2] = lo16<T>(raw.y); bv[3] = hi16<T>(raw.y);
           }
+          uint32_t mw = 0x01010101u;  // BOOL attn_mask bytes of the 4 keys
+          if (MASK) mw = mask4(jb);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             float t;
             if (SOFTCAP) t = cap_l2 * tanh_e((sacc[kb][4 * q4 + e] * p.scale + bv[e]) * inv_cap);
             else t = (sacc[kb][4 * q4 + e] * p.scale + bv[e]) * kLog2e;
-            sacc[kb][4 * q4 + e] = t;
+            // a false mask element excludes the key after the score pipeline
+            sacc[kb][4 * q4 + e] = ((mw >> (8 * e)) & 0xffu) ? t : kNegInf;
           }
         }
     }
@@ -556,11 +580,13 @@ hipError_t launch_td(const Params &p, const FPlan &pl, hipStream_t st) {
   const int64_t n = (int64_t)p.B * p.Hkv * pl.n_hg * pl.n_qt;
   if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)n), block(kThreads);
-  const bool bias = p.bias != nullptr, cap = p.softcap > 0.f;
-  if (bias && cap) hipLaunchKernelGGL((flash_fwd_kernel<T, D, true, true>), grid, block, 0, st, p, pl);
-  else if (bias) hipLaunchKernelGGL((flash_fwd_kernel<T, D, true, false>), grid, block, 0, st, p, pl);
-  else if (cap) hipLaunchKernelGGL((flash_fwd_kernel<T, D, false, true>), grid, block, 0, st, p, pl);
-  else hipLaunchKernelGGL((flash_fwd_kernel<T, D, false, false>), grid, block, 0, st, p, pl);
+  const int bm = p.mask ? 2 : (p.bias ? 1 : 0);
+  const bool cap = p.softcap > 0.f;
+#define OLK_FLASH(BMV, CAPV) hipLaunchKernelGGL((flash_fwd_kernel<T, D, BMV, CAPV>), grid, block, 0, st, p, pl)
+  if (bm == 2) { if (cap) OLK_FLASH(2, true); else OLK_FLASH(2, false); }
+  else if (bm == 1) { if (cap) OLK_FLASH(1, true); else OLK_FLASH(1, false); }
+  else { if (cap) OLK_FLASH(0, true); else OLK_FLASH(0, false); }
+#undef OLK_FLASH
   return hipGetLastError();
 }
 
@@ -581,6 +607,8 @@ hipError_t launch_flash(const Params &p, int dtype, hipStream_t st) {
   pl.xcd_remap = n_bg % 8 == 0 ? 1 : 0;
   pl.bias_vec = (p.bias_si % 4 == 0 && p.bias_sh % 4 == 0 && p.bias_sb % 4 == 0 &&
                  ((uintptr_t)p.bias & 7) == 0) ? 1 : 0;
+  pl.mask_vec = (p.mask_si % 4 == 0 && p.mask_sh % 4 == 0 && p.mask_sb % 4 == 0 &&
+                 ((uintptr_t)p.mask & 3) == 0) ? 1 : 0;
   pl.fuse_present = flash_fuses_present(p) ? 1 : 0;
   if (dtype == DT_BF16)
     return p.D == 64 ? launch_td<bf16, 64>(p, pl, st) : launch_td<bf16, 128>(p, pl, st);

@@ -141,6 +141,11 @@ WORKLOADS: Dict[str, Problem] = {
     "gqa_prefill_rope_bf16": Problem(
         op="gqa", dtype="bf16", B=4, S=2048, L=2048, P=0, Hq=32, Hkv=8, D=128,
         Dv=128, causal=1, window=-1, rotary=1),
+    # ai.onnx Attention over (B, 1, 1, T) BOOL key masks, 80% of keys attended
+    "attention_boolmask_bf16": Problem(
+        op="attention", dtype="bf16", B=4, S=2048, L=2048, P=0, Hq=32, Hkv=8, D=128,
+        Dv=128, causal=0, window=-1, has_lens=False, mask_kind="bool",
+        mask_bhs=(4, 1, 1)),
 }
 
 WORKLOAD_ORDER = [
@@ -150,6 +155,7 @@ WORKLOAD_ORDER = [
     "gqa_decode_f16",
     "mha_cross_f16",
     "gqa_prefill_rope_bf16",
+    "attention_boolmask_bf16",
 ]
 
 
