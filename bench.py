@@ -241,6 +241,28 @@ def run_workload(name, steps, warmup, with_cpu, cpu_s, is_headline):
     return p, res
 
 
+def run_backward(steps: int, warmup: int):
+    """GroupQueryAttention backward on the headline shape: dQ, dK, dV from Q, K,
+    V and a seeded dY.  Algorithmic FLOPs: 2*(3*D + 2*Dv) per unmasked (query,
+    key) pair (S recomputed, dP, dV, dK, dQ)."""
+    import torch
+    from transformer_attention_fwd_amd import olk
+    from transformer_attention_fwd_amd.workloads import workload
+    p, inputs = workload(HEADLINE)
+    dev = {k: v.to("cuda") for k, v in inputs.items()}
+    g = torch.Generator().manual_seed(5)
+    dy = torch.randn(p.B, p.S, p.Hq * p.Dv, generator=g).to(p.torch_dtype).cuda()
+    call = olk.BwdCall(p, dev, dy)
+    ms, _ = time_launches(call, steps, warmup)
+    fl = 2.0 * (3 * p.D + 2 * p.Dv) * float(allowed_pairs(p, inputs).sum()) * p.Hq
+    res = {"value": fl / (ms * 1e-3) / 1e12, "unit": "TFLOP/s", "ms_per_step": ms,
+           "kernel": olk.olk_last_kernel_name(), "flops_per_step": fl}
+    res["frac_of_peak"] = res["value"] / MFMA_PEAK_TFLOPS[p.dtype]
+    del call, dev
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -268,6 +290,11 @@ def main():
                   f"err={r['max_abs_err_sampled']:.2e}", file=sys.stderr, flush=True)
             secondary[name] = {k: r[k] for k in ("value", "unit", "frac_of_peak", "ms_per_step",
                                                  "kernel", "max_abs_err_sampled")}
+    if not args.no_secondary:
+        r = run_backward(max(3, args.steps // 10), 1)
+        print(f"[bench] gqa_backward_bf16: {r['value']:.1f} {r['unit']} ({r['ms_per_step']:.3f} ms)",
+              file=sys.stderr, flush=True)
+        secondary["gqa_backward_bf16"] = r
     line = {
         "metric": "attention TFLOP/s (prefill) + KV GB/s (decode), % of MI355X MFMA/HBM peak",
         "value": round(head["value"], 3),

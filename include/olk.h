@@ -205,6 +205,37 @@ olk_status olk_attention_decode(const olk_attn_desc *desc, const olk_attn_io *io
                                 void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static string naming a status. */
+/*
+ * Backward of the GroupQueryAttention forward (onnx-light-cpu C++ API page
+ * "Custom operators", RegisterCustomOperatorGradients, GroupQueryAttention
+ * gradient): the probabilities P are recomputed from Q, K, V; with
+ * dP = dY V^T, delta_i = sum_j P_ij dP_ij and dS = P * (dP - delta) * scale,
+ *   dQ = dS K,  dK = dS^T Q,  dV = P^T dY,
+ * the gradients of the query heads that share a KV head summed into that KV
+ * head, each output rounded once to the element type.  Scope: op GQA without
+ * past (past_seq 0; query i at position i), causal 0/1, local_window_size,
+ * scale; rank-3 tensors.  Attention bias, softcap, head_sink, rotary, masks
+ * and the qk output are OLK_E_UNSUPPORTED.  seqlens is required as for the
+ * forward (with no past every batch attends over its S keys).
+ */
+typedef struct {
+  const void *q;             /* (B,S,Hq*D) */
+  const void *k, *v;         /* (B,S,Hkv*D), (B,S,Hkv*Dv) */
+  const int32_t *seqlens;    /* (B) seqlens_k */
+  const void *dy;            /* (B,S,Hq*Dv) gradient of Y */
+  void *dq;                  /* (B,S,Hq*D) output */
+  void *dk, *dv;             /* (B,S,Hkv*D), (B,S,Hkv*Dv) outputs */
+} olk_attn_bwd_io;
+
+/* Bytes of workspace olk_attention_bwd needs: two floats per (b, h, i) row. */
+size_t olk_bwd_workspace_bytes(const olk_attn_desc *desc);
+
+/* Validates, then launches the backward on `stream`.  Workspace: at least
+ * olk_bwd_workspace_bytes(desc) bytes, 16-byte aligned (OLK_E_WORKSPACE).
+ * Outputs must not overlap inputs or each other (OLK_E_SHAPE). */
+olk_status olk_attention_bwd(const olk_attn_desc *desc, const olk_attn_bwd_io *io,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
 const char *olk_status_str(olk_status status);
 
 /* Name of the last kernel this thread launched through the library ("" if none). */

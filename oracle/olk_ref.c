@@ -581,3 +581,70 @@ int olk_ref_qk(const ref_desc *d, const ref_inputs *in, int mode, double *out, i
   }
   return err ? -1 : 0;
 }
+
+/*
+ * R22: backward of the GroupQueryAttention forward without past (onnx-light-cpu
+ * C++ API "Custom operators", RegisterCustomOperatorGradients, GroupQueryAttention
+ * gradient: probabilities P recomputed by the forward, softmax backward, the
+ * score gradient scaled by the forward scale, dQ = dS K, dK = dS^T Q and
+ * dV = P^T dY summed over the query heads that share a KV head).  In float64:
+ *   dP_ij = dY_i . V_j,  Di = sum_j P_ij dP_ij,  dS_ij = P_ij (dP_ij - Di) * scale,
+ *   dQ_i = sum_j dS_ij K_j,  dK_j = sum_(h in group) sum_i dS_ij Q_i,
+ *   dV_j = sum_(h in group) sum_i P_ij dY_i.
+ * dy is (B, S, Hq*Dv) of the element type; dq (B,S,Hq,D), dk (B,S,Hkv,D) and
+ * dv (B,S,Hkv,Dv) are float64 outputs (rounding to the element type is the
+ * caller's comparison).
+ */
+int olk_ref_attention_bwd(const ref_desc *d, const ref_inputs *in, const void *dy, double *dq,
+                          double *dk, double *dv) {
+  if (check_desc(d, in) != 0 || !dy || !dq || !dk || !dv) return -1;
+  if (d->op != REF_GQA || d->past_seq != 0 || in->bias || in->sink || d->softcap > 0.0f ||
+      d->do_rotary || d->q_rank != 3 || d->kv_rank != 3)
+    return -1;
+  const int B = d->batch, S = d->q_seq, Hq = d->q_heads, Hkv = d->kv_heads;
+  const int D = d->head_size, Dv = d->v_head_size, G = Hq / Hkv;
+  const double scale = scale_of(d);
+  memset(dq, 0, sizeof(double) * (size_t)B * S * Hq * D);
+  memset(dk, 0, sizeof(double) * (size_t)B * S * Hkv * D);
+  memset(dv, 0, sizeof(double) * (size_t)B * S * Hkv * Dv);
+  double *w = (double *)malloc(sizeof(double) * (size_t)max_keys(d));
+  double *qbuf = (double *)malloc(sizeof(double) * (size_t)D);
+  double *dp = (double *)malloc(sizeof(double) * (size_t)max_keys(d));
+  int err = 0;
+  for (int b = 0; b < B && !err; ++b)
+    for (int h = 0; h < Hq && !err; ++h) {
+      const int g = h / G;
+      for (int i = 0; i < S; ++i) {
+        double sink_w;
+        seqinfo s;
+        long n = row_weights(d, in, b, h, i, w, &sink_w, qbuf, &s);
+        if (n < 0) { err = 1; break; }
+        double Di = 0.0;
+        for (long j = 0; j < s.total_b; ++j) {
+          dp[j] = 0.0;
+          if (w[j] == 0.0) continue;
+          for (int c = 0; c < Dv; ++c)
+            dp[j] += elem(dy, d->dtype, (((size_t)b * S + i) * Hq + h) * Dv + c) *
+                     key_elem(d, in, &s, b, g, j, c, 1);
+          Di += w[j] * dp[j];
+        }
+        for (long j = 0; j < s.total_b; ++j) {
+          if (w[j] == 0.0) continue;
+          const double ds = w[j] * (dp[j] - Di) * scale;
+          double *dqi = dq + (((size_t)b * S + i) * Hq + h) * D;
+          double *dkj = dk + (((size_t)b * S + j) * Hkv + g) * D;
+          double *dvj = dv + (((size_t)b * S + j) * Hkv + g) * Dv;
+          for (int c = 0; c < D; ++c) {
+            dqi[c] += ds * key_elem(d, in, &s, b, g, j, c, 0);
+            dkj[c] += ds * qbuf[c];
+          }
+          for (int c = 0; c < Dv; ++c)
+            dvj[c] += w[j] * elem(dy, d->dtype, (((size_t)b * S + i) * Hq + h) * Dv + c);
+        }
+      }
+    }
+  free(w);
+  free(qbuf);
+  free(dp);
+  return err ? -1 : 0;
+}

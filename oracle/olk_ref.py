@@ -71,6 +71,8 @@ def lib():
         _lib.olk_ref_present.argtypes = [P(_Desc), P(_Inputs), ctypes.c_void_p, ctypes.c_void_p]
         _lib.olk_ref_qk.argtypes = [P(_Desc), P(_Inputs), ctypes.c_int, ctypes.c_void_p,
                                     ctypes.c_int]
+        _lib.olk_ref_attention_bwd.argtypes = [P(_Desc), P(_Inputs), ctypes.c_void_p,
+                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     return _lib
 
 
@@ -177,3 +179,18 @@ def qk(p, inputs: Dict[str, torch.Tensor], mode: int, threads: int = 0) -> np.nd
     if rc != 0:
         raise ValueError("oracle rejected the problem")
     return out
+
+
+def attention_bwd(p, inputs: Dict[str, torch.Tensor], dy: torch.Tensor):
+    """R22 gradients of the GroupQueryAttention forward (no past): float64
+    dq (B, S, Hq, D), dk (B, S, Hkv, D), dv (B, S, Hkv, Dv)."""
+    b = _Bound(inputs)
+    dyc = dy.detach().to("cpu").contiguous()
+    dq = np.zeros((p.B, p.S, p.Hq, p.D))
+    dk = np.zeros((p.B, p.S, p.Hkv, p.D))
+    dv = np.zeros((p.B, p.S, p.Hkv, p.Dv))
+    rc = lib().olk_ref_attention_bwd(ctypes.byref(_desc(p)), ctypes.byref(b.s), dyc.data_ptr(),
+                                     dq.ctypes.data, dk.ctypes.data, dv.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle rejected the problem")
+    return dq, dk, dv

@@ -259,3 +259,26 @@ def test_mask_rules():
     io = fake_io(att)
     io.qk_out = io.q
     assert olk.olk_validate(olk.make_desc(att.with_(qk_mode=0)), io) == olk.OLK_E_SHAPE
+
+
+def test_backward_rules():
+    p = Problem(op="gqa", dtype="bf16", B=2, S=64, L=64, Hq=8, Hkv=2, D=128, Dv=128, causal=1)
+    names = ["q", "k", "v", "seqlens", "dy", "dq", "dk", "dv"]
+
+    def st(p, ws=1 << 20, **over):
+        ptr = {n: _BASE + (i + 1) * (1 << 36) for i, n in enumerate(names)}
+        ptr.update(over)
+        io = olk.olk_attn_bwd_io(**ptr)
+        return olk.olk_attention_bwd(olk.make_desc(p), io, _BASE + 60 * (1 << 36), ws, 0)
+
+    # invalid inputs are rejected before anything is launched
+    assert st(p, dy=None) == olk.OLK_E_NULL
+    assert st(p, seqlens=None) == olk.OLK_E_NULL
+    assert st(p.with_(P=4)) == olk.OLK_E_UNSUPPORTED          # no past
+    assert st(p.with_(softcap=5.0)) == olk.OLK_E_UNSUPPORTED
+    assert st(p.with_(rotary=1)) == olk.OLK_E_UNSUPPORTED
+    assert st(p.with_(op="mha", Hkv=8, kv_rank=3)) == olk.OLK_E_UNSUPPORTED
+    assert st(p, ws=16) == olk.OLK_E_WORKSPACE
+    assert st(p, dk=_BASE + 1 * (1 << 36)) == olk.OLK_E_SHAPE  # dk overlaps q
+    n = olk.olk_bwd_workspace_bytes(olk.make_desc(p))
+    assert n >= 2 * 4 * 2 * 64 * 8 and n % 256 == 0

@@ -723,3 +723,40 @@ def test_mha_rank3_projection_bias_matches_sdpa():
     v = _bnsh_kv(p, inp["v"], p.Dv) + pb[2 * n:].view(1, p.Hq, 1, p.Dv)
     want = torch.nn.functional.scaled_dot_product_attention(q, k, v).permute(0, 2, 1, 3)
     np.testing.assert_allclose(olk_ref.attention(p, inp), want.numpy(), rtol=0, atol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# GroupQueryAttention backward (R22) against torch autograd through SDPA in
+# float64 (heads expanded by repeat_interleave, so autograd sums the groups).
+# ---------------------------------------------------------------------------
+
+def _bwd_problem(**kw):
+    base = dict(op="gqa", dtype="f32", B=2, S=9, L=9, Hq=4, Hkv=2, D=16, Dv=16, causal=1)
+    base.update(kw)
+    return Problem(**base)
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(causal=0), dict(window=3),
+                                dict(dtype="bf16", Hkv=1, D=24, Dv=8)])
+def test_backward_matches_torch_autograd(kw):
+    p = _bwd_problem(**kw)
+    inp = make_inputs(p, 81)
+    g = torch.Generator().manual_seed(3)
+    dy = torch.randn(p.B, p.S, p.Hq * p.Dv, generator=g).to(p.torch_dtype)
+    q = _bnsh_q(p, inp["q"]).clone().requires_grad_(True)
+    k = _bnsh_kv(p, inp["k"], p.D).clone().requires_grad_(True)
+    v = _bnsh_kv(p, inp["v"], p.Dv).clone().requires_grad_(True)
+    G = p.Hq // p.Hkv
+    ke, ve = k.repeat_interleave(G, dim=1), v.repeat_interleave(G, dim=1)
+    pos = torch.arange(p.S)
+    allow = torch.ones(p.S, p.S, dtype=torch.bool)
+    if p.causal:
+        allow &= pos[None, :] <= pos[:, None]
+    if p.window > 0:
+        allow &= pos[None, :] >= pos[:, None] - p.window + 1
+    y = torch.nn.functional.scaled_dot_product_attention(q, ke, ve, attn_mask=allow)
+    y.backward(_f64(dy).view(p.B, p.S, p.Hq, p.Dv).permute(0, 2, 1, 3))
+    dq, dk, dv = olk_ref.attention_bwd(p, inp, dy)
+    np.testing.assert_allclose(dq, q.grad.permute(0, 2, 1, 3).numpy(), rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(dk, k.grad.permute(0, 2, 1, 3).numpy(), rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(dv, v.grad.permute(0, 2, 1, 3).numpy(), rtol=1e-9, atol=1e-11)

@@ -427,6 +427,56 @@ olk_status olk_attention_decode(const olk_attn_desc *desc, const olk_attn_io *io
   return e == hipSuccess ? OLK_OK : OLK_E_HIP;
 }
 
+size_t olk_bwd_workspace_bytes(const olk_attn_desc *d) {
+  if (!d || d->batch <= 0 || d->q_seq <= 0 || d->q_num_heads <= 0) return 0;
+  const size_t bytes = (size_t)d->batch * d->q_seq * d->q_num_heads * 2 * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+olk_status olk_attention_bwd(const olk_attn_desc *desc, const olk_attn_bwd_io *io,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+  if (!desc || !io) return OLK_E_NULL;
+  // scope of the backward first, then the forward contract on the same tensors
+  if (desc->op != OLK_OP_GQA || desc->past_seq != 0 || desc->softcap > 0.f ||
+      desc->do_rotary || desc->mask_kind != OLK_MASK_NONE || desc->kv_inplace)
+    return OLK_E_UNSUPPORTED;
+  olk_attn_io fio;
+  memset(&fio, 0, sizeof(fio));
+  fio.q = io->q;
+  fio.k = io->k;
+  fio.v = io->v;
+  fio.seqlens = io->seqlens;
+  fio.y = io->dq;  // stands in for a Y-sized output in the null checks only
+  olk_status st = validate(desc, &fio);
+  if (st != OLK_OK) return st;
+  const olk_attn_desc *d = desc;
+  const size_t es = esize_of(d->dtype);
+  const size_t B = d->batch, S = d->q_seq, Hq = d->q_num_heads, Hkv = d->kv_num_heads,
+               D = d->head_size, Dv = d->v_head_size;
+  const size_t nq = B * S * Hq * D * es, nk = B * S * Hkv * D * es, nv = B * S * Hkv * Dv * es,
+               ndy = B * S * Hq * Dv * es;
+  if (ndy && !io->dy) return OLK_E_NULL;
+  if ((nq && !io->dq) || (nk && !io->dk) || (nv && !io->dv)) return OLK_E_NULL;
+  const Range outs[3] = {{(const char *)io->dq, nq}, {(const char *)io->dk, nk},
+                         {(const char *)io->dv, nv}};
+  const Range ins[4] = {{(const char *)io->q, nq}, {(const char *)io->k, nk},
+                        {(const char *)io->v, nv}, {(const char *)io->dy, ndy}};
+  for (int a = 0; a < 3; ++a) {
+    for (int b = 0; b < 4; ++b)
+      if (overlaps(outs[a], ins[b])) return OLK_E_SHAPE;
+    for (int b = a + 1; b < 3; ++b)
+      if (overlaps(outs[a], outs[b])) return OLK_E_SHAPE;
+  }
+  const size_t need = olk_bwd_workspace_bytes(desc);
+  if (need && (!workspace || workspace_bytes < need)) return OLK_E_WORKSPACE;
+  if (((uintptr_t)workspace & 15) != 0) return OLK_E_WORKSPACE;
+  const olk::Params p = make_params(desc, &fio);
+  const hipError_t e = olk::launch_backward(p, desc->dtype, io->dy, io->dq, io->dk, io->dv,
+                                            (float *)workspace, (hipStream_t)stream);
+  g_last_kernel = "olk_bwd_stats+dq+dkv";
+  return e == hipSuccess ? OLK_OK : OLK_E_HIP;
+}
+
 const char *olk_status_str(olk_status s) {
   switch (s) {
     case OLK_OK: return "ok";

@@ -112,5 +112,7 @@ hipError_t launch_present(const Params &p, int dtype, hipStream_t st);
 hipError_t launch_rope(const Params &p, int dtype, hipStream_t st);
 hipError_t launch_qk(const Params &p, int dtype, hipStream_t st);
 hipError_t launch_kv_bias(const Params &p, int dtype, hipStream_t st);
+hipError_t launch_backward(const Params &p, int dtype, const void *dy, void *dq, void *dk,
+                           void *dv, float *ws, hipStream_t st);
 
 }  // namespace olk

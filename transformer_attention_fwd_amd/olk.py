@@ -57,6 +57,11 @@ class olk_attn_io(ctypes.Structure):
         "qk_out")]
 
 
+class olk_attn_bwd_io(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "q", "k", "v", "seqlens", "dy", "dq", "dk", "dv")]
+
+
 _P = ctypes.POINTER
 _lib.olk_validate.argtypes = [_P(olk_attn_desc), _P(olk_attn_io)]
 _lib.olk_validate.restype = ctypes.c_int
@@ -67,13 +72,19 @@ _lib.olk_attention_fwd.restype = ctypes.c_int
 _lib.olk_attention_decode.argtypes = [_P(olk_attn_desc), _P(olk_attn_io), ctypes.c_void_p,
                                       ctypes.c_size_t, ctypes.c_void_p]
 _lib.olk_attention_decode.restype = ctypes.c_int
+_lib.olk_bwd_workspace_bytes.argtypes = [_P(olk_attn_desc)]
+_lib.olk_bwd_workspace_bytes.restype = ctypes.c_size_t
+_lib.olk_attention_bwd.argtypes = [_P(olk_attn_desc), _P(olk_attn_bwd_io), ctypes.c_void_p,
+                                   ctypes.c_size_t, ctypes.c_void_p]
+_lib.olk_attention_bwd.restype = ctypes.c_int
 _lib.olk_status_str.argtypes = [ctypes.c_int]
 _lib.olk_status_str.restype = ctypes.c_char_p
 _lib.olk_last_kernel_name.argtypes = []
 _lib.olk_last_kernel_name.restype = ctypes.c_char_p
 
 EXPORTED = ("olk_validate", "olk_workspace_bytes", "olk_attention_fwd", "olk_attention_decode",
-            "olk_status_str", "olk_last_kernel_name")
+            "olk_bwd_workspace_bytes", "olk_attention_bwd", "olk_status_str",
+            "olk_last_kernel_name")
 
 
 class OlkError(RuntimeError):
@@ -104,6 +115,16 @@ def olk_attention_decode(desc: olk_attn_desc, io: olk_attn_io, workspace: int,
                          workspace_bytes: int, stream: int) -> int:
     return _lib.olk_attention_decode(ctypes.byref(desc), ctypes.byref(io), workspace,
                                      workspace_bytes, stream)
+
+
+def olk_bwd_workspace_bytes(desc: olk_attn_desc) -> int:
+    return _lib.olk_bwd_workspace_bytes(ctypes.byref(desc))
+
+
+def olk_attention_bwd(desc: olk_attn_desc, io: olk_attn_bwd_io, workspace: int,
+                      workspace_bytes: int, stream: int) -> int:
+    return _lib.olk_attention_bwd(ctypes.byref(desc), ctypes.byref(io), workspace,
+                                  workspace_bytes, stream)
 
 
 def olk_status_str(status: int) -> str:
@@ -215,3 +236,28 @@ def attention(p: Problem, dev: Dict[str, torch.Tensor], **kw):
     c = Call(p, dev, **kw)
     c.launch()
     return c.y, c.present_k, c.present_v
+
+
+class BwdCall:
+    """One prepared backward call: descriptor, gradient outputs and workspace."""
+
+    def __init__(self, p: Problem, dev: Dict[str, torch.Tensor], dy: torch.Tensor):
+        device = dev["q"].device
+        self.p = p
+        self.dy = dy
+        self.dq = torch.empty_like(dev["q"])
+        self.dk = torch.empty_like(dev["k"])
+        self.dv = torch.empty_like(dev["v"])
+        self.desc = make_desc(p)
+        self.io = olk_attn_bwd_io(q=_ptr(dev["q"]), k=_ptr(dev["k"]), v=_ptr(dev["v"]),
+                                  seqlens=_ptr(dev.get("lens")), dy=_ptr(dy), dq=_ptr(self.dq),
+                                  dk=_ptr(self.dk), dv=_ptr(self.dv))
+        self.ws_bytes = olk_bwd_workspace_bytes(self.desc)
+        self.ws = (torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+                   if self.ws_bytes else None)
+
+    def launch(self, stream: Optional[int] = None) -> None:
+        s = current_stream() if stream is None else stream
+        st = olk_attention_bwd(self.desc, self.io, _ptr(self.ws), self.ws_bytes, s)
+        if st != OLK_OK:
+            raise OlkError(st)
