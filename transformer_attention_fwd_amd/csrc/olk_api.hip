@@ -473,7 +473,9 @@ olk_status olk_attention_bwd(const olk_attn_desc *desc, const olk_attn_bwd_io *i
   const olk::Params p = make_params(desc, &fio);
   const hipError_t e = olk::launch_backward(p, desc->dtype, io->dy, io->dq, io->dk, io->dv,
                                             (float *)workspace, (hipStream_t)stream);
-  g_last_kernel = "olk_bwd_stats+dq+dkv";
+  g_last_kernel = olk::backward_mfma_supports(p, desc->dtype, io->dy, io->dq, io->dk, io->dv)
+                      ? "olk_bwd_dq_mfma+dkv_mfma"
+                      : "olk_bwd_stats+dq+dkv";
   return e == hipSuccess ? OLK_OK : OLK_E_HIP;
 }
 

@@ -226,6 +226,8 @@ hipError_t launch_bwd_t(const Params &p, const void *dy, void *dq, void *dk, voi
 hipError_t launch_backward(const Params &p, int dtype, const void *dy, void *dq, void *dk,
                            void *dv, float *ws, hipStream_t st) {
   if (p.B == 0 || p.S == 0) return hipSuccess;
+  if (backward_mfma_supports(p, dtype, dy, dq, dk, dv))
+    return launch_backward_mfma(p, dtype, dy, dq, dk, dv, ws, st);
   if (dtype == DT_BF16) return launch_bwd_t<bf16>(p, dy, dq, dk, dv, ws, st);
   if (dtype == DT_F16) return launch_bwd_t<f16>(p, dy, dq, dk, dv, ws, st);
   return launch_bwd_t<float>(p, dy, dq, dk, dv, ws, st);

@@ -114,5 +114,11 @@ hipError_t launch_qk(const Params &p, int dtype, hipStream_t st);
 hipError_t launch_kv_bias(const Params &p, int dtype, hipStream_t st);
 hipError_t launch_backward(const Params &p, int dtype, const void *dy, void *dq, void *dk,
                            void *dv, float *ws, hipStream_t st);
+// Matrix-core backward: f16/bf16, D == Dv in {64, 128}, power-of-two head
+// groups, 16-byte aligned rows.  launch_backward takes it when it applies.
+bool backward_mfma_supports(const Params &p, int dtype, const void *dy, const void *dq,
+                            const void *dk, const void *dv);
+hipError_t launch_backward_mfma(const Params &p, int dtype, const void *dy, void *dq, void *dk,
+                                void *dv, float *ws, hipStream_t st);
 
 }  // namespace olk
