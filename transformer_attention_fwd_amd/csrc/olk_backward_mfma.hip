@@ -31,6 +31,8 @@
 // current tile computes.
 #include "olk_internal.h"
 
+#include <type_traits>
+
 namespace olk {
 namespace {
 
@@ -75,6 +77,16 @@ __device__ __forceinline__ int quad_slot(int qq) { return ((qq & 1) << 1) | (qq 
 
 __device__ __forceinline__ uint4 sel4(bool keep, uint4 x) {
   return keep ? x : make_uint4(0, 0, 0, 0);
+}
+
+// Raw buffer over `bytes` bytes from `base` (word 3 of the gfx9 descriptor:
+// 32-bit raw accesses).  Loads at offsets at or beyond `bytes` return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t bytes) {
+  const int n = bytes <= 0 ? 0 : (int)(bytes > 0x7fffffff ? 0x7fffffff : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, n, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
 
 // Column offset (elements) inside a transposed row of R columns for the
@@ -169,29 +181,37 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma(Params p, BwdPlan pl,
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   // staging maps: row-major rows tid / CH (+ RPP u), chunk tid % CH; the
-  // transposed K^T tile takes quad tid % 8 (keys 4q..4q+3) x chunk tid / 8
+  // transposed K^T tile takes quad tid % 8 (keys 4q..4q+3) x chunk tid / 8.
+  // Loads go through buffers that start at the tile's first key and end at
+  // key S, so keys past the sequence read as zeros; offsets are per thread.
   const int rrow = tid / CH, rch = tid % CH;
   const int tq = tid % (BN / 4), tc = tid / (BN / 4);
   const bool tstager = tid < NTT;
   const T *kb = (const T *)p.k + b * p.k_sb + (int64_t)g * p.k_sh;
   const T *vb = (const T *)p.v + b * p.v_sb + (int64_t)g * p.v_sh;
+  uint32_t ko[NU], vo[NU], kto[4];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    ko[u] = (uint32_t)(((rrow + u * RPP) * p.k_ss + rch * 8) * (int64_t)sizeof(T));
+    vo[u] = (uint32_t)(((rrow + u * RPP) * p.v_ss + rch * 8) * (int64_t)sizeof(T));
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) kto[u] = (uint32_t)(((4 * tq + u) * p.k_ss + tc * 8) * (int64_t)sizeof(T));
   uint4 rk[NU], rv[NU], rt[4];
   auto load = [&](int kt, bool with_t) __attribute__((always_inline)) {
     const int j0 = kt * BN;
+    const auto kr = rsrc(kb + (int64_t)j0 * p.k_ss,
+                         ((int64_t)(p.S - j0) * p.k_ss - g * p.k_sh) * (int64_t)sizeof(T));
+    const auto vr = rsrc(vb + (int64_t)j0 * p.v_ss,
+                         ((int64_t)(p.S - j0) * p.v_ss - g * p.v_sh) * (int64_t)sizeof(T));
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-      const int j = j0 + rrow + u * RPP;
-      const int jj = min(j, p.S - 1);
-      rk[u] = sel4(j < p.S, *(const uint4 *)(kb + (int64_t)jj * p.k_ss + rch * 8));
-      rv[u] = sel4(j < p.S, *(const uint4 *)(vb + (int64_t)jj * p.v_ss + rch * 8));
+      rk[u] = bload(kr, ko[u]);
+      rv[u] = bload(vr, vo[u]);
     }
     if (with_t && tstager) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int j = j0 + 4 * tq + u;
-        const int jj = min(j, p.S - 1);
-        rt[u] = sel4(j < p.S, *(const uint4 *)(kb + (int64_t)jj * p.k_ss + tc * 8));
-      }
+      for (int u = 0; u < 4; ++u) rt[u] = bload(kr, kto[u]);
     }
   };
   auto store = [&](int buf, bool with_t) __attribute__((always_inline)) {
@@ -215,10 +235,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma(Params p, BwdPlan pl,
     }
   };
   auto allowed = [&](int j) __attribute__((always_inline)) {
-    bool ok = j < p.S;
-    if (p.causal && j > row_i) ok = false;
-    if (p.window > 0 && j < row_i - p.window + 1) ok = false;
-    return ok;
+    return (j < p.S) & (!p.causal | (j <= row_i)) & ((p.window <= 0) | (j >= row_i - p.window + 1));
   };
   auto need_mask = [&](int kt) __attribute__((always_inline)) {
     const int j0 = kt * BN;
@@ -236,18 +253,23 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma(Params p, BwdPlan pl,
     const int buf = (kt - kt0) & 1;
     const bool more = kt + 1 < kt1;
     if (more) load(kt + 1, false);
-    if (wave_active) {
+    if (__builtin_amdgcn_readfirstlane((int)wave_active)) {
       f32x16 sacc, dpacc;
       scores(buf, sacc, dpacc);
-      const bool msk = need_mask(kt);
-      float mx = kNegInf;
+      // the mask test is one scalar branch per tile
+      auto scale_mask = [&](auto MASKED) __attribute__((always_inline)) {
+        float mx = kNegInf;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float t = sacc[r] * sl;
-        if (msk && !allowed(kt * BN + 8 * (r >> 2) + 4 * half + (r & 3))) t = kNegInf;
-        sacc[r] = t;
-        mx = fmaxf(mx, t);
-      }
+        for (int r = 0; r < 16; ++r) {
+          float t = sacc[r] * sl;
+          if (MASKED) t = allowed(kt * BN + 8 * (r >> 2) + 4 * half + (r & 3)) ? t : kNegInf;
+          sacc[r] = t;
+          mx = fmaxf(mx, t);
+        }
+        return mx;
+      };
+      const float mx = __builtin_amdgcn_readfirstlane((int)need_mask(kt))
+                           ? scale_mask(std::true_type()) : scale_mask(std::false_type());
       const float mn = fmaxf(m, mx);
       const float mu = mn == kNegInf ? 0.f : mn;
       const float alpha = ex2(m - mu);
@@ -298,17 +320,20 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma(Params p, BwdPlan pl,
     const int buf = (kt - kt0) & 1;
     const bool more = kt + 1 < kt1;
     if (more) load(kt + 1, true);
-    if (wave_active) {
+    if (__builtin_amdgcn_readfirstlane((int)wave_active)) {
       f32x16 sacc, dpacc;
       scores(buf, sacc, dpacc);
-      const bool msk = need_mask(kt);
+      auto dscore = [&](auto MASKED) __attribute__((always_inline)) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float t = __builtin_fmaf(sacc[r], sl, -L2);
-        if (msk && !allowed(kt * BN + 8 * (r >> 2) + 4 * half + (r & 3))) t = kNegInf;
-        const float pr = ex2(t);
-        sacc[r] = pr * (dpacc[r] - Dl);  // dS / scale
-      }
+        for (int r = 0; r < 16; ++r) {
+          float t = __builtin_fmaf(sacc[r], sl, -L2);
+          if (MASKED) t = allowed(kt * BN + 8 * (r >> 2) + 4 * half + (r & 3)) ? t : kNegInf;
+          const float pr = ex2(t);
+          sacc[r] = pr * (dpacc[r] - Dl);  // dS / scale
+        }
+      };
+      if (__builtin_amdgcn_readfirstlane((int)need_mask(kt))) dscore(std::true_type());
+      else dscore(std::false_type());
       // lane half h supplies keys 16 st + {4h..4h+3, 8+4h..8+4h+3}
 #pragma unroll
       for (int st = 0; st < BN / 16; ++st) {
@@ -339,23 +364,34 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma(Params p, BwdPlan pl,
 // ---------------------------------------------------------------------------
 // dK and dV
 // ---------------------------------------------------------------------------
+constexpr int kDkvThreads = 512;
+
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkv_mfma(Params p, BwdPlan pl,
-                                                            const T *__restrict__ dy,
-                                                            const float *__restrict__ lse2,
-                                                            const float *__restrict__ delta,
-                                                            T *__restrict__ dk,
-                                                            T *__restrict__ dv) {
+__global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_mfma(Params p, BwdPlan pl,
+                                                               const T *__restrict__ dy,
+                                                               const float *__restrict__ lse2,
+                                                               const float *__restrict__ delta,
+                                                               T *__restrict__ dk,
+                                                               T *__restrict__ dv) {
   typedef typename BV<T>::v8 vec8;
-  constexpr int QT = 64;          // row slots per tile
+  constexpr int QT = 32;          // row slots per tile (a whole number of queries)
   constexpr int CH = D / 8;
   constexpr int NKS = D / 16;
   constexpr int NDB = D / 32;
   constexpr int KST = D + 8;
   constexpr int TST = QT + 8;
-  constexpr int RPP = kThreads / CH;
+  constexpr int RPP = 256 / CH;   // row-major rows per pass of the producer threads
   constexpr int NU = QT / RPP;
-  constexpr int NTT = (QT / 4) * CH;
+  constexpr int NTT = (QT / 4) * CH;  // transposed tasks per operand
+  static_assert(NTT <= 128, "each half of the consumer threads stages one transposed tile");
+  // Producer wavefronts 0-3 (one per SIMD) own keys 32 w .. 32 w + 31 of the
+  // block: S = Q K^T and dP = dY V^T of tile t on the matrix core, then P and
+  // dS / scale on the VALU, handed over through LDS in the B-operand layout.
+  // Consumer wavefronts 4-7 (one per SIMD, same keys) accumulate
+  // dV^T += dY^T P and dK^T += Q^T dS of tile t - 1 meanwhile, so one SIMD
+  // overlaps a producer's exponentials with a consumer's MFMAs.  Producers
+  // stage the row-major Q / dY tiles and the row statistics, consumers the
+  // transposed Q^T / dY^T tiles; one barrier per step.
   __shared__ __attribute__((aligned(16))) T qlds[2][QT * KST];
   __shared__ __attribute__((aligned(16))) T dylds[2][QT * KST];
   __shared__ __attribute__((aligned(16))) T qtlds[2][D * TST];
@@ -363,16 +399,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_mfma(Params p, BwdPlan pl
   __shared__ __attribute__((aligned(16))) float lse_s[2][QT];
   __shared__ __attribute__((aligned(16))) float dl_s[2][QT];
   __shared__ __attribute__((aligned(16))) int qi_s[2][QT];
+  __shared__ __attribute__((aligned(16))) uint4 xch[2][4][QT / 16][2][64];  // P, dS per lane
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
+  const bool consumer = __builtin_amdgcn_readfirstlane(wave) >= 4;
+  const int kw = wave & 3;  // key group of the wavefront
   const int n_bg = p.B * p.Hkv;
   const int bg = blockIdx.x % n_bg;
   const int kblk = blockIdx.x / n_bg;  // early (heavy under causal) key blocks first
   const int g = bg % p.Hkv, b = bg / p.Hkv;
   const int lg = pl.log2g, G = 1 << lg, nslots = p.S << lg;
   const int j0 = kblk * 128, j_last = min(p.S, j0 + 128) - 1;
-  const int jw = j0 + wave * 32, jw_last = min(p.S - 1, jw + 31);
+  const int jw = j0 + kw * 32, jw_last = min(p.S - 1, jw + 31);
   const int key = jw + col;
   const bool key_ok = key < p.S;
   const bool wave_keys = jw < p.S;
@@ -382,80 +421,181 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_mfma(Params p, BwdPlan pl
   const int s_lo = i_lo << lg, s_hi = i_hi << lg;
   const int n_t = (s_hi - s_lo + QT - 1) / QT;
 
-  // K and V of the lane's key: B operands (key column, dims 16 ks + 8 half + e)
-  vec8 kreg[NKS], vreg[NKS];
-  {
-    const int kk = min(key, p.S - 1);
-    const T *kr = (const T *)p.k + b * p.k_sb + (int64_t)kk * p.k_ss + (int64_t)g * p.k_sh;
-    const T *vr = (const T *)p.v + b * p.v_sb + (int64_t)kk * p.v_ss + (int64_t)g * p.v_sh;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const int d0 = ks * 16 + half * 8;
-      kreg[ks] = __builtin_bit_cast(vec8, sel4(key_ok, *(const uint4 *)(kr + d0)));
-      vreg[ks] = __builtin_bit_cast(vec8, sel4(key_ok, *(const uint4 *)(vr + d0)));
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  // Tile t is QT consecutive slots = QT / G whole queries from query i0; row r
+  // is (query i0 + r / G, head g G + r % G).  Q and dY go through buffers from
+  // row i0 to the end of the batch, so rows past the sequence read as zeros.
+  const int64_t dy_ss = (int64_t)p.Hq * D;
+  auto q_off = [&](int r, int c) {
+    return (uint32_t)(((r >> lg) * p.q_ss + (int64_t)(g * G + (r & (G - 1))) * p.q_sh + c * 8) *
+                      (int64_t)sizeof(T));
+  };
+  auto dy_off = [&](int r, int c) {
+    return (uint32_t)(((r >> lg) * dy_ss + (int64_t)(g * G + (r & (G - 1))) * D + c * 8) *
+                      (int64_t)sizeof(T));
+  };
+  const T *qb = (const T *)p.q + b * p.q_sb;
+  const T *dyb = dy + (int64_t)b * p.S * dy_ss;
+  auto q_rsrc = [&](int i0) {
+    return rsrc(qb + (int64_t)i0 * p.q_ss, (int64_t)(p.S - i0) * p.q_ss * (int64_t)sizeof(T));
+  };
+  auto dy_rsrc = [&](int i0) {
+    return rsrc(dyb + (int64_t)i0 * dy_ss, (int64_t)(p.S - i0) * dy_ss * (int64_t)sizeof(T));
+  };
+  auto tile_i0 = [&](int t) { return (s_lo + t * QT) >> lg; };
 
-  const int rrow = tid / CH, rch = tid % CH;
-  const int tq = tid % (QT / 4), tc = tid / (QT / 4);
-  const bool tstager = tid < NTT;
-  uint4 rq[NU], rdy[NU], tqr[4], tdyr[4];
-  float r_lse = kPosInf, r_dl = 0.f;
-  int r_qi = 0;
-  // slot sigma of the tile -> Q row / dY row (clamped to a valid row)
-  auto q_row = [&](int sg) __attribute__((always_inline)) {
-    const int s = min(sg, nslots - 1);
-    return (const T *)p.q + b * p.q_sb + (int64_t)(s >> lg) * p.q_ss +
-           (int64_t)(g * G + (s & (G - 1))) * p.q_sh;
-  };
-  auto dy_row = [&](int sg) __attribute__((always_inline)) {
-    const int s = min(sg, nslots - 1);
-    return dy + (((int64_t)b * p.S + (s >> lg)) * p.Hq + g * G + (s & (G - 1))) * D;
-  };
-  auto load = [&](int t) __attribute__((always_inline)) {
-    const int st0 = s_lo + t * QT;
+  if (!consumer) {
+    // ---------------- producer ----------------
+    vec8 kreg[NKS], vreg[NKS];
+    {
+      const int kk = min(key, p.S - 1);
+      const T *kr = (const T *)p.k + b * p.k_sb + (int64_t)kk * p.k_ss + (int64_t)g * p.k_sh;
+      const T *vr = (const T *)p.v + b * p.v_sb + (int64_t)kk * p.v_ss + (int64_t)g * p.v_sh;
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const int sg = st0 + rrow + u * RPP;
-      rq[u] = sel4(sg < nslots, *(const uint4 *)(q_row(sg) + rch * 8));
-      rdy[u] = sel4(sg < nslots, *(const uint4 *)(dy_row(sg) + rch * 8));
-    }
-    if (tstager) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int sg = st0 + 4 * tq + u;
-        tqr[u] = sel4(sg < nslots, *(const uint4 *)(q_row(sg) + tc * 8));
-        tdyr[u] = sel4(sg < nslots, *(const uint4 *)(dy_row(sg) + tc * 8));
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int d0 = ks * 16 + half * 8;
+        kreg[ks] = __builtin_bit_cast(vec8, sel4(key_ok, *(const uint4 *)(kr + d0)));
+        vreg[ks] = __builtin_bit_cast(vec8, sel4(key_ok, *(const uint4 *)(vr + d0)));
       }
     }
-    if (tid < QT) {
-      const int sg = st0 + tid;
-      const int s = min(sg, nslots - 1);
-      const int64_t r = ((int64_t)b * p.Hq + g * G + (s & (G - 1))) * p.S + (s >> lg);
-      const float lv = lse2[r], dv_ = delta[r];
-      r_lse = sg < nslots ? lv : kPosInf;
-      r_dl = sg < nslots ? dv_ : 0.f;
-      r_qi = s >> lg;
+    // row-major staging: rows tid / CH (+ RPP u), chunk tid % CH, Q and dY
+    const int rrow = tid / CH, rch = tid % CH;
+    uint32_t qo[NU], dyo[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      qo[u] = q_off(rrow + u * RPP, rch);
+      dyo[u] = dy_off(rrow + u * RPP, rch);
+    }
+    uint4 rq[NU], rdy[NU];
+    float r_lse = kPosInf, r_dl = 0.f;
+    int r_qi = 0;
+    auto load = [&](int t) __attribute__((always_inline)) {
+      const int i0 = tile_i0(t);
+      const auto qr = q_rsrc(i0), dr = dy_rsrc(i0);
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        rq[u] = bload(qr, qo[u]);
+        rdy[u] = bload(dr, dyo[u]);
+      }
+      if (tid < QT) {
+        const int i = i0 + (tid >> lg);
+        const int64_t r = ((int64_t)b * p.Hq + g * G + (tid & (G - 1))) * p.S + min(i, p.S - 1);
+        const float lv = lse2[r], dv_ = delta[r];
+        r_lse = i < p.S ? lv : kPosInf;  // rows past the sequence: P = 0
+        r_dl = i < p.S ? dv_ : 0.f;
+        r_qi = i;
+      }
+    };
+    auto store = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        *(uint4 *)&qlds[buf][(rrow + u * RPP) * KST + rch * 8] = rq[u];
+        *(uint4 *)&dylds[buf][(rrow + u * RPP) * KST + rch * 8] = rdy[u];
+      }
+      if (tid < QT) {
+        lse_s[buf][tid] = r_lse;
+        dl_s[buf][tid] = r_dl;
+        qi_s[buf][tid] = r_qi;
+      }
+    };
+    const float sl = p.scale * kLog2e;
+    // P and dS / scale of tile t into the hand-over buffer; rows of the S / dP
+    // accumulators are slots 8 q4 + 4 half + e
+    auto produce = [&](auto MASKED, int t, bool dead) __attribute__((always_inline)) {
+      const int buf = t & 1;
+      const T *ql = qlds[buf], *dyl = dylds[buf];
+      f32x16 sacc, dpacc;
+      const f32x16 zero = {};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const vec8 aq = *(const vec8 *)&ql[col * KST + ks * 16 + half * 8];
+        const vec8 ad = *(const vec8 *)&dyl[col * KST + ks * 16 + half * 8];
+        sacc = mma(aq, kreg[ks], ks == 0 ? zero : sacc);
+        dpacc = mma(ad, vreg[ks], ks == 0 ? zero : dpacc);
+      }
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int s4 = 8 * q4 + 4 * half;
+        const float4 lv = *(const float4 *)&lse_s[buf][s4];
+        const float4 dl = *(const float4 *)&dl_s[buf][s4];
+        int4 qi = make_int4(0, 0, 0, 0);
+        if (MASKED) qi = *(const int4 *)&qi_s[buf][s4];
+        const float lva[4] = {lv.x, lv.y, lv.z, lv.w}, dla[4] = {dl.x, dl.y, dl.z, dl.w};
+        const int qia[4] = {qi.x, qi.y, qi.z, qi.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * q4 + e;
+          float x = __builtin_fmaf(sacc[r], sl, -lva[e]);
+          if (MASKED) {
+            const int i = qia[e];
+            const bool ok = !dead & (!p.causal | (key <= i)) &
+                            ((p.window <= 0) | (key >= i - p.window + 1));
+            x = ok ? x : kNegInf;
+          }
+          const float pr = ex2(x);
+          sacc[r] = pr;
+          dpacc[r] = pr * (dpacc[r] - dla[e]);
+        }
+      }
+      // lane half h supplies slots 16 st + {4h..4h+3, 8+4h..8+4h+3}
+#pragma unroll
+      for (int st = 0; st < QT / 16; ++st) {
+        vec8 pb, dsb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pb[e] = (T)sacc[8 * st + e];
+          dsb[e] = (T)dpacc[8 * st + e];
+        }
+        xch[buf][kw][st][0][lane] = __builtin_bit_cast(uint4, pb);
+        xch[buf][kw][st][1][lane] = __builtin_bit_cast(uint4, dsb);
+      }
+    };
+    if (n_t > 0) {
+      load(0);
+      store(0);
+    }
+    __syncthreads();
+    for (int t = 0; t <= n_t; ++t) {
+      const bool more = t + 1 < n_t;
+      if (more) load(t + 1);
+      if (t < n_t) {
+        // A tile that no key of the wave sees is computed too, fully masked.
+        const int st0 = s_lo + t * QT;
+        const int ia = st0 >> lg, ib = (min(nslots, st0 + QT) - 1) >> lg;
+        const bool dead = !wave_keys || (p.causal && ib < jw) ||
+                          (p.window > 0 && ia - p.window + 1 > jw_last);
+        const bool msk = dead || (p.causal && ia < jw_last) ||
+                         (p.window > 0 && ib - p.window + 1 > jw);
+        if (__builtin_amdgcn_readfirstlane((int)msk)) produce(std::true_type(), t, dead);
+        else produce(std::false_type(), t, dead);
+      }
+      if (more) store((t + 1) & 1);
+      __syncthreads();
+    }
+    return;
+  }
+
+  // ---------------- consumer ----------------
+  // transposed staging: threads 256..383 Q^T, 384..511 dY^T; task t = tid % 128
+  // -> quad t % (QT/4) (rows 4q..4q+3) x chunk t / (QT/4)
+  const int tt = tid & 127;
+  const bool t_dy = __builtin_amdgcn_readfirstlane(wave) >= 6;  // uniform: scalar buffer choice
+  const int tq = tt % (QT / 4), tc = tt / (QT / 4);
+  const bool tstager = tt < NTT;
+  uint32_t to[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) to[u] = t_dy ? dy_off(4 * tq + u, tc) : q_off(4 * tq + u, tc);
+  uint4 rt[4];
+  auto load = [&](int t) __attribute__((always_inline)) {
+    if (tstager) {
+      const int i0 = tile_i0(t);
+      const auto tr = t_dy ? dy_rsrc(i0) : q_rsrc(i0);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) rt[u] = bload(tr, to[u]);
     }
   };
   auto store = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      *(uint4 *)&qlds[buf][(rrow + u * RPP) * KST + rch * 8] = rq[u];
-      *(uint4 *)&dylds[buf][(rrow + u * RPP) * KST + rch * 8] = rdy[u];
-    }
-    if (tstager) {
-      store_tr<T, QT>(qtlds[buf], tqr, tq, tc);
-      store_tr<T, QT>(dytlds[buf], tdyr, tq, tc);
-    }
-    if (tid < QT) {
-      lse_s[buf][tid] = r_lse;
-      dl_s[buf][tid] = r_dl;
-      qi_s[buf][tid] = r_qi;
-    }
+    if (tstager) store_tr<T, QT>(t_dy ? dytlds[buf] : qtlds[buf], rt, tq, tc);
   };
-
   f32x16 dkacc[NDB], dvacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -464,73 +604,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_mfma(Params p, BwdPlan pl
       dkacc[db][r] = 0.f;
       dvacc[db][r] = 0.f;
     }
-  const float sl = p.scale * kLog2e;
-
-  if (n_t > 0) {
-    load(0);
-    store(0);
-  }
   __syncthreads();
-  for (int t = 0; t < n_t; ++t) {
-    const int buf = t & 1;
-    const bool more = t + 1 < n_t;
-    if (more) load(t + 1);
-    const int st0 = s_lo + t * QT;
-    const int ia = st0 >> lg, ib = (min(nslots, st0 + QT) - 1) >> lg;
-    const bool dead = !wave_keys || (p.causal && ib < jw) ||
-                      (p.window > 0 && ia - p.window + 1 > jw_last);
-    if (!dead) {
-      const bool msk = (p.causal && ia < jw_last) || (p.window > 0 && ib - p.window + 1 > jw);
-      const T *ql = qlds[buf], *dyl = dylds[buf];
-      f32x16 sacc[2], dpacc[2];
-      const f32x16 zero = {};
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          const vec8 aq = *(const vec8 *)&ql[(mb * 32 + col) * KST + ks * 16 + half * 8];
-          const vec8 ad = *(const vec8 *)&dyl[(mb * 32 + col) * KST + ks * 16 + half * 8];
-          sacc[mb] = mma(aq, kreg[ks], ks == 0 ? zero : sacc[mb]);
-          dpacc[mb] = mma(ad, vreg[ks], ks == 0 ? zero : dpacc[mb]);
-        }
-      // P and dS / scale; rows are slots 32 mb + 8 q4 + 4 half + e
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int s4 = mb * 32 + 8 * q4 + 4 * half;
-          const float4 lv = *(const float4 *)&lse_s[buf][s4];
-          const float4 dl = *(const float4 *)&dl_s[buf][s4];
-          int4 qi = make_int4(0, 0, 0, 0);
-          if (msk) qi = *(const int4 *)&qi_s[buf][s4];
-          const float lva[4] = {lv.x, lv.y, lv.z, lv.w}, dla[4] = {dl.x, dl.y, dl.z, dl.w};
-          const int qia[4] = {qi.x, qi.y, qi.z, qi.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * q4 + e;
-            float x = __builtin_fmaf(sacc[mb][r], sl, -lva[e]);
-            if (msk) {
-              const int i = qia[e];
-              bool ok = true;
-              if (p.causal && key > i) ok = false;
-              if (p.window > 0 && key < i - p.window + 1) ok = false;
-              x = ok ? x : kNegInf;
-            }
-            const float pr = ex2(x);
-            sacc[mb][r] = pr;
-            dpacc[mb][r] = pr * (dpacc[mb][r] - dla[e]);
-          }
-        }
+  for (int t = 0; t <= n_t; ++t) {
+    if (t < n_t) load(t);
+    if (t > 0) {
+      const int buf = (t - 1) & 1;
       const T *qtl = qtlds[buf], *dytl = dytlds[buf];
-      // lane half h supplies slots 16 st + {4h..4h+3, 8+4h..8+4h+3}
 #pragma unroll
       for (int st = 0; st < QT / 16; ++st) {
-        vec8 pb, dsb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pb[e] = (T)sacc[st >> 1][8 * (st & 1) + e];
-          dsb[e] = (T)dpacc[st >> 1][8 * (st & 1) + e];
-        }
+        const vec8 pb = __builtin_bit_cast(vec8, xch[buf][kw][st][0][lane]);
+        const vec8 dsb = __builtin_bit_cast(vec8, xch[buf][kw][st][1][lane]);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           dvacc[db] = mma(read_tr<T, QT>(dytl, db, col, st, half), pb, dvacc[db]);
@@ -538,7 +621,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_mfma(Params p, BwdPlan pl
         }
       }
     }
-    if (more) store(buf ^ 1);
+    if (t < n_t) store(t & 1);
     __syncthreads();
   }
   if (!key_ok) return;
@@ -571,7 +654,7 @@ hipError_t launch_t(const Params &p, const void *dy, void *dq, void *dk, void *d
   hipLaunchKernelGGL((bwd_dq_mfma<T, D>), dim3(pl.n_qtile * n_bg), dim3(kThreads), 0, st, p, pl,
                      (const T *)dy, lse, delta, (T *)dq);
   const int n_kb = (p.S + 127) / 128;
-  hipLaunchKernelGGL((bwd_dkv_mfma<T, D>), dim3(n_kb * n_bg), dim3(kThreads), 0, st, p, pl,
+  hipLaunchKernelGGL((bwd_dkv_mfma<T, D>), dim3(n_kb * n_bg), dim3(kDkvThreads), 0, st, p, pl,
                      (const T *)dy, lse, delta, (T *)dk, (T *)dv);
   return hipGetLastError();
 }
@@ -582,8 +665,14 @@ bool backward_mfma_supports(const Params &p, int dtype, const void *dy, const vo
                             const void *dk, const void *dv) {
   if (dtype != DT_BF16 && dtype != DT_F16) return false;
   if (p.D != p.Dv || (p.D != 64 && p.D != 128)) return false;
-  if (p.G <= 0 || (p.G & (p.G - 1)) != 0) return false;  // slot -> (query, head) by shifts
+  // slot -> (query, head) by shifts; a 32-slot tile holds whole queries
+  if (p.G <= 0 || p.G > 32 || (p.G & (p.G - 1)) != 0) return false;
   if ((int64_t)p.S * p.G > (1ll << 30)) return false;
+  // buffer loads address one batch of Q, K, V or dY with 32-bit byte offsets
+  const int64_t es = 2;
+  if ((int64_t)p.S * p.q_ss * es > 0x7fffffff || (int64_t)p.S * p.k_ss * es > 0x7fffffff ||
+      (int64_t)p.S * p.v_ss * es > 0x7fffffff || (int64_t)p.S * p.Hq * p.D * es > 0x7fffffff)
+    return false;
   auto al16 = [](const void *x) { return ((uintptr_t)x & 15) == 0; };
   auto al8 = [](const void *x) { return ((uintptr_t)x & 7) == 0; };
   // 16-byte operand loads of Q, K, V, dY rows; 8-byte output stores
