@@ -181,24 +181,23 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma(Params p, BwdPlan pl,
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   // staging maps: row-major rows tid / CH (+ RPP u), chunk tid % CH; the
-  // transposed K^T tile takes quad tid % 8 (keys 4q..4q+3) x chunk tid / 8.
-  // Loads go through buffers that start at the tile's first key and end at
-  // key S, so keys past the sequence read as zeros; offsets are per thread.
+  // transposed K^T tile (built from the row-major K tile in LDS) takes quad
+  // tid % 8 (keys 4q..4q+3) x chunk tid / 8.  Loads go through buffers that
+  // start at the tile's first key and end at key S, so keys past the sequence
+  // read as zeros; offsets are per thread.
   const int rrow = tid / CH, rch = tid % CH;
   const int tq = tid % (BN / 4), tc = tid / (BN / 4);
   const bool tstager = tid < NTT;
   const T *kb = (const T *)p.k + b * p.k_sb + (int64_t)g * p.k_sh;
   const T *vb = (const T *)p.v + b * p.v_sb + (int64_t)g * p.v_sh;
-  uint32_t ko[NU], vo[NU], kto[4];
+  uint32_t ko[NU], vo[NU];
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
     ko[u] = (uint32_t)(((rrow + u * RPP) * p.k_ss + rch * 8) * (int64_t)sizeof(T));
     vo[u] = (uint32_t)(((rrow + u * RPP) * p.v_ss + rch * 8) * (int64_t)sizeof(T));
   }
-#pragma unroll
-  for (int u = 0; u < 4; ++u) kto[u] = (uint32_t)(((4 * tq + u) * p.k_ss + tc * 8) * (int64_t)sizeof(T));
   uint4 rk[NU], rv[NU], rt[4];
-  auto load = [&](int kt, bool with_t) __attribute__((always_inline)) {
+  auto load = [&](int kt, bool) __attribute__((always_inline)) {
     const int j0 = kt * BN;
     const auto kr = rsrc(kb + (int64_t)j0 * p.k_ss,
                          ((int64_t)(p.S - j0) * p.k_ss - g * p.k_sh) * (int64_t)sizeof(T));
@@ -209,18 +208,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma(Params p, BwdPlan pl,
       rk[u] = bload(kr, ko[u]);
       rv[u] = bload(vr, vo[u]);
     }
-    if (with_t && tstager) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) rt[u] = bload(kr, kto[u]);
-    }
   };
-  auto store = [&](int buf, bool with_t) __attribute__((always_inline)) {
+  auto store = [&](int buf, bool) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       *(uint4 *)&klds[buf][(rrow + u * RPP) * KST + rch * 8] = rk[u];
       *(uint4 *)&vlds[buf][(rrow + u * RPP) * KST + rch * 8] = rv[u];
     }
-    if (with_t && tstager) store_tr<T, BN>(ktlds[buf], rt, tq, tc);
   };
   // S^T and dP^T of one tile (key rows, slot columns)
   auto scores = [&](int buf, f32x16 &sacc, f32x16 &dpacc) __attribute__((always_inline)) {
@@ -313,39 +307,52 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma(Params p, BwdPlan pl,
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) dqacc[db][r] = 0.f;
-  load(kt0, true);
-  store(0, true);
+  // K^T of tile kt is built in LDS from the row-major K tile during step kt
+  // and used by the dQ MFMAs of step kt + 1, together with dS of tile kt kept
+  // in registers; the last step only finishes dQ.
+  vec8 dsh[BN / 16];
+  load(kt0, false);
+  store(0, false);
   __syncthreads();
-  for (int kt = kt0; kt < kt1; ++kt) {
+  for (int kt = kt0; kt <= kt1; ++kt) {
     const int buf = (kt - kt0) & 1;
-    const bool more = kt + 1 < kt1;
-    if (more) load(kt + 1, true);
+    const bool cur = kt < kt1, more = kt + 1 < kt1;
+    if (more) load(kt + 1, false);
+    if (cur && tstager) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) rt[u] = *(const uint4 *)&klds[buf][(4 * tq + u) * KST + tc * 8];
+      store_tr<T, BN>(ktlds[buf], rt, tq, tc);
+    }
     if (__builtin_amdgcn_readfirstlane((int)wave_active)) {
-      f32x16 sacc, dpacc;
-      scores(buf, sacc, dpacc);
-      auto dscore = [&](auto MASKED) __attribute__((always_inline)) {
+      if (kt > kt0) {
+        // lane half h supplies keys 16 st + {4h..4h+3, 8+4h..8+4h+3}
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float t = __builtin_fmaf(sacc[r], sl, -L2);
-          if (MASKED) t = allowed(kt * BN + 8 * (r >> 2) + 4 * half + (r & 3)) ? t : kNegInf;
-          const float pr = ex2(t);
-          sacc[r] = pr * (dpacc[r] - Dl);  // dS / scale
-        }
-      };
-      if (__builtin_amdgcn_readfirstlane((int)need_mask(kt))) dscore(std::true_type());
-      else dscore(std::false_type());
-      // lane half h supplies keys 16 st + {4h..4h+3, 8+4h..8+4h+3}
+        for (int st = 0; st < BN / 16; ++st)
 #pragma unroll
-      for (int st = 0; st < BN / 16; ++st) {
-        vec8 dsb;
+          for (int db = 0; db < NDB; ++db)
+            dqacc[db] = mma(read_tr<T, BN>(ktlds[buf ^ 1], db, col, st, half), dsh[st], dqacc[db]);
+      }
+      if (cur) {
+        f32x16 sacc, dpacc;
+        scores(buf, sacc, dpacc);
+        auto dscore = [&](auto MASKED) __attribute__((always_inline)) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dsb[e] = (T)sacc[8 * st + e];
+          for (int r = 0; r < 16; ++r) {
+            float t = __builtin_fmaf(sacc[r], sl, -L2);
+            if (MASKED) t = allowed(kt * BN + 8 * (r >> 2) + 4 * half + (r & 3)) ? t : kNegInf;
+            const float pr = ex2(t);
+            sacc[r] = pr * (dpacc[r] - Dl);  // dS / scale
+          }
+        };
+        if (__builtin_amdgcn_readfirstlane((int)need_mask(kt))) dscore(std::true_type());
+        else dscore(std::false_type());
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          dqacc[db] = mma(read_tr<T, BN>(ktlds[buf], db, col, st, half), dsb, dqacc[db]);
+        for (int st = 0; st < BN / 16; ++st)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) dsh[st][e] = (T)sacc[8 * st + e];
       }
     }
-    if (more) store(buf ^ 1, true);
+    if (more) store(buf ^ 1, false);
     __syncthreads();
   }
   if (!row_ok) return;
@@ -390,8 +397,8 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_mfma(Params p, BwdPlan
   // Consumer wavefronts 4-7 (one per SIMD, same keys) accumulate
   // dV^T += dY^T P and dK^T += Q^T dS of tile t - 1 meanwhile, so one SIMD
   // overlaps a producer's exponentials with a consumer's MFMAs.  Producers
-  // stage the row-major Q / dY tiles and the row statistics, consumers the
-  // transposed Q^T / dY^T tiles; one barrier per step.
+  // load the row-major Q / dY tiles and the row statistics, consumers build
+  // the transposed Q^T / dY^T tiles from them in LDS; one barrier per step.
   __shared__ __attribute__((aligned(16))) T qlds[2][QT * KST];
   __shared__ __attribute__((aligned(16))) T dylds[2][QT * KST];
   __shared__ __attribute__((aligned(16))) T qtlds[2][D * TST];
@@ -465,36 +472,40 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_mfma(Params p, BwdPlan
       qo[u] = q_off(rrow + u * RPP, rch);
       dyo[u] = dy_off(rrow + u * RPP, rch);
     }
-    uint4 rq[NU], rdy[NU];
-    float r_lse = kPosInf, r_dl = 0.f;
-    int r_qi = 0;
-    auto load = [&](int t) __attribute__((always_inline)) {
+    // Loads run two steps ahead of the compute: tile t + 2 is loaded into one
+    // register set during step t and stored to LDS at the end of step t + 1.
+    struct Stage {
+      uint4 q[NU], dy[NU];
+      float lse, dl;
+      int qi;
+    };
+    auto load = [&](int t, Stage &sg) __attribute__((always_inline)) {
       const int i0 = tile_i0(t);
       const auto qr = q_rsrc(i0), dr = dy_rsrc(i0);
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
-        rq[u] = bload(qr, qo[u]);
-        rdy[u] = bload(dr, dyo[u]);
+        sg.q[u] = bload(qr, qo[u]);
+        sg.dy[u] = bload(dr, dyo[u]);
       }
       if (tid < QT) {
         const int i = i0 + (tid >> lg);
         const int64_t r = ((int64_t)b * p.Hq + g * G + (tid & (G - 1))) * p.S + min(i, p.S - 1);
         const float lv = lse2[r], dv_ = delta[r];
-        r_lse = i < p.S ? lv : kPosInf;  // rows past the sequence: P = 0
-        r_dl = i < p.S ? dv_ : 0.f;
-        r_qi = i;
+        sg.lse = i < p.S ? lv : kPosInf;  // rows past the sequence: P = 0
+        sg.dl = i < p.S ? dv_ : 0.f;
+        sg.qi = i;
       }
     };
-    auto store = [&](int buf) __attribute__((always_inline)) {
+    auto store = [&](int buf, const Stage &sg) __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
-        *(uint4 *)&qlds[buf][(rrow + u * RPP) * KST + rch * 8] = rq[u];
-        *(uint4 *)&dylds[buf][(rrow + u * RPP) * KST + rch * 8] = rdy[u];
+        *(uint4 *)&qlds[buf][(rrow + u * RPP) * KST + rch * 8] = sg.q[u];
+        *(uint4 *)&dylds[buf][(rrow + u * RPP) * KST + rch * 8] = sg.dy[u];
       }
       if (tid < QT) {
-        lse_s[buf][tid] = r_lse;
-        dl_s[buf][tid] = r_dl;
-        qi_s[buf][tid] = r_qi;
+        lse_s[buf][tid] = sg.lse;
+        dl_s[buf][tid] = sg.dl;
+        qi_s[buf][tid] = sg.qi;
       }
     };
     const float sl = p.scale * kLog2e;
@@ -549,48 +560,58 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_mfma(Params p, BwdPlan
         xch[buf][kw][st][1][lane] = __builtin_bit_cast(uint4, dsb);
       }
     };
+    auto compute = [&](int t) __attribute__((always_inline)) {
+      // A tile that no key of the wave sees is computed too, fully masked.
+      const int st0 = s_lo + t * QT;
+      const int ia = st0 >> lg, ib = (min(nslots, st0 + QT) - 1) >> lg;
+      const bool dead = !wave_keys || (p.causal && ib < jw) ||
+                        (p.window > 0 && ia - p.window + 1 > jw_last);
+      const bool msk = dead || (p.causal && ia < jw_last) ||
+                       (p.window > 0 && ib - p.window + 1 > jw);
+      if (__builtin_amdgcn_readfirstlane((int)msk)) produce(std::true_type(), t, dead);
+      else produce(std::false_type(), t, dead);
+    };
+    Stage sa, sb;
+    sa.lse = sb.lse = kPosInf;
+    sa.dl = sb.dl = 0.f;
+    sa.qi = sb.qi = 0;
     if (n_t > 0) {
-      load(0);
-      store(0);
+      load(0, sa);
+      store(0, sa);
     }
     __syncthreads();
-    for (int t = 0; t <= n_t; ++t) {
-      const bool more = t + 1 < n_t;
-      if (more) load(t + 1);
-      if (t < n_t) {
-        // A tile that no key of the wave sees is computed too, fully masked.
-        const int st0 = s_lo + t * QT;
-        const int ia = st0 >> lg, ib = (min(nslots, st0 + QT) - 1) >> lg;
-        const bool dead = !wave_keys || (p.causal && ib < jw) ||
-                          (p.window > 0 && ia - p.window + 1 > jw_last);
-        const bool msk = dead || (p.causal && ia < jw_last) ||
-                         (p.window > 0 && ib - p.window + 1 > jw);
-        if (__builtin_amdgcn_readfirstlane((int)msk)) produce(std::true_type(), t, dead);
-        else produce(std::false_type(), t, dead);
-      }
-      if (more) store((t + 1) & 1);
+    if (n_t > 1) load(1, sb);
+    for (int t = 0; t < n_t; t += 2) {
+      if (t + 2 < n_t) load(t + 2, sa);
+      compute(t);
+      if (t + 1 < n_t) store((t + 1) & 1, sb);
       __syncthreads();
+      if (t + 1 < n_t) {
+        if (t + 3 < n_t) load(t + 3, sb);
+        compute(t + 1);
+        if (t + 2 < n_t) store(t & 1, sa);
+        __syncthreads();
+      }
     }
+    __syncthreads();  // the consumer's last step
     return;
   }
 
   // ---------------- consumer ----------------
-  // transposed staging: threads 256..383 Q^T, 384..511 dY^T; task t = tid % 128
-  // -> quad t % (QT/4) (rows 4q..4q+3) x chunk t / (QT/4)
+  // The transposed tiles are built from the row-major tiles the producers
+  // staged (4 rows x one 16-byte chunk per task): threads 256..383 Q^T,
+  // 384..511 dY^T; task t = tid % 128 -> quad t % (QT/4) (rows 4q..4q+3) x
+  // chunk t / (QT/4).
   const int tt = tid & 127;
-  const bool t_dy = __builtin_amdgcn_readfirstlane(wave) >= 6;  // uniform: scalar buffer choice
+  const bool t_dy = __builtin_amdgcn_readfirstlane(wave) >= 6;  // uniform
   const int tq = tt % (QT / 4), tc = tt / (QT / 4);
   const bool tstager = tt < NTT;
-  uint32_t to[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) to[u] = t_dy ? dy_off(4 * tq + u, tc) : q_off(4 * tq + u, tc);
   uint4 rt[4];
   auto load = [&](int t) __attribute__((always_inline)) {
     if (tstager) {
-      const int i0 = tile_i0(t);
-      const auto tr = t_dy ? dy_rsrc(i0) : q_rsrc(i0);
+      const T *src = t_dy ? dylds[t & 1] : qlds[t & 1];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) rt[u] = bload(tr, to[u]);
+      for (int u = 0; u < 4; ++u) rt[u] = *(const uint4 *)&src[(4 * tq + u) * KST + tc * 8];
     }
   };
   auto store = [&](int buf) __attribute__((always_inline)) {
