@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="time only the GroupQueryAttention backward line (for profiling)")
     return ap.parse_args()
 
 
@@ -272,6 +274,10 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs an MI355X"
     torch.cuda.set_device(0)
+    if args.backward_only:
+        r = run_backward(args.steps, args.warmup)
+        print(json.dumps({"workload": "gqa_backward_bf16", **r}), flush=True)
+        return
     t_start = time.perf_counter()
     p, head = run_workload(args.workload, args.steps, args.warmup, not args.no_cpu,
                            args.cpu_seconds, True)

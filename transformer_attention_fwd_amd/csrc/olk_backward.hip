@@ -5,6 +5,9 @@
 // scale, dQ = dS K, dK = dS^T Q, dV = P^T dY with the grouped K/V head
 // gradients summed back to their KV head, and a cast to the input type).
 //
+// These kernels take every shape in scope that the matrix-core kernels of
+// olk_backward_mfma.hip do not (fp32, other head sizes, Dv != D, head groups
+// that are not a power of two up to 32).
 // Three kernels, fp32 VALU arithmetic, one 64-lane wavefront per work item:
 //   bwd_stats_kernel  per query row: lse_i = log sum_j exp(s_ij) over the
 //                     allowed keys (s = scaled score) and

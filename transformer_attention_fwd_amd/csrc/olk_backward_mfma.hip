@@ -17,18 +17,19 @@
 //   operands).  Pass 1 runs the online log-sum-exp and delta_i = sum_j P dP
 //   in the exp2 domain and stores lse2_i = log2 sum_j 2^(s_ij log2 e) and
 //   delta_i for the second kernel; pass 2 recomputes P and dS and accumulates
-//   dQ^T += K^T dS^T with dS^T as the B operand and K^T staged transposed.
-// bwd_dkv_mfma: a workgroup is 4 wavefronts x 32 keys (K and V of its keys in
-//   registers as the B operands); row slots advance in tiles of 64.  In the
-//   S = Q K^T accumulator layout a lane owns one key, so P and dS are the B
-//   operands of dV^T += dY^T P and dK^T += Q^T dS, with dY^T and Q^T staged
-//   transposed.
+//   dQ^T += K^T dS^T with dS^T as the B operand, one tile behind the scores,
+//   with K^T transposed in LDS from the row-major K tile.
+// bwd_dkv_mfma: a workgroup owns 128 keys and is 8 wavefronts, two per SIMD.
+//   Producers hold K and V of 32 keys in registers as the B operands of
+//   S = Q K^T and dP = dY V^T (a lane owns one key), make P and dS for a tile
+//   of 32 row slots and hand them over through LDS; consumers (same keys, one
+//   tile behind) accumulate dV^T += dY^T P and dK^T += Q^T dS with P and dS as
+//   the B operands and dY^T, Q^T transposed in LDS from the row-major tiles.
 // Transposed tiles put each 16-row group in the order {0-3, 8-11, 4-7, 12-15},
 // the k order in which a lane half supplies an accumulator column as a B
 // operand, pad rows by 16 bytes and XOR-swizzle 16-byte chunks by (row / 32);
 // row-major tiles pad rows by 16 bytes.  Tiles are double-buffered in LDS with
-// one barrier per tile; the next tile's global loads are in flight while the
-// current tile computes.
+// one barrier per step; global loads are in flight while earlier tiles compute.
 #include "olk_internal.h"
 
 #include <type_traits>
