@@ -8,7 +8,8 @@
 // header page, "class Attention").  The decomposition is ours:
 //
 // * A workgroup is 4 wavefronts x 32 row slots; two workgroups share a CU
-//   (two wavefronts per SIMD, so one wave's MFMAs overlap the other's softmax).
+//   (two wavefronts per SIMD, so one wave's MFMAs overlap the other's softmax;
+//   three at head size 64).
 //   Slots pack the GH query heads sharing one KV head with consecutive queries
 //   (slot -> (query, head)): every K/V tile in LDS serves the whole head group.
 // * S^T = K Q^T and O^T += V^T P^T run on v_mfma_f32_32x32x16.  In the S^T
@@ -104,9 +105,14 @@ struct FPlan {
   int fuse_present;
 };
 
+// Wavefronts per SIMD the register budget is sized for: three at head size 64
+// (more workgroups resident when a grid holds few query tiles; the BOOL-mask
+// form needs more registers and keeps two), two at head size 128.
+template <int D, int BM> constexpr int kOcc = (D == 64 && BM != 2) ? 3 : 2;
+
 // BM: 0 no bias, 1 attn_bias, 2 BOOL attn_mask (with or without attn_bias)
 template <typename T, int D, int BM, bool SOFTCAP>
-__global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Params p, FPlan pl) {
+__global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Params p, FPlan pl) {
   typedef typename FV<T>::v8 vec8;
   constexpr bool BIAS = BM != 0;   // the score epilogue reads a bias row
   constexpr bool MASK = BM == 2;
@@ -335,8 +341,9 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(Params p, FPlan 
       if (jb + e < p.mask_cols) w |= (uint32_t)mask_row[jb + e] << (8 * e);
     return w;
   };
-  // At head size 64 the bias of the next tile is prefetched with its K/V.
-  constexpr bool BPRE = BIAS && D == 64;
+  // At head size 64 with two wavefronts per SIMD the bias of the next tile is
+  // prefetched with its K/V (with three, its registers are not available).
+  constexpr bool BPRE = BIAS && D == 64 && kOcc<D, BM> == 2;
   uint2 bcur[BPRE ? KB : 1][4], bnext[BPRE ? KB : 1][4];
   auto load_bias = [&](int kt, uint2 (&bb)[BPRE ? KB : 1][4]) {
 #pragma unroll
