@@ -15,6 +15,7 @@
 namespace olk {
 hipError_t launch_flash(const Params &p, int dtype, hipStream_t st);
 bool flash_fuses_present(const Params &p);
+bool flash_rotates_q(const Params &p);
 hipError_t launch_tiled(const Params &p, int dtype, hipStream_t st);
 hipError_t launch_tiled_split(const Params &p, int dtype, int split_tiles, float *ws,
                               hipStream_t st);
@@ -315,15 +316,20 @@ hipError_t kv_bias_prepass(olk::Params &p, int dtype, hipStream_t st) {
 // pre-pass (rotated Q into Y, rotated new K and new V into present), and
 // return the parameters of the attention proper: Q read from Y, every key read
 // from present, nothing left for the attention kernels to write into present.
-hipError_t rotary_prepass(olk::Params &p, int dtype, hipStream_t st) {
+// With q_in_kernel the prefill kernel rotates Q as it loads it: the pre-pass
+// leaves Q alone and the attention reads Q from Q.
+hipError_t rotary_prepass(olk::Params &p, int dtype, hipStream_t st, bool q_in_kernel = false) {
   olk::Params pp = p;
   pp.present_past_only = 1;
   hipError_t e = olk::launch_present(pp, dtype, st);
   if (e != hipSuccess) return e;
+  p.rot_q = q_in_kernel ? 1 : 0;
   e = olk::launch_rope(p, dtype, st);
   if (e != hipSuccess) return e;
-  p.q = p.y;
-  p.q_sb = p.y_sb; p.q_ss = p.y_ss; p.q_sh = p.y_sh;
+  if (!q_in_kernel) {
+    p.q = p.y;
+    p.q_sb = p.y_sb; p.q_ss = p.y_ss; p.q_sh = p.y_sh;
+  }
   p.past_k = p.present_k;
   p.past_v = p.present_v;
   p.past_rows = p.T;
@@ -363,13 +369,19 @@ olk_status olk_attention_fwd(const olk_attn_desc *desc, const olk_attn_io *io, v
   // the kernel choice is made on the parameters the attention kernel gets (with
   // do_rotary, Q is read from Y); check it before anything is launched
   olk::Params pa = p;
-  if (desc->do_rotary) { pa.q = pa.y; pa.q_sb = pa.y_sb; pa.q_ss = pa.y_ss; pa.q_sh = pa.y_sh; }
-  const bool tiled_ok = olk::tiled_supports(pa, desc->dtype);
+  // do_rotary: the prefill kernel rotates Q itself where it can, otherwise Q is
+  // rotated into Y by the pre-pass and read from there
+  const bool q_in_kernel = desc->do_rotary && desc->kernel != OLK_KERNEL_GENERIC &&
+                           olk::tiled_supports(p, desc->dtype) && olk::flash_rotates_q(p);
+  if (desc->do_rotary && !q_in_kernel) {
+    pa.q = pa.y; pa.q_sb = pa.y_sb; pa.q_ss = pa.y_ss; pa.q_sh = pa.y_sh;
+  }
+  const bool tiled_ok = q_in_kernel || olk::tiled_supports(pa, desc->dtype);
   if (desc->kernel == OLK_KERNEL_TILED && !tiled_ok) return OLK_E_UNSUPPORTED;
   const bool use_tiled = desc->kernel != OLK_KERNEL_GENERIC && tiled_ok;
   hipError_t e = hipSuccess;
   if (desc->do_rotary) {
-    e = rotary_prepass(p, desc->dtype, s);
+    e = rotary_prepass(p, desc->dtype, s, q_in_kernel);
   } else if (kv_bias_path(desc, io)) {
     e = kv_bias_prepass(p, desc->dtype, s);
   } else {

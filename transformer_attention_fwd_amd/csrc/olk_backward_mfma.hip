@@ -198,7 +198,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma(Params p, BwdPlan pl,
     vo[u] = (uint32_t)(((rrow + u * RPP) * p.v_ss + rch * 8) * (int64_t)sizeof(T));
   }
   uint4 rk[NU], rv[NU], rt[4];
-  auto load = [&](int kt, bool) __attribute__((always_inline)) {
+  auto load = [&](int kt) __attribute__((always_inline)) {
     const int j0 = kt * BN;
     const auto kr = rsrc(kb + (int64_t)j0 * p.k_ss,
                          ((int64_t)(p.S - j0) * p.k_ss - g * p.k_sh) * (int64_t)sizeof(T));
@@ -210,7 +210,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma(Params p, BwdPlan pl,
       rv[u] = bload(vr, vo[u]);
     }
   };
-  auto store = [&](int buf, bool) __attribute__((always_inline)) {
+  auto store = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       *(uint4 *)&klds[buf][(rrow + u * RPP) * KST + rch * 8] = rk[u];
@@ -241,13 +241,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma(Params p, BwdPlan pl,
 
   // ---- pass 1: lse2 and delta of the slot (each lane half over its keys) ----
   float m = kNegInf, l = 0.f, a = 0.f;
-  load(kt0, false);
-  store(0, false);
+  load(kt0);
+  store(0);
   __syncthreads();
   for (int kt = kt0; kt < kt1; ++kt) {
     const int buf = (kt - kt0) & 1;
     const bool more = kt + 1 < kt1;
-    if (more) load(kt + 1, false);
+    if (more) load(kt + 1);
     if (__builtin_amdgcn_readfirstlane((int)wave_active)) {
       f32x16 sacc, dpacc;
       scores(buf, sacc, dpacc);
@@ -279,7 +279,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma(Params p, BwdPlan pl,
       a = __builtin_fmaf(a, alpha, as);
       m = mn;
     }
-    if (more) store(buf ^ 1, false);
+    if (more) store(buf ^ 1);
     __syncthreads();
   }
   float L2 = kPosInf, Dl = 0.f;  // no allowed key: P = 0 everywhere
@@ -312,13 +312,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma(Params p, BwdPlan pl,
   // and used by the dQ MFMAs of step kt + 1, together with dS of tile kt kept
   // in registers; the last step only finishes dQ.
   vec8 dsh[BN / 16];
-  load(kt0, false);
-  store(0, false);
+  load(kt0);
+  store(0);
   __syncthreads();
   for (int kt = kt0; kt <= kt1; ++kt) {
     const int buf = (kt - kt0) & 1;
     const bool cur = kt < kt1, more = kt + 1 < kt1;
-    if (more) load(kt + 1, false);
+    if (more) load(kt + 1);
     if (cur && tstager) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) rt[u] = *(const uint4 *)&klds[buf][(4 * tq + u) * KST + tc * 8];
@@ -353,7 +353,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_mfma(Params p, BwdPlan pl,
           for (int e = 0; e < 8; ++e) dsh[st][e] = (T)sacc[8 * st + e];
       }
     }
-    if (more) store(buf ^ 1, false);
+    if (more) store(buf ^ 1);
     __syncthreads();
   }
   if (!row_ok) return;

@@ -76,6 +76,12 @@ template <> __device__ __forceinline__ float hi16<f16>(uint32_t w) {
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// two floats rounded (RNE) to the element type, packed low / high
+template <typename T> __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  const T l = (T)lo, h = (T)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
+}
+
 // Value of lane ^ 32 combined with this lane's, via v_permlane32_swap (with
 // both operands x, the two results hold x of lane l and of lane l ^ 32).
 __device__ __forceinline__ float max_halves(float x) {
@@ -85,11 +91,6 @@ __device__ __forceinline__ float max_halves(float x) {
 __device__ __forceinline__ float sum_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// tanh x = 1 - 2 / (e^{2x} + 1); saturates to +-1 without NaN.
-__device__ __forceinline__ float tanh_e(float x) {
-  return 1.0f - 2.0f * __builtin_amdgcn_rcpf(ex2(x * (2.0f * kLog2e)) + 1.0f);
 }
 
 // Position of key k (0 <= k < 16) inside its 16-key group of a V^T row: the
@@ -173,21 +174,78 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
   {
     const T *qr = (const T *)p.q + b * p.q_sb + (int64_t)(row_ok ? row_i : 0) * p.q_ss +
                   row_h * p.q_sh;
+    uint4 raw[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      raw[ks] = make_uint4(0, 0, 0, 0);
+      if (row_ok) raw[ks] = *(const uint4 *)(qr + ks * 16 + half * 8);
+    }
+    if (p.rot_q) {
+      // Rotary embedding of Q at position past_b + i, the same float32
+      // arithmetic and single rounding as the rotary pre-pass (pair (x1, x2)
+      // -> (fma(x1, c, -(x2 s)), fma(x2, c, x1 s))).  Split halves over the
+      // whole head: dims d and d + D/2 sit in chunks ks and ks + NKS/2 of the
+      // same lane; interleaved pairs (2k, 2k+1) sit inside one chunk.
+      const int pos = min(s.past + row_i, p.rot_max - 1);
+      const T *cs = (const T *)p.cos_cache + (int64_t)pos * (p.rot_dim / 2);
+      const T *sn = (const T *)p.sin_cache + (int64_t)pos * (p.rot_dim / 2);
+      auto rot1 = [](float x1, float x2, float c, float sv) { return __builtin_fmaf(x1, c, -__fmul_rn(x2, sv)); };
+      auto rot2 = [](float x1, float x2, float c, float sv) { return __builtin_fmaf(x2, c, __fmul_rn(x1, sv)); };
+      if (!p.rot_inter) {
+#pragma unroll
+        for (int ks = 0; ks < NKS / 2; ++ks) {
+          const int k0 = ks * 16 + half * 8;
+          const uint4 c8 = *(const uint4 *)(cs + k0), s8 = *(const uint4 *)(sn + k0);
+          const uint32_t *a = (const uint32_t *)&raw[ks], *bb = (const uint32_t *)&raw[ks + NKS / 2];
+          const uint32_t *cw = (const uint32_t *)&c8, *sw = (const uint32_t *)&s8;
+          uint4 oa, ob;
+          uint32_t *oaw = (uint32_t *)&oa, *obw = (uint32_t *)&ob;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const float x1l = lo16<T>(a[w]), x1h = hi16<T>(a[w]);
+            const float x2l = lo16<T>(bb[w]), x2h = hi16<T>(bb[w]);
+            const float cl = lo16<T>(cw[w]), ch = hi16<T>(cw[w]);
+            const float sl_ = lo16<T>(sw[w]), sh_ = hi16<T>(sw[w]);
+            oaw[w] = pack2<T>(rot1(x1l, x2l, cl, sl_), rot1(x1h, x2h, ch, sh_));
+            obw[w] = pack2<T>(rot2(x1l, x2l, cl, sl_), rot2(x1h, x2h, ch, sh_));
+          }
+          raw[ks] = oa;
+          raw[ks + NKS / 2] = ob;
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const int d0 = ks * 16 + half * 8;
+          if (d0 < p.rot_dim) {
+            const uint2 c4 = *(const uint2 *)(cs + d0 / 2), s4 = *(const uint2 *)(sn + d0 / 2);
+            const uint32_t *a = (const uint32_t *)&raw[ks];
+            const float cv[4] = {lo16<T>(c4.x), hi16<T>(c4.x), lo16<T>(c4.y), hi16<T>(c4.y)};
+            const float sv[4] = {lo16<T>(s4.x), hi16<T>(s4.x), lo16<T>(s4.y), hi16<T>(s4.y)};
+            uint4 o;
+            uint32_t *ow = (uint32_t *)&o;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              const float x1 = lo16<T>(a[w]), x2 = hi16<T>(a[w]);
+              ow[w] = pack2<T>(rot1(x1, x2, cv[w], sv[w]), rot2(x1, x2, cv[w], sv[w]));
+            }
+            raw[ks] = o;
+          }
+        }
+      }
+    }
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       const int d0 = ks * 16 + half * 8;
-      uint4 raw = make_uint4(0, 0, 0, 0);
-      if (row_ok) raw = *(const uint4 *)(qr + d0);
       if (p.proj_bias && row_ok) {
         const uint4 braw = *(const uint4 *)((const T *)p.proj_bias + row_h * D + d0);
-        const uint32_t *w = (const uint32_t *)&raw, *bw = (const uint32_t *)&braw;
+        const uint32_t *w = (const uint32_t *)&raw[ks], *bw = (const uint32_t *)&braw;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           qreg[ks][2 * e] = (T)(lo16<T>(w[e]) + lo16<T>(bw[e]));
           qreg[ks][2 * e + 1] = (T)(hi16<T>(w[e]) + hi16<T>(bw[e]));
         }
       } else {
-        qreg[ks] = __builtin_bit_cast(vec8, raw);
+        qreg[ks] = __builtin_bit_cast(vec8, raw[ks]);
       }
     }
   }
@@ -310,8 +368,11 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
 
   const float sl = p.scale * kLog2e;
   const bool scale_pos = p.scale > 0.f;
+  // softcap in the log2 domain: c tanh(u) = c - 2c / (e^{2u} + 1) with
+  // u = (s scale + bias) / c; e^{2u} = 2^(s cap_a + bias cap_b)
   const float inv_cap = SOFTCAP ? 1.0f / p.softcap : 0.f;
   const float cap_l2 = p.softcap * kLog2e;
+  const float cap_b = 2.0f * kLog2e * inv_cap, cap_a = p.scale * cap_b;
   const float mfv_l2 = p.mfv * kLog2e;
   const float mfv_raw = p.mfv / p.scale;  // the same offset before the scale (scale > 0)
   const T *bias_row = BIAS ? (const T *)p.bias + b * p.bias_sb + row_h * p.bias_sh +
@@ -413,7 +474,12 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             float t;
-            if (SOFTCAP) t = cap_l2 * tanh_e((sacc[kb][4 * q4 + e] * p.scale + bv[e]) * inv_cap);
+            if (SOFTCAP) {
+              const float x2 = BIAS ? __builtin_fmaf(sacc[kb][4 * q4 + e], cap_a, bv[e] * cap_b)
+                                    : sacc[kb][4 * q4 + e] * cap_a;
+              // saturates to +-c without NaN (rcp of +inf is 0)
+              t = __builtin_fmaf(__builtin_amdgcn_rcpf(ex2(x2) + 1.0f), -2.0f * cap_l2, cap_l2);
+            }
             else t = (sacc[kb][4 * q4 + e] * p.scale + bv[e]) * kLog2e;
             // a false mask element excludes the key after the score pipeline
             sacc[kb][4 * q4 + e] = ((mw >> (8 * e)) & 0xffu) ? t : kNegInf;
@@ -598,6 +664,17 @@ hipError_t launch_td(const Params &p, const FPlan &pl, hipStream_t st) {
 }
 
 }  // namespace
+
+// Whether the prefill kernel can rotate Q itself (do_rotary): split halves
+// over the whole head, or interleaved pairs over a multiple of 8 dims, with
+// cos/sin rows aligned for 16-byte (8-byte) loads.
+bool flash_rotates_q(const Params &p) {
+  if (p.op != OP_GQA || !p.cos_cache || !p.sin_cache || p.rot_dim <= 0) return false;
+  const uintptr_t al = p.rot_inter ? 7 : 15;
+  if ((((uintptr_t)p.cos_cache | (uintptr_t)p.sin_cache) & al) != 0) return false;
+  if (p.rot_inter) return p.rot_dim % 8 == 0 && (p.rot_dim / 2) % 4 == 0;
+  return p.rot_dim == p.D && (p.rot_dim / 2) % 8 == 0;
+}
 
 // Whether the prefill kernel writes the present rows of the new keys itself.
 bool flash_fuses_present(const Params &p) {

@@ -47,6 +47,7 @@ struct Params {
   // rotary embedding (used by the rotary pre-pass only)
   const void *cos_cache, *sin_cache;
   int rot_dim, rot_inter, rot_max;
+  int rot_q;  // the prefill kernel rotates Q as it loads it (the pre-pass skips Q)
 };
 
 // Per-batch sequence bookkeeping (integer; read once per workgroup).

@@ -9,7 +9,8 @@
 //   * the Hq query heads are rotated into Y (same (B, S, Hq*D) layout as Q);
 //     the attention kernels then read Q from Y, and each workgroup reads all
 //     of its Q rows before it writes any Y row, or (split paths) Y is written
-//     by a later kernel;
+//     by a later kernel.  With rot_q the prefill kernel rotates Q itself as
+//     it loads it, with the same arithmetic, and this pass skips Q;
 //   * the Hkv new key heads are rotated into present_k[b, g, past_b + i];
 //   * the new value heads are copied (bits) into present_v[b, g, past_b + i].
 // The attention kernels then take every key from present.
@@ -147,7 +148,7 @@ __global__ __launch_bounds__(kThreads) void rope_vec_kernel(Params p) {
   if (j >= p.T) return;
   const int pos = j < p.rot_max ? j : p.rot_max - 1;
   const int nt = vec_tasks<T>(p), vt = p.Dv / 8;
-  const int nq = p.Hq * nt, nk = p.Hkv * nt, nv = p.Hkv * vt;
+  const int nq = p.rot_q ? 0 : p.Hq * nt, nk = p.Hkv * nt, nv = p.Hkv * vt;
   const T *qrow = (const T *)p.q + b * p.q_sb + (int64_t)i * p.q_ss;
   T *yrow = (T *)p.y + b * p.y_sb + (int64_t)i * p.y_ss;
   for (int t = threadIdx.x; t < nq + nk + nv; t += kThreads) {
@@ -178,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(Params p) {
   const int j = s.past + i;  // absolute position of query i and of new key i
   if (j >= p.T) return;
   const int pos = j < p.rot_max ? j : p.rot_max - 1;
-  const int nq = p.Hq * p.D, nk = p.Hkv * p.D, nv = p.Hkv * p.Dv;
+  const int nq = p.rot_q ? 0 : p.Hq * p.D, nk = p.Hkv * p.D, nv = p.Hkv * p.Dv;
   const T *qrow = (const T *)p.q + b * p.q_sb + (int64_t)i * p.q_ss;
   T *yrow = (T *)p.y + b * p.y_sb + (int64_t)i * p.y_ss;
   for (int t = threadIdx.x; t < nq + nk + nv; t += kThreads) {
