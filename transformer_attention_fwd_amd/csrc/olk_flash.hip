@@ -23,7 +23,7 @@
 //   are conflict-free, and 16-byte chunks are XOR-swizzled by (row / 32) to
 //   spread the transposing writes; that key is uniform across each read
 //   instruction, so reads keep immediate offsets.
-// * Keys advance in tiles of 32 (head size 128) or 64 (head size 64).
+// * Keys advance in tiles of 64.
 // * K/V tiles are double-buffered in LDS, one barrier per tile; the next
 //   tile's global loads are in flight while the current tile computes.
 // * Online softmax in the exp2 domain, the scale folded into the exponent's
