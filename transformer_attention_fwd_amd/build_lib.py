@@ -57,7 +57,9 @@ def build(verbose: bool = False) -> str:
     if failed:
         raise RuntimeError("hipcc failed on: " + ", ".join(failed))
     tmp = LIB + ".tmp%d" % os.getpid()
-    subprocess.run([hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp],
+    # --no-undefined: a kernel the host pass dropped (its launch stub missing)
+    # fails here instead of when the library is loaded
+    subprocess.run([hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-Wl,--no-undefined", *objs, "-o", tmp],
                    check=True)
     os.replace(tmp, LIB)
     return LIB

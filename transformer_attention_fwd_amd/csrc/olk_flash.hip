@@ -16,13 +16,13 @@
 //   accumulator layout a lane owns one row slot and half of a tile's keys, so
 //   the softmax max/sum are in-lane plus one exchange with lane ^ 32, and P^T
 //   is already the B operand of the PV MFMA.
-// * K is staged row-major; V is staged transposed (V^T, key-major rows per head
-//   dimension) by a 4x4 register transpose, so every MFMA operand is one
-//   ds_read_b128.  The key order inside each 16-key group of V^T follows the
-//   MFMA's k order of P^T.  Rows are padded by 16 bytes so the operand reads
-//   are conflict-free, and 16-byte chunks are XOR-swizzled by (row / 32) to
-//   spread the transposing writes; that key is uniform across each read
-//   instruction, so reads keep immediate offsets.
+// * K and V tiles go from memory straight into LDS (global_load_lds_dwordx4:
+//   16 bytes per lane, no staging registers), unpadded rows with the 16-byte
+//   chunks of each row XOR-swizzled by a function of the row, one function
+//   for K (the QK^T operand reads 16 rows at one chunk per 16 lanes) and one
+//   for V.  The V^T operand of PV is read with ds_read_b64_tr_b16 from the
+//   row-major V tile: each transposed read hands a lane 4 consecutive keys of
+//   its head dimension, in the k order in which the accumulator supplies P^T.
 // * Keys advance in tiles of 64.
 // * K/V tiles are double-buffered in LDS, one barrier per tile; the next
 //   tile's global loads are in flight while the current tile computes.
@@ -30,9 +30,9 @@
 //   FMA; per-key masks only on boundary tiles, written as -inf in place.  O is rescaled only when a row's running max grows by more
 //   than 2^8 (the final division uses the same max, so the result is unchanged).
 // * GroupQueryAttention present rows of the new keys are stored by the
-//   workgroup whose queries sit at those positions: with causal masking from
-//   its last two LDS tiles after the loop, otherwise while the rows pass
-//   through registers.
+//   workgroup whose queries sit at those positions, copied from LDS: with
+//   causal masking from its last two tiles after the loop, otherwise while
+//   the owning tile is resident.
 #include "olk_internal.h"
 
 namespace olk {
@@ -75,6 +75,12 @@ template <> __device__ __forceinline__ float hi16<f16>(uint32_t w) {
 }
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 16 bytes from global memory straight into LDS: lane l's bytes land at
+// lds + 16 l (the LDS address is the same for every lane of the instruction)
+__device__ __forceinline__ void load_lds16(const void *g, void *lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
 
 // two floats rounded (RNE) to the element type, packed low / high
 template <typename T> __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
@@ -123,11 +129,9 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
   constexpr int NST = BN / 16;          // 16-key PV steps per tile
   constexpr int NKS = D / 16;           // QK^T k-steps
   constexpr int NDB = D / 32;           // 32-wide output blocks
-  constexpr int KST = D + 8;            // K row stride (elements)
-  constexpr int VST = BN + 8;           // V^T row stride (elements)
-  constexpr int NCH_V = BN / 8;         // 16-byte chunks per V^T row
-  __shared__ __attribute__((aligned(16))) T klds[2][BN * KST];
-  __shared__ __attribute__((aligned(16))) T vlds[2][D * VST];
+  constexpr int RB = D * 2;             // bytes per K / V row in LDS (unpadded)
+  __shared__ __attribute__((aligned(16))) T klds[2][BN * D];
+  __shared__ __attribute__((aligned(16))) T vlds[2][BN * D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
@@ -159,7 +163,8 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
   if (BM == 1 || (MASK && p.bias)) hi = min(hi, p.bias_cols);
   if (MASK) hi = min(hi, p.mask_cols);
   const int lo = p.window > 0 ? max(0, pos_min - p.window + 1) : 0;
-  const int kt0 = lo / BN, kt1 = (hi + BN - 1) / BN;
+  // no key tile at all when no key is allowed (every row then outputs 0)
+  const int kt0 = lo / BN, kt1 = hi > lo ? (hi + BN - 1) / BN : kt0;
 
   // ---- this lane's row slot ----
   const int slot = wave * 32 + col;
@@ -255,25 +260,29 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
   // tile until the next tile's prefetch loads have landed as well.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
-  // ---- staging: thread owns key quad q (4 keys) x 16-byte chunk c; at head
-  // size 64 the upper half of the workgroup has no quad to stage ----
-  // ---- staging.  LDS writes are bank-conflict free on gfx950 when 16 lanes
-  // cover one contiguous row, so K and V use different lane maps:
-  //  K: lane -> 16-byte chunk lane % CH of row lane / CH; the workgroup covers
-  //     4 * RPI rows per pass, NUK passes per tile.
-  //  V: lane -> key quad vq = lane % 16 (4 keys) x chunk vc = 4 * wave + lane / 16;
-  //     after the 4x4 register transpose, 16 lanes write one full V^T row.
-  //     At head size 64 only waves 0-1 stage V. ----
-  constexpr int RPI = 64 / CH;              // K rows per wavefront pass
-  constexpr int NUK = BN / (4 * RPI);       // K passes per tile
-  const int kchunk = lane % CH;
-  const int krow0 = wave * RPI + lane / CH;  // row of pass 0; pass u adds 4 * RPI * u
-  const int vq = lane & 15, vc = 4 * wave + (lane >> 4);
-  const bool vstager = vc < CH;
-  const int vslot = 16 * (vq >> 2) + 4 * quad_slot(vq & 3);  // V^T slot of the quad's key 0
-  // V^T column offset of the quad: chunk XOR-swizzled by (row / 32) = vc / 4,
-  // which is the same for all 8 rows a thread writes
-  const int vchunk_off = (((vslot >> 3) ^ (2 * ((vc >> 2) & (NCH_V / 2 - 1)))) * 8) + (vslot & 7);
+  // ---- staging: K and V tiles go from memory straight into LDS ----
+  // A direct load writes 16 bytes per lane at consecutive LDS addresses (1 KB
+  // per instruction = RPL rows); each lane picks which 16-byte chunk of its
+  // row it loads, so a row's chunks are stored XOR-swizzled:
+  //  K: slot p of row r holds chunk p ^ fk(r); the QK^T operand reads (16
+  //     rows at one chunk per 16 lanes) then hit 16 different bank groups;
+  //  V: slot p of row r holds chunk p ^ fv(r); the transposed PV operand reads
+  //     (4 rows x 64 bytes per 32 lanes) hit 64 different banks.
+  // Keys outside [lo, hi) load the nearest row inside it instead (caller data,
+  // finite; their scores are masked, so their P is exactly 0).
+  constexpr int RPL = 1024 / RB;        // rows per load instruction
+  constexpr int NLD = BN / (4 * RPL);   // load instructions per wavefront per tile and matrix
+  auto fk = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
+  auto fv = [](int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); };
+  int lrow[NLD];
+  uint32_t kcb[NLD], vcb[NLD];  // byte offset of the loaded chunk inside its row
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int r = (wave * NLD + i) * RPL + lane / CH, pch = lane % CH;
+    lrow[i] = r;
+    kcb[i] = 16u * (uint32_t)(pch ^ fk(r));
+    vcb[i] = 16u * (uint32_t)(pch ^ fv(r));
+  }
   const T *kpast = (const T *)p.past_k + ((int64_t)b * p.Hkv + g) * p.past_rows * D;
   const T *vpast = (const T *)p.past_v + ((int64_t)b * p.Hkv + g) * p.past_rows * D;
   const T *knew = (const T *)p.k + b * p.k_sb + g * p.k_sh;
@@ -282,89 +291,70 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
   const int own_lo = s.past + i0, own_hi = s.past + i_last + 1;
   // Causal: the owned rows are the last keys the loop stages (at most BN of
   // them), so both LDS buffers still hold them afterwards and present is
-  // written once the loop is done; stores inside the loop would make every
-  // later wait for tile loads also wait for the store acknowledgements.
+  // written once the loop is done; otherwise each owned row is copied from
+  // LDS while its tile is resident.
   const bool fuse_end = fuse && p.causal && pl.QW <= BN;
   const bool fuse_loop = fuse && !fuse_end;
   T *pres_k = (T *)p.present_k + ((int64_t)b * p.Hkv + g) * p.T * D;
   T *pres_v = (T *)p.present_v + ((int64_t)b * p.Hkv + g) * p.T * D;
 
-  uint4 rk[NUK], rv[4];  // staging registers: K of tile t+2, V of tile t+1
-
-  // Row j of K or V: the past buffer below past_b, the new input above; keys
-  // outside [lo, hi) read as zeros, never NaN.
-  auto load_row = [&](int j, const T *pastp, const T *newp, int64_t new_ss, int chunk) __attribute__((always_inline)) {
-    const T *src = j >= s.src ? newp + (int64_t)(j - s.src) * new_ss : pastp + (int64_t)j * D;
-    return j >= lo && j < hi ? *(const uint4 *)(src + chunk * 8) : make_uint4(0, 0, 0, 0);
-  };
-  // Whole tiles inside one source use a uniform base plus 32-bit lane offsets.
-  // first row r0 and row step of the NU rows a thread loads
-  auto load_rows = [&](int kt, const T *pastp, const T *newp, int64_t new_ss, int r0, int rstep,
-                       int chunk, auto &buf) __attribute__((always_inline)) {
-    constexpr int NU = sizeof(buf) / sizeof(buf[0]);
+  auto issue_loads = [&](int kt, int buf) __attribute__((always_inline)) {
     const int j0 = kt * BN;
+    char *kl = (char *)klds[buf] + wave * NLD * 1024;
+    char *vl = (char *)vlds[buf] + wave * NLD * 1024;
     const bool full = j0 >= lo && j0 + BN <= hi;
-    if (full && j0 >= s.src) {
-      const char *base = (const char *)(newp + (int64_t)(j0 - s.src) * new_ss);
-      const uint32_t rs = (uint32_t)new_ss * (uint32_t)sizeof(T);
-      const uint32_t off = (uint32_t)r0 * rs + (uint32_t)chunk * 16u;
+    if (full && (j0 >= s.src || j0 + BN <= s.src)) {
+      // the whole tile from one source: uniform base plus 32-bit lane offsets
+      const bool nw = j0 >= s.src;
+      const char *kb = (const char *)(nw ? knew + (int64_t)(j0 - s.src) * p.k_ss : kpast + (int64_t)j0 * D);
+      const char *vb = (const char *)(nw ? vnew + (int64_t)(j0 - s.src) * p.v_ss : vpast + (int64_t)j0 * D);
+      const uint32_t krs = (uint32_t)(nw ? p.k_ss : D) * (uint32_t)sizeof(T);
+      const uint32_t vrs = (uint32_t)(nw ? p.v_ss : D) * (uint32_t)sizeof(T);
 #pragma unroll
-      for (int u = 0; u < NU; ++u) buf[u] = *(const uint4 *)(base + off + u * rstep * rs);
-    } else if (full && j0 + BN <= s.src) {
-      const char *base = (const char *)(pastp + (int64_t)j0 * D);
-      const uint32_t rs = D * (uint32_t)sizeof(T);
-      const uint32_t off = (uint32_t)r0 * rs + (uint32_t)chunk * 16u;
-#pragma unroll
-      for (int u = 0; u < NU; ++u) buf[u] = *(const uint4 *)(base + off + u * rstep * rs);
+      for (int i = 0; i < NLD; ++i) {
+        load_lds16(kb + (uint32_t)lrow[i] * krs + kcb[i], kl + i * 1024);
+        load_lds16(vb + (uint32_t)lrow[i] * vrs + vcb[i], vl + i * 1024);
+      }
     } else {
 #pragma unroll
-      for (int u = 0; u < NU; ++u) buf[u] = load_row(j0 + r0 + u * rstep, pastp, newp, new_ss, chunk);
-    }
-  };
-  auto load_k = [&](int kt) __attribute__((always_inline)) {
-    load_rows(kt, kpast, knew, p.k_ss, krow0, 4 * RPI, kchunk, rk);
-  };
-  auto load_v = [&](int kt) __attribute__((always_inline)) {
-    if (vstager) load_rows(kt, vpast, vnew, p.v_ss, 4 * vq, 1, vc, rv);
-  };
-  auto store_k = [&](int kt, int buf) __attribute__((always_inline)) {
-    T *kl = klds[buf];
-#pragma unroll
-    for (int u = 0; u < NUK; ++u) *(uint4 *)&kl[(krow0 + 4 * RPI * u) * KST + kchunk * 8] = rk[u];
-    if (fuse_loop && kt * BN < own_hi && kt * BN + BN > own_lo) {
-#pragma unroll
-      for (int u = 0; u < NUK; ++u) {
-        const int j = kt * BN + krow0 + 4 * RPI * u;
-        if (j >= own_lo && j < own_hi)
-          *(uint4 *)((char *)pres_k + ((uint32_t)j * D + (uint32_t)kchunk * 8u) * sizeof(T)) = rk[u];
+      for (int i = 0; i < NLD; ++i) {
+        const int j = j0 + lrow[i];
+        const int jj = j < lo ? lo : (j >= hi ? hi - 1 : j);
+        const bool nw = jj >= s.src;
+        const char *kr = (const char *)(nw ? knew + (int64_t)(jj - s.src) * p.k_ss : kpast + (int64_t)jj * D);
+        const char *vr = (const char *)(nw ? vnew + (int64_t)(jj - s.src) * p.v_ss : vpast + (int64_t)jj * D);
+        load_lds16(kr + kcb[i], kl + i * 1024);
+        load_lds16(vr + vcb[i], vl + i * 1024);
       }
     }
   };
-  // 4 keys x 8 dims -> 8 dims x 4 keys (V^T), 8 bytes per dim row
-  auto store_v = [&](int kt, int buf) __attribute__((always_inline)) {
-    if (!vstager) return;
-    T *vl = vlds[buf];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t r0 = ((const uint32_t *)&rv[0])[w], r1 = ((const uint32_t *)&rv[1])[w];
-      const uint32_t r2 = ((const uint32_t *)&rv[2])[w], r3 = ((const uint32_t *)&rv[3])[w];
-#pragma unroll
-      for (int hl = 0; hl < 2; ++hl) {
-        const uint32_t sel = hl ? 0x07060302u : 0x05040100u;
-        const uint2 kk = make_uint2(__builtin_amdgcn_perm(r1, r0, sel), __builtin_amdgcn_perm(r3, r2, sel));
-        const int d = vc * 8 + 2 * w + hl;
-        *(uint2 *)&vl[d * VST + vchunk_off] = kk;
-      }
-    }
-    if (fuse_loop && kt * BN < own_hi && kt * BN + BN > own_lo) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int j = kt * BN + 4 * vq + u;
-        if (j >= own_lo && j < own_hi)
-          *(uint4 *)((char *)pres_v + ((uint32_t)j * D + (uint32_t)vc * 8u) * sizeof(T)) = rv[u];
-      }
+  // present rows of the owned keys of tile kt (resident in buffer `buf`)
+  auto copy_owned = [&](int kt, int buf) __attribute__((always_inline)) {
+    const int j0 = kt * BN;
+    const int a = max(own_lo, j0), e = min(own_hi, j0 + BN);
+    for (int t = tid; t < (e - a) * CH; t += kThreads) {
+      const int j = a + t / CH, cc = t % CH, r = j - j0;
+      *(uint4 *)((char *)pres_k + ((uint32_t)j * D + cc * 8u) * sizeof(T)) =
+          *(const uint4 *)((const char *)klds[buf] + r * RB + 16 * (cc ^ fk(r)));
+      *(uint4 *)((char *)pres_v + ((uint32_t)j * D + cc * 8u) * sizeof(T)) =
+          *(const uint4 *)((const char *)vlds[buf] + r * RB + 16 * (cc ^ fv(r)));
     }
   };
+  // K operand offsets inside a tile (row kb * 32 + col; fk does not depend on kb)
+  uint32_t koff[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) koff[ks] = (uint32_t)(col * RB + 16 * ((2 * ks + half) ^ fk(col)));
+  // V^T operand (transposed reads): lane (group g4 = lane / 16, j = lane % 16)
+  // addresses row 4 half + j / 4 (+ 16 st + 8 rd), dims 32 db + 16 (g4 & 1) + 4 (j & 3);
+  // the read hands lane l dim 32 db + (l & 31) of 4 consecutive keys
+  uint32_t voff[NDB];
+  {
+    const int j = lane & 15, g4 = lane >> 4, q = j >> 2;
+    const int t2 = 2 * (g4 & 1) + ((j & 3) >> 1);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      voff[db] = (uint32_t)((4 * half + q) * RB + 16 * ((4 * db + t2) ^ fv(4 * half + q)) + 8 * (j & 1));
+  }
 
   const float sl = p.scale * kLog2e;
   const bool scale_pos = p.scale > 0.f;
@@ -422,13 +412,13 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
 
   // S^T of one tile: KB blocks of 32 keys
   auto qk = [&](int buf, f32x16 (&sacc)[KB]) {
-    const T *kl = klds[buf];
+    const char *kl = (const char *)klds[buf];
     const f32x16 zero = {};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const vec8 a = *(const vec8 *)&kl[(kb * 32 + col) * KST + ks * 16 + half * 8];
+        const vec8 a = *(const vec8 *)(kl + kb * 32 * RB + koff[ks]);
         sacc[kb] = mma(a, qreg[ks], ks == 0 ? zero : sacc[kb]);
       }
     }
@@ -449,7 +439,7 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
   // masked and unmasked tiles share one body.
   auto softmax_pv = [&](int kt, int buf, f32x16 (&sacc)[KB], bool masked) {
     constexpr bool GENERAL = BIAS || SOFTCAP;
-    const T *vl = vlds[buf];
+    const char *vl = (const char *)vlds[buf];
     const int j0 = kt * BN;
     auto allowed = [&](int j) {
       bool ok = j >= lo && j < hi;
@@ -532,9 +522,14 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
       }
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const int d = db * 32 + col;
-        const int swz = 2 * (db & (NCH_V / 2 - 1));  // uniform across the instruction
-        const vec8 a = *(const vec8 *)&vl[d * VST + (((2 * st + half) ^ swz) * 8)];
+        // keys 16 st + 4 half + {0..3} and 16 st + 8 + 4 half + {0..3} of dim 32 db + col
+        typedef short s16x4 __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) s16x4 *tr_ptr;
+        const uint2 lo = __builtin_bit_cast(
+            uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((tr_ptr)(vl + 16 * st * RB + voff[db])));
+        const uint2 hi = __builtin_bit_cast(
+            uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((tr_ptr)(vl + (16 * st + 8) * RB + voff[db])));
+        const vec8 a = __builtin_bit_cast(vec8, make_uint4(lo.x, lo.y, hi.x, hi.y));
         o[db] = mma(a, pb, o[db]);
       }
     }
@@ -542,24 +537,24 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
   };
 
   if (kt0 < kt1) {
-    load_k(kt0);
-    load_v(kt0);
+    issue_loads(kt0, 0);
     if (BPRE) load_bias(kt0, bcur);
-    store_k(kt0, 0);
-    store_v(kt0, 0);
   }
+  // direct loads write LDS behind the compiler's back: wait for them before
+  // the barrier that publishes the tile
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
-  // The next tile's loads go out first and land in the other LDS buffer
-  // after this tile's compute, so a full tile (and the other workgroup on the
-  // CU) covers their latency.
+  // The next tile's loads go out first and land in the other LDS buffer while
+  // this tile computes (a full tile and the other workgroup on the CU cover
+  // their latency).
   for (int kt = kt0; kt < kt1; ++kt) {
     const int buf = (kt - kt0) & 1;
     const bool more = kt + 1 < kt1;
     if (more) {
-      load_k(kt + 1);
-      load_v(kt + 1);
+      issue_loads(kt + 1, buf ^ 1);
       if (BPRE) load_bias(kt + 1, bnext);
     }
+    if (fuse_loop && kt * BN < own_hi && kt * BN + BN > own_lo) copy_owned(kt, buf);
     if (wave_active) {
       f32x16 sacc[KB];
       qk(buf, sacc);
@@ -569,43 +564,20 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
                              j0 < lo || (p.pad_add && j0 + BN > s.pad);
       softmax_pv(kt, buf, sacc, need_mask);
     }
-    if (more) {
-      store_k(kt + 1, buf ^ 1);
-      store_v(kt + 1, buf ^ 1);
-      if (BPRE) {
+    if (more && BPRE) {
 #pragma unroll
-        for (int kb = 0; kb < (BPRE ? KB : 1); ++kb)
+      for (int kb = 0; kb < (BPRE ? KB : 1); ++kb)
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) bcur[kb][q4] = bnext[kb][q4];
-      }
+        for (int q4 = 0; q4 < 4; ++q4) bcur[kb][q4] = bnext[kb][q4];
     }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
   }
 
   // ---- present rows of the owned keys, from the last two LDS tiles ----
   if (fuse_end && kt0 < kt1) {
-    const int n_own = own_hi - own_lo;
-    for (int t = tid; t < n_own * CH; t += kThreads) {
-      const int j = own_lo + t / CH, cc = t % CH;
-      const int kt = j / BN, bi = (kt - kt0) & 1, r = j - kt * BN;
-      *(uint4 *)((char *)pres_k + ((uint32_t)j * D + cc * 8u) * sizeof(T)) =
-          *(const uint4 *)&klds[bi][r * KST + cc * 8];
-      // V row r from V^T: element d sits at its row's swizzled key slot
-      const int slot = 16 * (r >> 4) + 4 * quad_slot((r >> 2) & 3) + (r & 3);
-      uint16_t e8[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = cc * 8 + e;
-        const int chunk = (slot >> 3) ^ (2 * ((d >> 5) & (NCH_V / 2 - 1)));
-        e8[e] = __builtin_bit_cast(uint16_t, vlds[bi][d * VST + chunk * 8 + (slot & 7)]);
-      }
-      uint4 row;
-      row.x = e8[0] | ((uint32_t)e8[1] << 16);
-      row.y = e8[2] | ((uint32_t)e8[3] << 16);
-      row.z = e8[4] | ((uint32_t)e8[5] << 16);
-      row.w = e8[6] | ((uint32_t)e8[7] << 16);
-      *(uint4 *)((char *)pres_v + ((uint32_t)j * D + cc * 8u) * sizeof(T)) = row;
-    }
+    const int kt_first = max(kt0, own_lo / BN);
+    for (int kt = kt_first; kt < kt1; ++kt) copy_owned(kt, (kt - kt0) & 1);
   }
 
   // ---- epilogue: combine halves, sink, normalise, store ----
