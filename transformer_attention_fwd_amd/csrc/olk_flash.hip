@@ -133,7 +133,8 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
   __shared__ __attribute__((aligned(16))) T klds[2][BN * D];
   __shared__ __attribute__((aligned(16))) T vlds[2][BN * D];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar LDS bases
   const int half = lane >> 5, col = lane & 31;
 
   // ---- workgroup -> (q tile, b, g, hg); late (heavy) query tiles first ----
@@ -274,14 +275,19 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
   constexpr int NLD = BN / (4 * RPL);   // load instructions per wavefront per tile and matrix
   auto fk = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
   auto fv = [](int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); };
+  // per lane: tile row and byte offsets inside a tile of new K/V rows
+  // (strides k_ss / v_ss), fixed for the kernel
   int lrow[NLD];
-  uint32_t kcb[NLD], vcb[NLD];  // byte offset of the loaded chunk inside its row
+  uint32_t kcb[NLD], vcb[NLD];        // byte offset of the loaded chunk inside its row
+  uint32_t kon[NLD], von[NLD];
 #pragma unroll
   for (int i = 0; i < NLD; ++i) {
     const int r = (wave * NLD + i) * RPL + lane / CH, pch = lane % CH;
     lrow[i] = r;
     kcb[i] = 16u * (uint32_t)(pch ^ fk(r));
     vcb[i] = 16u * (uint32_t)(pch ^ fv(r));
+    kon[i] = (uint32_t)r * (uint32_t)p.k_ss * (uint32_t)sizeof(T) + kcb[i];
+    von[i] = (uint32_t)r * (uint32_t)p.v_ss * (uint32_t)sizeof(T) + vcb[i];
   }
   const T *kpast = (const T *)p.past_k + ((int64_t)b * p.Hkv + g) * p.past_rows * D;
   const T *vpast = (const T *)p.past_v + ((int64_t)b * p.Hkv + g) * p.past_rows * D;
@@ -304,16 +310,25 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
     char *vl = (char *)vlds[buf] + wave * NLD * 1024;
     const bool full = j0 >= lo && j0 + BN <= hi;
     if (full && (j0 >= s.src || j0 + BN <= s.src)) {
-      // the whole tile from one source: uniform base plus 32-bit lane offsets
-      const bool nw = j0 >= s.src;
-      const char *kb = (const char *)(nw ? knew + (int64_t)(j0 - s.src) * p.k_ss : kpast + (int64_t)j0 * D);
-      const char *vb = (const char *)(nw ? vnew + (int64_t)(j0 - s.src) * p.v_ss : vpast + (int64_t)j0 * D);
-      const uint32_t krs = (uint32_t)(nw ? p.k_ss : D) * (uint32_t)sizeof(T);
-      const uint32_t vrs = (uint32_t)(nw ? p.v_ss : D) * (uint32_t)sizeof(T);
+      // the whole tile from one source: uniform base plus the fixed 32-bit
+      // lane offsets of that source
+      if (j0 >= s.src) {
+        const char *kb = (const char *)(knew + (int64_t)(j0 - s.src) * p.k_ss);
+        const char *vb = (const char *)(vnew + (int64_t)(j0 - s.src) * p.v_ss);
 #pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        load_lds16(kb + (uint32_t)lrow[i] * krs + kcb[i], kl + i * 1024);
-        load_lds16(vb + (uint32_t)lrow[i] * vrs + vcb[i], vl + i * 1024);
+        for (int i = 0; i < NLD; ++i) {
+          load_lds16(kb + kon[i], kl + i * 1024);
+          load_lds16(vb + von[i], vl + i * 1024);
+        }
+      } else {
+        const char *kb = (const char *)(kpast + (int64_t)j0 * D);
+        const char *vb = (const char *)(vpast + (int64_t)j0 * D);
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+          const uint32_t ro = (uint32_t)lrow[i] * (uint32_t)(D * sizeof(T));  // past rows are dense
+          load_lds16(kb + ro + kcb[i], kl + i * 1024);
+          load_lds16(vb + ro + vcb[i], vl + i * 1024);
+        }
       }
     } else {
 #pragma unroll
