@@ -173,6 +173,11 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
   const int row_h = g * p.G + hg * pl.GH + slot % pl.GH;
   const bool row_ok = row_i < p.S;
   const int row_pos = s.qoff + row_i;
+  // the keys this row slot may attend form one interval [a_lo, a_lo + a_w):
+  // the workgroup's range, cut by the causal and window limits of its position
+  const int a_lo = p.window > 0 ? max(lo, row_pos - p.window + 1) : lo;
+  const int a_hi = p.causal ? min(hi, row_pos + 1) : hi;
+  const uint32_t a_w = a_hi > a_lo ? (uint32_t)(a_hi - a_lo) : 0u;
   const bool wave_active = i0 + (wave * 32) / pl.GH < p.S;
 
   // ---- Q^T operand (B of S^T = K Q^T): slot col, d = 16 ks + 8 half + e ----
@@ -456,12 +461,6 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
     constexpr bool GENERAL = BIAS || SOFTCAP;
     const char *vl = (const char *)vlds[buf];
     const int j0 = kt * BN;
-    auto allowed = [&](int j) {
-      bool ok = j >= lo && j < hi;
-      if (p.causal && j > row_pos) ok = false;
-      if (p.window > 0 && j < row_pos - p.window + 1) ok = false;
-      return ok;
-    };
     if (GENERAL) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -492,15 +491,21 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
         }
     }
     if (masked) {
+      // key of element r of block kb: j0 + 4 half + kb 32 + 8 (r / 4) + r % 4
+      if (p.pad_add) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (j0 + 4 * half + kb * 32 + 8 * (r >> 2) + (r & 3) >= s.pad)
+              sacc[kb][r] += GENERAL ? mfv_l2 : mfv_raw;
+      }
+      const int jr = j0 + 4 * half - a_lo;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = j0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          float t = sacc[kb][r];
-          if (p.pad_add && j >= s.pad) t += GENERAL ? mfv_l2 : mfv_raw;
-          sacc[kb][r] = allowed(j) ? t : kNegInf;
-        }
+        for (int r = 0; r < 16; ++r)
+          sacc[kb][r] = (uint32_t)(jr + kb * 32 + 8 * (r >> 2) + (r & 3)) < a_w ? sacc[kb][r] : kNegInf;
     }
     float mx = kNegInf;
 #pragma unroll
