@@ -130,8 +130,18 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
   constexpr int NKS = D / 16;           // QK^T k-steps
   constexpr int NDB = D / 32;           // 32-wide output blocks
   constexpr int RB = D * 2;             // bytes per K / V row in LDS (unpadded)
-  __shared__ __attribute__((aligned(16))) T klds[2][BN * D];
-  __shared__ __attribute__((aligned(16))) T vlds[2][BN * D];
+  // Double buffers as four separate variables.  With the key loop unrolled by
+  // two (UNROLL2) each access names one of them, so the wait-count analysis
+  // can tell the loads landing in one buffer from the reads of the other and
+  // does not wait for the next tile's loads before the first read of this
+  // one.  The forms whose registers do not allow the unrolled body (head
+  // size 64 at three wavefronts per SIMD, BOOL mask with softcap) select the
+  // buffers at run time and keep that wait.
+  constexpr bool UNROLL2 = D == 128 && !(BM == 2 && SOFTCAP);
+  __shared__ __attribute__((aligned(16))) T klds0[BN * D];
+  __shared__ __attribute__((aligned(16))) T klds1[BN * D];
+  __shared__ __attribute__((aligned(16))) T vlds0[BN * D];
+  __shared__ __attribute__((aligned(16))) T vlds1[BN * D];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar LDS bases
@@ -309,10 +319,10 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
   T *pres_k = (T *)p.present_k + ((int64_t)b * p.Hkv + g) * p.T * D;
   T *pres_v = (T *)p.present_v + ((int64_t)b * p.Hkv + g) * p.T * D;
 
-  auto issue_loads = [&](int kt, int buf) __attribute__((always_inline)) {
+  auto issue_loads = [&](int kt, T *kdst, T *vdst) __attribute__((always_inline)) {
     const int j0 = kt * BN;
-    char *kl = (char *)klds[buf] + wave * NLD * 1024;
-    char *vl = (char *)vlds[buf] + wave * NLD * 1024;
+    char *kl = (char *)kdst + wave * NLD * 1024;
+    char *vl = (char *)vdst + wave * NLD * 1024;
     const bool full = j0 >= lo && j0 + BN <= hi;
     if (full && (j0 >= s.src || j0 + BN <= s.src)) {
       // the whole tile from one source: uniform base plus the fixed 32-bit
@@ -348,16 +358,16 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
       }
     }
   };
-  // present rows of the owned keys of tile kt (resident in buffer `buf`)
-  auto copy_owned = [&](int kt, int buf) __attribute__((always_inline)) {
+  // present rows of the owned keys of tile kt (resident in kbuf / vbuf)
+  auto copy_owned = [&](int kt, const T *kbuf, const T *vbuf) __attribute__((always_inline)) {
     const int j0 = kt * BN;
     const int a = max(own_lo, j0), e = min(own_hi, j0 + BN);
     for (int t = tid; t < (e - a) * CH; t += kThreads) {
       const int j = a + t / CH, cc = t % CH, r = j - j0;
       *(uint4 *)((char *)pres_k + ((uint32_t)j * D + cc * 8u) * sizeof(T)) =
-          *(const uint4 *)((const char *)klds[buf] + r * RB + 16 * (cc ^ fk(r)));
+          *(const uint4 *)((const char *)kbuf + r * RB + 16 * (cc ^ fk(r)));
       *(uint4 *)((char *)pres_v + ((uint32_t)j * D + cc * 8u) * sizeof(T)) =
-          *(const uint4 *)((const char *)vlds[buf] + r * RB + 16 * (cc ^ fv(r)));
+          *(const uint4 *)((const char *)vbuf + r * RB + 16 * (cc ^ fv(r)));
     }
   };
   // K operand offsets inside a tile (row kb * 32 + col; fk does not depend on kb)
@@ -431,8 +441,8 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
   float m = kNegInf, l = 0.f;
 
   // S^T of one tile: KB blocks of 32 keys
-  auto qk = [&](int buf, f32x16 (&sacc)[KB]) {
-    const char *kl = (const char *)klds[buf];
+  auto qk = [&](const T *kbuf, f32x16 (&sacc)[KB]) __attribute__((always_inline)) {
+    const char *kl = (const char *)kbuf;
     const f32x16 zero = {};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
@@ -457,9 +467,9 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
   // are rewritten into the log2 domain; otherwise they stay raw (scale > 0,
   // folded into the exponent's FMA) and masking only writes -inf in place, so
   // masked and unmasked tiles share one body.
-  auto softmax_pv = [&](int kt, int buf, f32x16 (&sacc)[KB], bool masked) {
+  auto softmax_pv = [&](int kt, const T *vbuf, f32x16 (&sacc)[KB], bool masked) __attribute__((always_inline)) {
     constexpr bool GENERAL = BIAS || SOFTCAP;
-    const char *vl = (const char *)vlds[buf];
+    const char *vl = (const char *)vbuf;
     const int j0 = kt * BN;
     if (GENERAL) {
 #pragma unroll
@@ -493,12 +503,14 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
     if (masked) {
       // key of element r of block kb: j0 + 4 half + kb 32 + 8 (r / 4) + r % 4
       if (p.pad_add) {
+        // keys from s.pad on get the filter value added: a select per score
+        const int jp = j0 + 4 * half - s.pad;
+        const float add = GENERAL ? mfv_l2 : mfv_raw;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (j0 + 4 * half + kb * 32 + 8 * (r >> 2) + (r & 3) >= s.pad)
-              sacc[kb][r] += GENERAL ? mfv_l2 : mfv_raw;
+            sacc[kb][r] += jp + kb * 32 + 8 * (r >> 2) + (r & 3) >= 0 ? add : 0.f;
       }
       const int jr = j0 + 4 * half - a_lo;
 #pragma unroll
@@ -557,32 +569,31 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
   };
 
   if (kt0 < kt1) {
-    issue_loads(kt0, 0);
+    issue_loads(kt0, klds0, vlds0);
     if (BPRE) load_bias(kt0, bcur);
   }
   // direct loads write LDS behind the compiler's back: wait for them before
   // the barrier that publishes the tile
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
-  // The next tile's loads go out first and land in the other LDS buffer while
-  // this tile computes (a full tile and the other workgroup on the CU cover
-  // their latency).
-  for (int kt = kt0; kt < kt1; ++kt) {
-    const int buf = (kt - kt0) & 1;
+  // One tile: the next tile's loads go out first and land in the other
+  // buffers while this tile computes (a full tile and the other workgroup on
+  // the CU cover their latency).
+  auto tile = [&](int kt, const T *kc, const T *vc, T *kn, T *vn) __attribute__((always_inline)) {
     const bool more = kt + 1 < kt1;
     if (more) {
-      issue_loads(kt + 1, buf ^ 1);
+      issue_loads(kt + 1, kn, vn);
       if (BPRE) load_bias(kt + 1, bnext);
     }
-    if (fuse_loop && kt * BN < own_hi && kt * BN + BN > own_lo) copy_owned(kt, buf);
+    if (fuse_loop && kt * BN < own_hi && kt * BN + BN > own_lo) copy_owned(kt, kc, vc);
     if (wave_active) {
       f32x16 sacc[KB];
-      qk(buf, sacc);
+      qk(kc, sacc);
       const int j0 = kt * BN;
       const bool need_mask = (p.causal && j0 + BN - 1 > pos_min) ||
                              (p.window > 0 && j0 < pos_max - p.window + 1) || j0 + BN > hi ||
                              j0 < lo || (p.pad_add && j0 + BN > s.pad);
-      softmax_pv(kt, buf, sacc, need_mask);
+      softmax_pv(kt, vc, sacc, need_mask);
     }
     if (more && BPRE) {
 #pragma unroll
@@ -592,12 +603,26 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
+  };
+  if constexpr (UNROLL2) {
+    for (int kt = kt0; kt < kt1; kt += 2) {
+      tile(kt, klds0, vlds0, klds1, vlds1);
+      if (kt + 1 < kt1) tile(kt + 1, klds1, vlds1, klds0, vlds0);
+    }
+  } else {
+    for (int kt = kt0; kt < kt1; ++kt) {
+      const bool odd = (kt - kt0) & 1;
+      tile(kt, odd ? klds1 : klds0, odd ? vlds1 : vlds0, odd ? klds0 : klds1, odd ? vlds0 : vlds1);
+    }
   }
 
   // ---- present rows of the owned keys, from the last two LDS tiles ----
   if (fuse_end && kt0 < kt1) {
     const int kt_first = max(kt0, own_lo / BN);
-    for (int kt = kt_first; kt < kt1; ++kt) copy_owned(kt, (kt - kt0) & 1);
+    for (int kt = kt_first; kt < kt1; ++kt) {
+      const bool odd = (kt - kt0) & 1;
+      copy_owned(kt, odd ? klds1 : klds0, odd ? vlds1 : vlds0);
+    }
   }
 
   // ---- epilogue: combine halves, sink, normalise, store ----
