@@ -461,10 +461,13 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
   auto qk = [&](const T *kbuf, f32x16 (&sacc)[KB]) __attribute__((always_inline)) {
     const char *kl = (const char *)kbuf;
     const f32x16 zero = {};
+    // block-major: the first 32 keys' scores are final while the second
+    // block's MFMAs run, so their row max can start (each chain keeps its
+    // k order, so the sums are the same)
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
+    for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
+      for (int ks = 0; ks < NKS; ++ks) {
         const vec8 a = *(const vec8 *)(kl + kb * 32 * RB + koff[ks]);
         sacc[kb] = mma(a, qreg[ks], ks == 0 ? zero : sacc[kb]);
       }
@@ -604,12 +607,12 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
     }
     if (fuse_loop && kt * BN < own_hi && kt * BN + BN > own_lo) copy_owned(kt, kc, vc);
     if (wave_active) {
-      f32x16 sacc[KB];
-      qk(kc, sacc);
       const int j0 = kt * BN;
       const bool need_mask = (p.causal && j0 + BN - 1 > pos_min) ||
                              (p.window > 0 && j0 < pos_max - p.window + 1) || j0 + BN > hi ||
                              j0 < lo || (p.pad_add && j0 + BN > s.pad);
+      f32x16 sacc[KB];
+      qk(kc, sacc);
       softmax_pv(kt, vc, sacc, need_mask);
     }
     if (more && BPRE) {
