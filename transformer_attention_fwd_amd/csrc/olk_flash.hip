@@ -416,10 +416,12 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
                                  (int64_t)(row_ok ? row_i : 0) * p.bias_si
                            : nullptr;
 
-  // 4 bias values of keys jb..jb+3 as raw 16-bit pairs (zeros past the bias columns)
-  auto bias4 = [&](int jb) {
+  // 4 bias values of keys jb..jb+3 as raw 16-bit pairs (zeros past the bias
+  // columns); full: the whole tile lies inside the columns and rows are
+  // aligned (the same for every lane, so no lane takes the other path)
+  auto bias4 = [&](int jb, bool full) {
     if (MASK && !p.bias) return make_uint2(0, 0);
-    if (pl.bias_vec && jb + 3 < p.bias_cols) return *(const uint2 *)(bias_row + jb);
+    if (full) return *(const uint2 *)(bias_row + jb);
     uint16_t e4[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -431,8 +433,8 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
                                                  row_h * p.mask_sh +
                                                  (int64_t)(row_ok ? row_i : 0) * p.mask_si
                                            : nullptr;
-  auto mask4 = [&](int jb) {
-    if (pl.mask_vec && jb + 3 < p.mask_cols) return *(const uint32_t *)(mask_row + jb);
+  auto mask4 = [&](int jb, bool full) {
+    if (full) return *(const uint32_t *)(mask_row + jb);
     uint32_t w = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -441,13 +443,30 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
   };
   // At head size 64 with two wavefronts per SIMD the bias of the next tile is
   // prefetched with its K/V (with three, its registers are not available).
+  // Otherwise a tile's bias and mask words are loaded at the start of the
+  // tile, before the next tile's K/V loads: the memory counter is in order,
+  // so waiting for loads issued after those would wait for them too.
   constexpr bool BPRE = BIAS && D == 64 && kOcc<D, BM> == 2;
-  uint2 bcur[BPRE ? KB : 1][4], bnext[BPRE ? KB : 1][4];
-  auto load_bias = [&](int kt, uint2 (&bb)[BPRE ? KB : 1][4]) {
+  typedef uint2 BiasWords[BIAS ? KB : 1][4];
+  typedef uint32_t MaskWords[MASK ? KB : 1][4];
+  BiasWords bcur, bnext;
+  auto load_bias = [&](int kt, BiasWords &bb) __attribute__((always_inline)) {
+    if constexpr (BIAS) {
+      const bool full = pl.bias_vec && kt * BN + BN <= p.bias_cols;
 #pragma unroll
-    for (int kb = 0; kb < (BPRE ? KB : 1); ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) bb[kb][q4] = bias4(kt * BN + kb * 32 + 8 * q4 + 4 * half);
+        for (int q4 = 0; q4 < 4; ++q4) bb[kb][q4] = bias4(kt * BN + kb * 32 + 8 * q4 + 4 * half, full);
+    }
+  };
+  auto load_mask = [&](int kt, MaskWords &mw) __attribute__((always_inline)) {
+    if constexpr (MASK) {
+      const bool full = pl.mask_vec && kt * BN + BN <= p.mask_cols;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) mw[kb][q4] = mask4(kt * BN + kb * 32 + 8 * q4 + 4 * half, full);
+    }
   };
 
   f32x16 o[NDB];
@@ -487,7 +506,8 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
   // are rewritten into the log2 domain; otherwise they stay raw (scale > 0,
   // folded into the exponent's FMA) and masking only writes -inf in place, so
   // masked and unmasked tiles share one body.
-  auto softmax_pv = [&](int kt, const T *vbuf, f32x16 (&sacc)[KB], bool masked) __attribute__((always_inline)) {
+  auto softmax_pv = [&](int kt, const T *vbuf, f32x16 (&sacc)[KB], bool masked, const BiasWords &bwt,
+                        const MaskWords &mwt) __attribute__((always_inline)) {
     constexpr bool GENERAL = BIAS || SOFTCAP;
     const char *vl = (const char *)vbuf;
     const int j0 = kt * BN;
@@ -499,12 +519,12 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
           const int jb = j0 + kb * 32 + 8 * q4 + 4 * half;  // 4 consecutive keys
           float bv[4] = {0.f, 0.f, 0.f, 0.f};
           if (BIAS) {
-            const uint2 raw = BPRE ? bcur[BPRE ? kb : 0][q4] : bias4(jb);
+            const uint2 raw = BPRE ? bcur[kb][q4] : bwt[kb][q4];
             bv[0] = lo16<T>(raw.x); bv[1] = hi16<T>(raw.x);
             bv[2] = lo16<T>(raw.y); bv[3] = hi16<T>(raw.y);
           }
           uint32_t mw = 0x01010101u;  // BOOL attn_mask bytes of the 4 keys
-          if (MASK) mw = mask4(jb);
+          if constexpr (MASK) mw = mwt[kb][q4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             float t;
@@ -601,6 +621,12 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
   // the CU cover their latency).
   auto tile = [&](int kt, const T *kc, const T *vc, T *kn, T *vn) __attribute__((always_inline)) {
     const bool more = kt + 1 < kt1;
+    BiasWords bwt;
+    MaskWords mwt;
+    if (wave_active) {
+      if (!BPRE) load_bias(kt, bwt);
+      load_mask(kt, mwt);
+    }
     if (more) {
       issue_loads(kt + 1, kn, vn);
       if (BPRE) load_bias(kt + 1, bnext);
@@ -613,11 +639,11 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
                              j0 < lo || (p.pad_add && j0 + BN > s.pad);
       f32x16 sacc[KB];
       qk(kc, sacc);
-      softmax_pv(kt, vc, sacc, need_mask);
+      softmax_pv(kt, vc, sacc, need_mask, bwt, mwt);
     }
     if (more && BPRE) {
 #pragma unroll
-      for (int kb = 0; kb < (BPRE ? KB : 1); ++kb)
+      for (int kb = 0; kb < (BIAS ? KB : 1); ++kb)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) bcur[kb][q4] = bnext[kb][q4];
     }
