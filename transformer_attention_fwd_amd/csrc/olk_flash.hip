@@ -452,20 +452,34 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
   BiasWords bcur, bnext;
   auto load_bias = [&](int kt, BiasWords &bb) __attribute__((always_inline)) {
     if constexpr (BIAS) {
-      const bool full = pl.bias_vec && kt * BN + BN <= p.bias_cols;
+      // one uniform choice for the tile (per-call choices leave the
+      // compiler unable to count the loads still in flight)
+      if (pl.bias_vec && kt * BN + BN <= p.bias_cols) {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) bb[kb][q4] = bias4(kt * BN + kb * 32 + 8 * q4 + 4 * half, full);
+          for (int q4 = 0; q4 < 4; ++q4) bb[kb][q4] = bias4(kt * BN + kb * 32 + 8 * q4 + 4 * half, true);
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) bb[kb][q4] = bias4(kt * BN + kb * 32 + 8 * q4 + 4 * half, false);
+      }
     }
   };
   auto load_mask = [&](int kt, MaskWords &mw) __attribute__((always_inline)) {
     if constexpr (MASK) {
-      const bool full = pl.mask_vec && kt * BN + BN <= p.mask_cols;
+      if (pl.mask_vec && kt * BN + BN <= p.mask_cols) {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) mw[kb][q4] = mask4(kt * BN + kb * 32 + 8 * q4 + 4 * half, full);
+          for (int q4 = 0; q4 < 4; ++q4) mw[kb][q4] = mask4(kt * BN + kb * 32 + 8 * q4 + 4 * half, true);
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) mw[kb][q4] = mask4(kt * BN + kb * 32 + 8 * q4 + 4 * half, false);
+      }
     }
   };
 
@@ -621,22 +635,32 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
   // the CU cover their latency).
   auto tile = [&](int kt, const T *kc, const T *vc, T *kn, T *vn) __attribute__((always_inline)) {
     const bool more = kt + 1 < kt1;
+    // present rows of this tile first: their stores count in the same
+    // in-order counter, so after the word loads they would hold up the wait
+    // for those words
+    if (fuse_loop && kt * BN < own_hi && kt * BN + BN > own_lo) copy_owned(kt, kc, vc);
     BiasWords bwt;
     MaskWords mwt;
     if (wave_active) {
       if (!BPRE) load_bias(kt, bwt);
       load_mask(kt, mwt);
     }
-    if (more) {
-      issue_loads(kt + 1, kn, vn);
-      if (BPRE) load_bias(kt + 1, bnext);
-    }
-    if (fuse_loop && kt * BN < own_hi && kt * BN + BN > own_lo) copy_owned(kt, kc, vc);
+    // (the empty asm keeps the compiler from issuing the word loads after
+    // the K/V loads below)
+    asm volatile("" ::: "memory");
+    // the next tile's K/V; the last tile reloads the previous one into the
+    // buffers that hold it (unread meanwhile), so every tile issues the same
+    // loads and the wait for the words above can leave these in flight
+    issue_loads(more ? kt + 1 : max(kt - 1, kt0), kn, vn);
+    if (more && BPRE) load_bias(kt + 1, bnext);
     if (wave_active) {
       const int j0 = kt * BN;
       const bool need_mask = (p.causal && j0 + BN - 1 > pos_min) ||
                              (p.window > 0 && j0 < pos_max - p.window + 1) || j0 + BN > hi ||
                              j0 < lo || (p.pad_add && j0 + BN > s.pad);
+      // the words have landed once at most the 2 NLD K/V loads issued after
+      // them are in flight (the counter is in order)
+      if constexpr (BIAS && !BPRE) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 | (2 * NLD));
       f32x16 sacc[KB];
       qk(kc, sacc);
       softmax_pv(kt, vc, sacc, need_mask, bwt, mwt);
