@@ -137,7 +137,8 @@ __device__ __forceinline__ void rotate_task(const Params &p, const T *src, T *ds
   }
 }
 
-// Vector form (R a multiple of 16, D a multiple of 8, 16-byte aligned rows):
+// Vector form (R a multiple of 16, D a multiple of 8, 16-byte aligned rows),
+// float32 elements (16-bit types take the multi-row form below):
 // one workgroup per (b, i) row; threads sweep the query-head tasks, the
 // key-head tasks and the 8-channel value chunks.
 template <typename T>
@@ -165,6 +166,122 @@ __global__ __launch_bounds__(kThreads) void rope_vec_kernel(Params p) {
       const T *vrow = (const T *)p.v + b * p.v_sb + (int64_t)i * p.v_ss + (int64_t)g * p.v_sh;
       T *dst = (T *)p.present_v + (((int64_t)b * p.Hkv + g) * p.T + j) * p.Dv;
       st8(dst + c0, ld8(vrow + c0));
+    }
+  }
+}
+
+// Vector form for 16-bit types, several rows per workgroup: a thread takes up
+// to TPT tasks (16-byte chunks of any row, head and kind) and issues all their
+// loads before it computes and stores any, so each thread keeps several loads
+// in flight and the grid is RPW times smaller than one workgroup per row.
+constexpr int kRowsPerWg = 8;
+template <typename T, int TPT>
+__global__ __launch_bounds__(kThreads) void rope_vec2_kernel(Params p) {
+  static_assert(sizeof(T) == 2, "16-bit element types");
+  const int b = blockIdx.y;
+  const Seq s = seq_info(p, b);
+  const int nt = vec_tasks<T>(p), vt = p.Dv / 8;
+  const int nq = p.rot_q ? 0 : p.Hq * nt, nk = p.Hkv * nt, nv = p.Hkv * vt;
+  const int per_row = nq + nk + nv;
+  const int i0 = blockIdx.x * kRowsPerWg;
+  const int total = min(kRowsPerWg, p.S - i0) * per_row;
+  const int R = p.rot_dim, half = R / 2, npair = half / 8;
+  for (int base = 0; base < total; base += kThreads * TPT) {
+    // phase 1: addresses and loads of every task of this thread
+    uint4 xa[TPT], xb[TPT], xc[TPT], xs[TPT];
+    T *dst[TPT];
+    int kind[TPT];  // 0: none, 1: rotate split pair, 2: rotate interleaved, 3: copy
+    int c0s[TPT];
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      kind[u] = 0;
+      const int t = base + u * kThreads + threadIdx.x;
+      if (t >= total) continue;
+      const int i = i0 + t / per_row, r = t % per_row;
+      const int j = s.past + i;
+      if (j >= p.T) continue;
+      const int pos = j < p.rot_max ? j : p.rot_max - 1;
+      const T *src;
+      int task;
+      if (r < nq + nk) {
+        if (r < nq) {
+          const int h = r / nt;
+          task = r % nt;
+          src = (const T *)p.q + b * p.q_sb + (int64_t)i * p.q_ss + (int64_t)h * p.q_sh;
+          dst[u] = (T *)p.y + b * p.y_sb + (int64_t)i * p.y_ss + (int64_t)h * p.y_sh;
+        } else {
+          const int g = (r - nq) / nt;
+          task = (r - nq) % nt;
+          src = (const T *)p.k + b * p.k_sb + (int64_t)i * p.k_ss + (int64_t)g * p.k_sh;
+          dst[u] = (T *)p.present_k + (((int64_t)b * p.Hkv + g) * p.T + j) * p.D;
+        }
+        const T *cs = (const T *)p.cos_cache + (int64_t)pos * half;
+        const T *sn = (const T *)p.sin_cache + (int64_t)pos * half;
+        if (p.rot_inter) {
+          const int c0 = 8 * task;
+          c0s[u] = c0;
+          xa[u] = *(const uint4 *)(src + c0);
+          if (c0 < R) {
+            kind[u] = 2;
+            const uint2 c4 = *(const uint2 *)(cs + c0 / 2), s4 = *(const uint2 *)(sn + c0 / 2);
+            xc[u] = make_uint4(c4.x, c4.y, 0, 0);
+            xs[u] = make_uint4(s4.x, s4.y, 0, 0);
+          } else {
+            kind[u] = 3;
+          }
+        } else if (task < npair) {
+          const int c0 = 8 * task;
+          c0s[u] = c0;
+          kind[u] = 1;
+          xa[u] = *(const uint4 *)(src + c0);
+          xb[u] = *(const uint4 *)(src + c0 + half);
+          xc[u] = *(const uint4 *)(cs + c0);
+          xs[u] = *(const uint4 *)(sn + c0);
+        } else {
+          const int c0 = R + 8 * (task - npair);
+          c0s[u] = c0;
+          kind[u] = 3;
+          xa[u] = *(const uint4 *)(src + c0);
+        }
+      } else {
+        const int g = (r - nq - nk) / vt, c0 = 8 * ((r - nq - nk) % vt);
+        c0s[u] = c0;
+        kind[u] = 3;
+        xa[u] = *(const uint4 *)((const T *)p.v + b * p.v_sb + (int64_t)i * p.v_ss +
+                                 (int64_t)g * p.v_sh + c0);
+        dst[u] = (T *)p.present_v + (((int64_t)b * p.Hkv + g) * p.T + j) * p.Dv;
+      }
+    }
+    // phase 2: the same float32 arithmetic as rotate_task, one rounding
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      if (kind[u] == 0) continue;
+      const int c0 = c0s[u];
+      if (kind[u] == 3) {
+        *(uint4 *)(dst[u] + c0) = xa[u];
+      } else if (kind[u] == 2) {
+        const T *x = (const T *)&xa[u], *c = (const T *)&xc[u], *sv = (const T *)&xs[u];
+        Chunk8<T> o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x1 = (float)x[2 * e], x2 = (float)x[2 * e + 1];
+          o.e[2 * e] = (T)rot_first(x1, x2, (float)c[e], (float)sv[e]);
+          o.e[2 * e + 1] = (T)rot_second(x1, x2, (float)c[e], (float)sv[e]);
+        }
+        st8(dst[u] + c0, o);
+      } else {
+        const T *a = (const T *)&xa[u], *bb = (const T *)&xb[u];
+        const T *c = (const T *)&xc[u], *sv = (const T *)&xs[u];
+        Chunk8<T> oa, ob;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x1 = (float)a[e], x2 = (float)bb[e];
+          oa.e[e] = (T)rot_first(x1, x2, (float)c[e], (float)sv[e]);
+          ob.e[e] = (T)rot_second(x1, x2, (float)c[e], (float)sv[e]);
+        }
+        st8(dst[u] + c0, oa);
+        st8(dst[u] + c0 + half, ob);
+      }
     }
   }
 }
@@ -215,8 +332,9 @@ hipError_t launch_rope(const Params &p, int dtype, hipStream_t st) {
                    (p.v_sh * es) % 16 == 0 && (p.v_ss * es) % 16 == 0 &&
                    (p.q_sb * es) % 16 == 0 && (p.k_sb * es) % 16 == 0 && (p.v_sb * es) % 16 == 0;
   if (vec) {
-    if (dtype == DT_BF16) hipLaunchKernelGGL(rope_vec_kernel<bf16>, grid, dim3(kThreads), 0, st, p);
-    else if (dtype == DT_F16) hipLaunchKernelGGL(rope_vec_kernel<f16>, grid, dim3(kThreads), 0, st, p);
+    const dim3 grid2((p.S + kRowsPerWg - 1) / kRowsPerWg, p.B);
+    if (dtype == DT_BF16) hipLaunchKernelGGL((rope_vec2_kernel<bf16, 4>), grid2, dim3(kThreads), 0, st, p);
+    else if (dtype == DT_F16) hipLaunchKernelGGL((rope_vec2_kernel<f16, 4>), grid2, dim3(kThreads), 0, st, p);
     else hipLaunchKernelGGL(rope_vec_kernel<float>, grid, dim3(kThreads), 0, st, p);
   } else {
     if (dtype == DT_BF16) hipLaunchKernelGGL(rope_kernel<bf16>, grid, dim3(kThreads), 0, st, p);
