@@ -78,6 +78,12 @@ SMALL = {
     "gqa_rope_dim12_f16": Problem(op="gqa", dtype="f16", B=2, S=33, L=33, P=8, Hq=4, Hkv=2,
                                   D=64, Dv=64, causal=1, lens_range=(0, 8), rotary=1,
                                   rotary_dim=12),
+    # split halves over part of the head (the pre-pass rotates Q too, and
+    # copies the channels past the rotary dimension), rows not a multiple of
+    # the pre-pass's 8-row workgroups, a past
+    "gqa_rope_partial_split_bf16": Problem(op="gqa", dtype="bf16", B=2, S=37, L=37, P=12,
+                                           Hq=8, Hkv=2, D=128, Dv=128, causal=1,
+                                           lens_range=(3, 12), rotary=1, rotary_dim=64),
     # mask surface: BOOL masks (broadcast, short), FLOAT masks broadcast over
     # queries with a short last dimension (tiled path), int64 nonpad lengths,
     # MultiHeadAttention binary masks
