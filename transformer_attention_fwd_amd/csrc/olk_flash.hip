@@ -23,12 +23,20 @@
 //   for V.  The V^T operand of PV is read with ds_read_b64_tr_b16 from the
 //   row-major V tile: each transposed read hands a lane 4 consecutive keys of
 //   its head dimension, in the k order in which the accumulator supplies P^T.
-// * Keys advance in tiles of 64.
-// * K/V tiles are double-buffered in LDS, one barrier per tile; the next
-//   tile's global loads are in flight while the current tile computes.
+// * Keys advance in tiles of 64, double-buffered in LDS with one barrier per
+//   tile; the next tile's loads are in flight while the current tile
+//   computes.  The buffers are separate LDS variables and the key loop is
+//   unrolled by two, so the compiler can tell the loads landing in one
+//   buffer from the reads of the other.  A tile's bias / BOOL-mask words are
+//   loaded before the next tile's K/V (the memory counter is in order).
+// * S^T is accumulated block-major (32 keys at a time), so the first block's
+//   row max can start beside the second block's MFMAs.
 // * Online softmax in the exp2 domain, the scale folded into the exponent's
-//   FMA; per-key masks only on boundary tiles, written as -inf in place.  O is rescaled only when a row's running max grows by more
-//   than 2^8 (the final division uses the same max, so the result is unchanged).
+//   FMA; per-key masks only on boundary tiles, written as -inf in place.  O
+//   is rescaled only when a row's running max grows by more than 2^8 (the
+//   final division uses the same max, so the result is unchanged).  The row
+//   sum adds the P values as rounded for the PV product (packed dot
+//   products), so Y is an exactly normalised mean of V rows.
 // * GroupQueryAttention present rows of the new keys are stored by the
 //   workgroup whose queries sit at those positions, copied from LDS: with
 //   causal masking from its last two tiles after the loop, otherwise while
