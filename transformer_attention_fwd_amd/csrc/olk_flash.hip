@@ -216,7 +216,8 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
   const bool wave_active = i0 + (wave * 32) / pl.GH < p.S;
 
   // ---- Q^T operand (B of S^T = K Q^T): slot col, d = 16 ks + 8 half + e ----
-  vec8 qreg[NKS];
+  vec8 qreg[NKS];  // filled by load_q below, after the first tile's loads are issued
+  auto load_q = [&]() __attribute__((always_inline)) {
   {
     const T *qr = (const T *)p.q + b * p.q_sb + (int64_t)(row_ok ? row_i : 0) * p.q_ss +
                   row_h * p.q_sh;
@@ -295,11 +296,7 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
       }
     }
   }
-  // Q is in registers from here on.  Waiting for its loads now, on every path,
-  // keeps the wait-count analysis from assuming they may still be in flight
-  // inside the loop, where it would otherwise hold the first MFMA of every
-  // tile until the next tile's prefetch loads have landed as well.
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  };
 
   // ---- staging: K and V tiles go from memory straight into LDS ----
   // A direct load writes 16 bytes per lane at consecutive LDS addresses (1 KB
@@ -630,12 +627,17 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
     l += lsum2[0] + lsum2[1];
   };
 
+  // The first tile's loads go out before the Q loads, so the two latencies
+  // overlap.  Waiting for all of them here, on every path, also keeps the
+  // wait-count analysis from assuming Q may still be in flight inside the
+  // loop (it would then hold the first MFMA of every tile until the next
+  // tile's loads had landed as well).  Direct loads write LDS behind the
+  // compiler's back: the wait comes before the barrier that publishes them.
   if (kt0 < kt1) {
     issue_loads(kt0, klds0, vlds0);
     if (BPRE) load_bias(kt0, bcur);
   }
-  // direct loads write LDS behind the compiler's back: wait for them before
-  // the barrier that publishes the tile
+  load_q();
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
   // One tile: the next tile's loads go out first and land in the other
