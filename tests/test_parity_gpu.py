@@ -42,6 +42,13 @@ SMALL = {
     "gqa_decode_sink_window_bf16": Problem(op="gqa", dtype="bf16", B=3, S=2, L=2, P=300,
                                            Hq=4, Hkv=1, D=64, Dv=64, causal=1, window=100,
                                            has_sink=True, lens_range=(50, 300)),
+    # head-size-128 decode with 8 and 16 row slots per KV head (PV on the
+    # matrix cores): window + sink, short and long pasts
+    "gqa_decode_rows8_bf16": Problem(op="gqa", dtype="bf16", B=3, S=2, L=2, P=333, Hq=16,
+                                     Hkv=4, D=128, Dv=128, causal=1, window=150,
+                                     has_sink=True, lens_range=(1, 333)),
+    "gqa_decode_rows16_f16": Problem(op="gqa", dtype="f16", B=2, S=1, L=1, P=1500, Hq=32,
+                                     Hkv=2, D=128, Dv=128, causal=1, lens_range=(0, 1500)),
     "gqa_noncausal_f32": Problem(op="gqa", dtype="f32", B=2, S=40, L=40, Hq=4, Hkv=2, D=32,
                                  Dv=32, causal=0),
     "gqa_softcap_small_f32": Problem(op="gqa", dtype="f32", B=1, S=50, L=50, Hq=2, Hkv=1,

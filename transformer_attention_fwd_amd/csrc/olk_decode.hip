@@ -327,11 +327,273 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p, DPlan pl) {
   }
 }
 
+
+// ---- head size 128: PV on the matrix cores ----
+// O^T += V^T P^T runs on v_mfma_f32_16x16x16: P^T (the B operand: lane l
+// holds keys 4 (l / 16) + i of slot l % 16) is the S^T accumulator itself,
+// and V^T (the A operand: lane l holds keys 4 (l / 16) + i of dim 16 blk +
+// l % 16) comes from ds_read_b64_tr_b16 on a per-wavefront LDS copy of the
+// step's 16 V rows.  The rows are loaded into registers (two steps ahead, like
+// K) and written to LDS just before their transposed reads; 16-byte chunk c of
+// row r sits at slot c ^ 2 (r & 7), so the four rows one 16-lane group reads
+// hit distinct banks.  A wavefront only reads the rows it wrote, and one
+// wavefront's LDS operations run in order, so no barrier or wait is needed
+// between the writes and the reads (nor against the previous step's reads).
+// (Loading V straight into LDS instead left direct-to-LDS loads and register
+// loads in flight together, and the compiler then waits for all loads.)
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+template <typename T> struct DV4;
+template <> struct DV4<bf16> { typedef s16x4 v4; };
+template <> struct DV4<f16> { typedef f16x4 v4; };
+__device__ __forceinline__ f32x4 mma16k16(f16x4 a, f16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16k16(s16x4 a, s16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+// two P values rounded to the element type, as the low / high halves of a word
+template <typename T> __device__ __forceinline__ uint32_t pack2p(float a, float b) {
+  const T x = (T)a, y = (T)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+template <typename T, int NR>
+__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p, DPlan pl) {
+  constexpr int D = 128;
+  typedef typename DV<T>::v8 vec8;
+  typedef typename DV4<T>::v4 vec4;
+  constexpr int NKS = D / 32;   // k-steps of QK^T (32 dims each)
+  constexpr int NBLK = D / 16;  // 16-dim blocks of O^T
+  constexpr int VRB = D * 2;    // bytes per V row in LDS
+  // V rows of the current step, one tile per wavefront
+  __shared__ __attribute__((aligned(16))) T vbw[4][kStep * D];
+  __shared__ __attribute__((aligned(16))) float mrg_ml[4][2][16];
+  __shared__ __attribute__((aligned(16))) float mrg_o[4][NR][D];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int split = blockIdx.x % pl.n_split;
+  const int bg = blockIdx.x / pl.n_split;
+  const int g = bg % p.Hkv, b = bg / p.Hkv;
+  const Seq s = seq_info(p, b);
+  const int nrows = p.G * p.S;
+
+  // key range of the workgroup: union over its rows, cut to the split
+  const int pos_min = s.qoff, pos_max = s.qoff + p.S - 1;
+  int hi = p.pad_add ? s.total : s.valid;
+  if (p.causal) hi = min(hi, pos_max + 1);
+  int lo = p.window > 0 ? max(0, pos_min - p.window + 1) : 0;
+  const int sp_lo = max(lo, split * pl.split_keys);
+  const int sp_hi = min(hi, (split + 1) * pl.split_keys);
+  const int base = (sp_lo / kStep) * kStep;
+  const int n_steps = sp_lo < sp_hi ? (sp_hi - base + kStep - 1) / kStep : 0;
+
+  // ---- Q^T operand: column n = lane % 16 is row slot n = (query n / G, head n % G) ----
+  const int n = lane & 15, kq = lane >> 4;
+  const int row_q = n / p.G, row_h = g * p.G + n % p.G;
+  const bool col_ok = n < nrows;
+  const int col_pos = s.qoff + row_q;
+  vec8 qreg[NKS];
+  {
+    const T *qr = (const T *)p.q + b * p.q_sb + (int64_t)(col_ok ? row_q : 0) * p.q_ss +
+                  (col_ok ? row_h : 0) * p.q_sh;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      uint4 raw = make_uint4(0, 0, 0, 0);
+      if (col_ok) raw = *(const uint4 *)(qr + ks * 32 + kq * 8);
+      qreg[ks] = __builtin_bit_cast(vec8, raw);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // Q in registers (vmcnt(0) only)
+
+  const T *kpast = (const T *)p.past_k + ((int64_t)b * p.Hkv + g) * p.past_rows * D;
+  const T *vpast = (const T *)p.past_v + ((int64_t)b * p.Hkv + g) * p.past_rows * D;
+  const T *knew = (const T *)p.k + b * p.k_sb + g * p.k_sh;
+  const T *vnew = (const T *)p.v + b * p.v_sb + g * p.v_sh;
+
+  // V registers: key 2 t + lane / 32, dims 4 (lane % 32) .. + 3 (8 bytes);
+  // written to LDS at row 2 t + lane / 32, chunk (lane % 32) / 2, half lane & 1
+  const int vcol = 4 * (lane & 31), vpar = lane >> 5;
+  // transposed reads: this lane addresses row 4 (l / 16) + (l % 16) / 4 and
+  // dims 16 blk + 4 ((l % 16) & 3), i.e. byte tro + 32 (blk ^ (row & 7))
+  const int trr = 4 * kq + ((lane & 15) >> 2);
+  const uint32_t tro = (uint32_t)(trr * VRB + 16 * (((lane & 3) >> 1)) + 8 * (lane & 1));
+  const int trx = trr & 7;
+
+  auto load_step = [&](int st, uint4 (&kk)[NKS], uint2 (&vv)[kStep / 2]) __attribute__((always_inline)) {
+    const int j0 = base + (wave + 4 * st) * kStep;
+    const bool full = j0 >= sp_lo && j0 + kStep <= sp_hi;
+    if (full && (j0 >= s.src || j0 + kStep <= s.src)) {
+      // the whole step from one source: uniform base + 32-bit lane offsets
+      const bool from_new = j0 >= s.src;
+      const char *kb = (const char *)(from_new ? knew + (int64_t)(j0 - s.src) * p.k_ss
+                                               : kpast + (int64_t)j0 * D);
+      const char *vb = (const char *)(from_new ? vnew + (int64_t)(j0 - s.src) * p.v_ss
+                                               : vpast + (int64_t)j0 * D);
+      const uint32_t krs = (uint32_t)(from_new ? p.k_ss : D) * (uint32_t)sizeof(T);
+      const uint32_t vrs = (uint32_t)(from_new ? p.v_ss : D) * (uint32_t)sizeof(T);
+      const uint32_t koff = (uint32_t)n * krs + (uint32_t)kq * 16u;
+#pragma unroll
+      for (int s2 = 0; s2 < NKS; ++s2) kk[s2] = ld_stream16(kb + koff + s2 * 64);
+      const uint32_t voff = (uint32_t)vpar * vrs + (uint32_t)vcol * (uint32_t)sizeof(T);
+#pragma unroll
+      for (int t = 0; t < kStep / 2; ++t) vv[t] = ld_stream8(vb + voff + 2 * t * vrs);
+      return;
+    }
+    // Steps that straddle the range or the past/new boundary: per-lane rows;
+    // rows outside [sp_lo, sp_hi) load row sp_lo (valid memory, finite
+    // values; their scores are masked, so their P is exactly 0).
+    auto row_ptr = [&](const T *pastp, const T *newp, int64_t new_ss, int j) {
+      const int jj = j >= sp_lo && j < sp_hi ? j : sp_lo;
+      const bool nw = jj >= s.src;
+      const int64_t off_new = (int64_t)(jj - s.src) * new_ss, off_past = (int64_t)jj * D;
+      return (nw ? newp : pastp) + (nw ? off_new : off_past);
+    };
+    const T *ks = row_ptr(kpast, knew, p.k_ss, j0 + n);
+#pragma unroll
+    for (int s2 = 0; s2 < NKS; ++s2) kk[s2] = *(const uint4 *)(ks + s2 * 32 + kq * 8);
+#pragma unroll
+    for (int t = 0; t < kStep / 2; ++t)
+      vv[t] = *(const uint2 *)(row_ptr(vpast, vnew, p.v_ss, j0 + 2 * t + vpar) + vcol);
+  };
+
+  float m = kNegInf, l = 0.f;
+  f32x4 o[NBLK];
+#pragma unroll
+  for (int blk = 0; blk < NBLK; ++blk) o[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float sl = p.scale * kLog2e;
+
+  const int my_steps = n_steps > wave ? (n_steps - wave + 3) / 4 : 0;
+  uint4 k0[NKS], k1[NKS], k2[NKS];
+  uint2 v0[kStep / 2], v1[kStep / 2], v2[kStep / 2];
+  char *vl = (char *)vbw[wave];
+  // this lane's 8-byte V pieces: row 2 t + vpar at byte vwo + 512 t
+  const int vwr = vpar;  // row parity; rows 2 t + vpar have (row & 7) = (2 t + vpar) & 7
+  auto body = [&](int it, uint4 (&kr)[NKS], const uint2 (&vr)[kStep / 2], uint4 (&kf)[NKS],
+                  uint2 (&vf)[kStep / 2]) __attribute__((always_inline)) {
+    if (it + 2 < my_steps) load_step(it + 2, kf, vf);
+    const int j0 = base + (wave + 4 * it) * kStep;
+    // S^T (16 keys x 16 slots)
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s2 = 0; s2 < NKS; ++s2) sacc = mma16(__builtin_bit_cast(vec8, kr[s2]), qreg[s2], sacc);
+    // scores of slot n for keys j0 + 4 kq + r, log2 domain, masked
+    float t4[4];
+    float mx = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = j0 + 4 * kq + r;
+      float t = sacc[r] * sl;
+      bool ok = j >= sp_lo && j < sp_hi;
+      if (p.causal && j > col_pos) ok = false;
+      if (p.window > 0 && j < col_pos - p.window + 1) ok = false;
+      if (p.pad_add && j >= s.pad) t += p.mfv * kLog2e;
+      t4[r] = ok ? t : kNegInf;
+      mx = fmaxf(mx, t4[r]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = max32(mx);
+    const float m_new = fmaxf(m, mx);
+    const bool grow = m_new > m + kRescale;
+    const float m_prev = m;
+    if (grow) m = m_new;
+    const float mu = m == kNegInf ? 0.f : m;
+    // P^T as the B operand, rounded; the row sum adds the rounded values
+    const uint32_t w0 = pack2p<T>(ex2(t4[0] - mu), ex2(t4[1] - mu));
+    const uint32_t w1 = pack2p<T>(ex2(t4[2] - mu), ex2(t4[3] - mu));
+    const vec4 pb = __builtin_bit_cast(vec4, make_uint2(w0, w1));
+    const float lsum = (lo16<T>(w0) + hi16<T>(w0)) + (lo16<T>(w1) + hi16<T>(w1));
+    // O^T columns and l follow a grown max (each lane holds its own slot)
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float alpha = grow ? ex2(m_prev - m) : 1.0f;
+      l *= alpha;
+#pragma unroll
+      for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[blk][r] *= alpha;
+    }
+    l += lsum;  // lane-local partial of slot n
+    // the step's V rows into this wavefront's LDS tile (swizzled chunks)
+#pragma unroll
+    for (int t = 0; t < kStep / 2; ++t) {
+      const int r = 2 * t + vwr;
+      const int c = (lane & 31) >> 1;
+      *(uint2 *)(vl + r * VRB + 16 * (c ^ (2 * (r & 7))) + 8 * (lane & 1)) = vr[t];
+    }
+    // PV on the matrix cores
+#pragma unroll
+    for (int blk = 0; blk < NBLK; ++blk) {
+      typedef __attribute__((address_space(3))) s16x4 *tr_ptr;
+      const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((tr_ptr)(vl + tro + 32 * (blk ^ trx)));
+      o[blk] = mma16k16(__builtin_bit_cast(vec4, a), pb, o[blk]);
+    }
+  };
+  if (my_steps > 0) load_step(0, k0, v0);
+  if (my_steps > 1) load_step(1, k1, v1);
+  for (int it = 0; it < my_steps; it += 3) {
+    body(it, k0, v0, k2, v2);
+    if (it + 1 < my_steps) body(it + 1, k1, v1, k0, v0);
+    if (it + 2 < my_steps) body(it + 2, k2, v2, k1, v1);
+  }
+
+  // ---- wave partials -> LDS: m, l per slot (from the 4 lanes of each slot) ----
+  float lsl = l + __shfl_xor(l, 16, 64);
+  lsl = sum32(lsl);
+  if (lane < 16) {
+    mrg_ml[wave][0][lane] = m;
+    mrg_ml[wave][1][lane] = lsl;
+  }
+  // O^T: lane l holds dims 16 blk + 4 (l / 16) + r of slot l % 16
+  if (n < NR) {
+#pragma unroll
+    for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mrg_o[wave][n][16 * blk + 4 * kq + r] = o[blk][r];
+  }
+  __syncthreads();
+
+  // ---- merge the 4 wavefronts; one record per valid row slot ----
+  for (int r = wave; r < NR; r += 4) {
+    if (r >= nrows) continue;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, mrg_ml[w][0][r]);
+    float sc[4], L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = mrg_ml[w][0][r];
+      sc[w] = mw == kNegInf ? 0.f : ex2(mw - M);
+      L += sc[w] * mrg_ml[w][1][r];
+    }
+    const int rq = r / p.G, rh = g * p.G + r % p.G;
+    const int64_t row = ((int64_t)b * p.S + rq) * p.Hq + rh;
+    float *out = pl.ws + (row * pl.n_split + split) * (int64_t)(D + 4);
+    if (lane == 0) {
+      out[0] = M == kNegInf ? kNegInf : M * kLn2;
+      out[1] = M == kNegInf ? 0.f : L;
+    }
+    for (int d = lane; d < D; d += 64) {
+      float acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) acc += sc[w] * mrg_o[w][r][d];
+      out[4 + d] = M == kNegInf ? 0.f : acc;
+    }
+  }
+}
+
 template <typename T, int D>
 hipError_t launch_nr(const Params &p, const DPlan &pl, int nr, dim3 grid, hipStream_t st) {
-  if (nr <= 4) hipLaunchKernelGGL((decode_kernel<T, D, 4>), grid, dim3(kThreads), 0, st, p, pl);
-  else if (nr <= 8) hipLaunchKernelGGL((decode_kernel<T, D, 8>), grid, dim3(kThreads), 0, st, p, pl);
-  else hipLaunchKernelGGL((decode_kernel<T, D, 16>), grid, dim3(kThreads), 0, st, p, pl);
+  if constexpr (D == 128) {
+    // head size 128: PV on the matrix cores
+    if (nr <= 4) hipLaunchKernelGGL((decode_mfma_kernel<T, 4>), grid, dim3(kThreads), 0, st, p, pl);
+    else if (nr <= 8) hipLaunchKernelGGL((decode_mfma_kernel<T, 8>), grid, dim3(kThreads), 0, st, p, pl);
+    else hipLaunchKernelGGL((decode_mfma_kernel<T, 16>), grid, dim3(kThreads), 0, st, p, pl);
+  } else {
+    if (nr <= 4) hipLaunchKernelGGL((decode_kernel<T, D, 4>), grid, dim3(kThreads), 0, st, p, pl);
+    else if (nr <= 8) hipLaunchKernelGGL((decode_kernel<T, D, 8>), grid, dim3(kThreads), 0, st, p, pl);
+    else hipLaunchKernelGGL((decode_kernel<T, D, 16>), grid, dim3(kThreads), 0, st, p, pl);
+  }
   return hipGetLastError();
 }
 
