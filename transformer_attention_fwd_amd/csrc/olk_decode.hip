@@ -14,9 +14,12 @@
 //   as the B operand (16 columns = the row slots (query, head)).
 // * The S^T accumulator puts each row slot's 16 scores in 4 lanes; the online
 //   softmax (exp2 domain, lazy rescale) reduces across them with lane swaps.
-// * PV on the VALU: P goes through a 1 KB LDS buffer per wavefront and is
-//   read back as broadcasts; lanes own 4 head dimensions of one key (two keys
-//   per instruction), so V rows are read fully coalesced and never transposed.
+// * PV: at head size 128 on v_mfma_f32_16x16x16 (decode_mfma_kernel below:
+//   P^T straight from the score accumulator, V^T by transposed LDS reads);
+//   at head size 64 on the VALU: P goes through a 1 KB LDS buffer per
+//   wavefront and is read back as broadcasts; lanes own 4 head dimensions of
+//   one key (two keys per instruction), so V rows are read fully coalesced
+//   and never transposed.
 // * The K and V of the next two steps are in flight while a step computes;
 //   the stream is read once, with non-temporal loads.
 // * The 4 wavefronts merge (m, l, O) through LDS and write one partial record
