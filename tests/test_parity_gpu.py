@@ -49,6 +49,13 @@ SMALL = {
                                      has_sink=True, lens_range=(1, 333)),
     "gqa_decode_rows16_f16": Problem(op="gqa", dtype="f16", B=2, S=1, L=1, P=1500, Hq=32,
                                      Hkv=2, D=128, Dv=128, causal=1, lens_range=(0, 1500)),
+    # 8192 keys: split counts that are multiples of 8 (8 decode splits, 16
+    # tiled splits), the case the split-major workgroup order is for
+    "gqa_decode_8k_bf16": Problem(op="gqa", dtype="bf16", B=2, S=1, L=1, P=8191, Hq=8,
+                                  Hkv=2, D=128, Dv=128, causal=1, lens_range=(3000, 8191)),
+    "gqa_decode_8k_rows32_f16": Problem(op="gqa", dtype="f16", B=1, S=2, L=2, P=8190,
+                                        Hq=16, Hkv=1, D=128, Dv=128, causal=1,
+                                        lens_range=(5000, 8190)),
     "gqa_noncausal_f32": Problem(op="gqa", dtype="f32", B=2, S=40, L=40, Hq=4, Hkv=2, D=32,
                                  Dv=32, causal=0),
     "gqa_softcap_small_f32": Problem(op="gqa", dtype="f32", B=1, S=50, L=50, Hq=2, Hkv=1,

@@ -8,7 +8,12 @@
 // Attention"); the decomposition is ours:
 //
 // * A workgroup owns one split (a range of SPLIT keys) of one (batch, KV head);
-//   its 4 wavefronts take interleaved 16-key steps of the split.
+//   its 4 wavefronts take interleaved 16-key steps of the split.  Workgroup
+//   ids are split-major: consecutive ids go round-robin over the 8 XCDs, so
+//   with (batch, KV head) fastest every split spreads over all XCDs whatever
+//   the split count (split-minor ids put split s on XCD s when the count is a
+//   multiple of 8, and the later splits of short sequences are empty), and
+//   the always-full first splits are dispatched before the short last ones.
 // * QK^T: v_mfma_f32_16x16x32 with K loaded from global memory straight into
 //   the A operand (16 keys x 32 dims, 16 bytes per lane) and Q^T held in VGPRs
 //   as the B operand (16 columns = the row slots (query, head)).
@@ -103,8 +108,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p, DPlan pl) {
   __shared__ __attribute__((aligned(16))) float mrg_o[4][NR][D];         // per-wave O
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int split = blockIdx.x % pl.n_split;
-  const int bg = blockIdx.x / pl.n_split;
+  const int split = blockIdx.x / (p.B * p.Hkv);  // split-major workgroup ids
+  const int bg = blockIdx.x % (p.B * p.Hkv);
   const int g = bg % p.Hkv, b = bg / p.Hkv;
   const Seq s = seq_info(p, b);
   const int nrows = p.G * p.S;
@@ -376,8 +381,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p, DPlan p
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int split = blockIdx.x % pl.n_split;
-  const int bg = blockIdx.x / pl.n_split;
+  const int split = blockIdx.x / (p.B * p.Hkv);  // split-major workgroup ids
+  const int bg = blockIdx.x % (p.B * p.Hkv);
   const int g = bg % p.Hkv, b = bg / p.Hkv;
   const Seq s = seq_info(p, b);
   const int nrows = p.G * p.S;

@@ -158,7 +158,7 @@ __global__ __launch_bounds__(kWave) void generic_kernel(Params p) {
   }
 }
 
-// Split-KV partial: block (split, h, b*S + i) handles keys
+// Split-KV partial: block (h, b*S + i, split) handles keys
 // [split*chunk, (split+1)*chunk) of the row and stores the record
 // [m, l, -, -, o[Dv]] (natural-log units, unnormalised; stride Dv + 4 floats).
 template <typename T>
@@ -166,8 +166,8 @@ __global__ __launch_bounds__(kWave) void generic_split_kernel(Params p, int chun
                                                               float *ws) {
   __shared__ float qs[256];
   __shared__ float ps[kWave];
-  const int split = blockIdx.x, h = blockIdx.y;
-  const int b = blockIdx.z / p.S, i = blockIdx.z % p.S;
+  const int split = blockIdx.z, h = blockIdx.x;  // split-major (slowest)
+  const int b = blockIdx.y / p.S, i = blockIdx.y % p.S;
   const Seq s = seq_info(p, b);
   load_q<T>(p, b, h, i, qs);
   int lo, hi;
@@ -318,7 +318,7 @@ hipError_t launch_generic(const Params &p, int dtype, hipStream_t st) {
 hipError_t launch_generic_split(const Params &p, int dtype, int chunk, int n_split, float *ws,
                                 hipStream_t st) {
   if (p.B == 0 || p.S == 0 || p.Hq == 0) return hipSuccess;
-  dim3 grid(n_split, p.Hq, p.B * p.S);
+  dim3 grid(p.Hq, p.B * p.S, n_split);
   if (dtype == DT_F32)
     hipLaunchKernelGGL(generic_split_kernel<float>, grid, dim3(kWave), 0, st, p, chunk, n_split, ws);
   else if (dtype == DT_F16)

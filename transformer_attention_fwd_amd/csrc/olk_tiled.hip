@@ -108,9 +108,11 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_kernel(Params p, Plan pl) {
 
   // ---- workgroup -> (split, q tile, b, g, hg) ----
   const int n_bg = p.B * p.Hkv * pl.n_hg;
-  int wid = blockIdx.x;
-  const int split = wid % pl.n_split;
-  wid /= pl.n_split;
+  // split-major: the split is the slowest index, so the ids within one split
+  // keep the XCD round-robin that the remap below assumes
+  const int per_split = n_bg * pl.n_qt;
+  const int split = blockIdx.x / per_split;
+  int wid = blockIdx.x % per_split;
   int bg, qrank;
   if (pl.xcd_remap) {  // consecutive ids go round-robin over the 8 XCDs
     const int per = n_bg / 8;
