@@ -268,7 +268,7 @@ def run_backward(steps: int, warmup: int):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+        print(json.dumps({"error": "the attention path runs one GPU per process and has no multi-GPU path; --gpus must be 1",
                           "n_gpus_requested": args.gpus}))
         sys.exit(2)
     import torch

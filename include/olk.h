@@ -199,12 +199,16 @@ olk_status olk_attention_fwd(const olk_attn_desc *desc, const olk_attn_io *io, v
  * head) are cut into chunks whose partial softmax states are merged by a
  * second kernel.  workspace: device memory of at least
  * olk_workspace_bytes(desc) bytes, 16-byte aligned, owned by the caller; its
- * contents on entry do not matter.  `stream` is a hipStream_t.
+ * contents on entry do not matter.  `stream` is a hipStream_t.  Errors: as
+ * olk_validate; OLK_E_WORKSPACE for a missing, short or misaligned
+ * workspace; OLK_E_UNSUPPORTED when batch * q_seq exceeds 65535, the keys
+ * need more than 4096 chunks of 512, or OLK_KERNEL_TILED is forced on a
+ * shape the tiled kernels do not take.  These are checked before anything is
+ * launched; OLK_E_HIP reports a failed launch.
  */
 olk_status olk_attention_decode(const olk_attn_desc *desc, const olk_attn_io *io,
                                 void *workspace, size_t workspace_bytes, void *stream);
 
-/* Static string naming a status. */
 /*
  * Backward of the GroupQueryAttention forward (onnx-light-cpu C++ API page
  * "Custom operators", RegisterCustomOperatorGradients, GroupQueryAttention
@@ -236,6 +240,7 @@ size_t olk_bwd_workspace_bytes(const olk_attn_desc *desc);
 olk_status olk_attention_bwd(const olk_attn_desc *desc, const olk_attn_bwd_io *io,
                              void *workspace, size_t workspace_bytes, void *stream);
 
+/* Static string naming a status. */
 const char *olk_status_str(olk_status status);
 
 /* Name of the last kernel this thread launched through the library ("" if none). */
