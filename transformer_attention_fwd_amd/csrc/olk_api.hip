@@ -420,6 +420,15 @@ olk_status olk_attention_decode(const olk_attn_desc *desc, const olk_attn_io *io
                  : kv_bias_path(desc, io) ? kv_bias_prepass(p, desc->dtype, s)
                                           : olk::launch_present(p, desc->dtype, s);
   if (e != hipSuccess) return OLK_E_HIP;
+  if (!p.keys_in_past && p.present_k && p.present_v) {
+    // present now holds the whole key sequence (past rows, then the new ones):
+    // the split kernels read every key from it, as from one past buffer
+    p.past_k = p.present_k;
+    p.past_v = p.present_v;
+    p.past_rows = p.T;
+    p.keys_in_past = 1;
+    p.present_k = p.present_v = nullptr;
+  }
   const int n_split = n_splits(desc);
   int n_comb = n_split;
   if (desc->kernel != OLK_KERNEL_GENERIC && tiled_ok && olk::decode_supports(p, desc->dtype)) {

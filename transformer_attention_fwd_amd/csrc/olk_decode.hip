@@ -50,6 +50,22 @@ __device__ __forceinline__ uint2 ld_stream8(const char *p) {
   return __builtin_bit_cast(uint2, __builtin_nontemporal_load((const u32x2 *)p));
 }
 
+// Raw buffer descriptor over `bytes` bytes at `base` (stride 0, 32-bit data
+// format word of the gfx9 family): loads at offsets >= bytes return zeros and
+// access no memory.
+constexpr int kBufWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kBufWord3);
+}
+// Streaming buffer loads (cache policy nt: read once).
+constexpr int kBufNT = 2;
+__device__ __forceinline__ uint4 ld_buf16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kBufNT));
+}
+__device__ __forceinline__ uint2 ld_buf8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kBufNT));
+}
+
 template <typename T> struct DV;
 template <> struct DV<bf16> { typedef bf16x8 v8; };
 template <> struct DV<f16> { typedef f16x8 v8; };
@@ -394,8 +410,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p, DPlan p
   int lo = p.window > 0 ? max(0, pos_min - p.window + 1) : 0;
   const int sp_lo = max(lo, split * pl.split_keys);
   const int sp_hi = min(hi, (split + 1) * pl.split_keys);
-  const int base = (sp_lo / kStep) * kStep;
-  const int n_steps = sp_lo < sp_hi ? (sp_hi - base + kStep - 1) / kStep : 0;
+  const int base = sp_lo;  // steps start at the first key of the split
+  const int n_steps = sp_lo < sp_hi ? (sp_hi - sp_lo + kStep - 1) / kStep : 0;
 
   // ---- Q^T operand: column n = lane % 16 is row slot n = (query n / G, head n % G) ----
   const int n = lane & 15, kq = lane >> 4;
@@ -415,10 +431,17 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p, DPlan p
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // Q in registers (vmcnt(0) only)
 
+  // Every key is in the past buffer (the present append ran first). The
+  // split's rows [sp_lo, sp_hi) are read through buffer descriptors based at
+  // row sp_lo and sized to the split: rows at or past sp_hi read as zeros
+  // without a memory access (range-checked offsets), so a partial last step
+  // needs no clamping and no per-lane path, and no row outside the split
+  // (unwritten cache slots included) is ever read.
   const T *kpast = (const T *)p.past_k + ((int64_t)b * p.Hkv + g) * p.past_rows * D;
   const T *vpast = (const T *)p.past_v + ((int64_t)b * p.Hkv + g) * p.past_rows * D;
-  const T *knew = (const T *)p.k + b * p.k_sb + g * p.k_sh;
-  const T *vnew = (const T *)p.v + b * p.v_sb + g * p.v_sh;
+  const uint32_t nrec = (uint32_t)max(sp_hi - sp_lo, 0) * (uint32_t)VRB;
+  const __amdgpu_buffer_rsrc_t krs = row_rsrc(kpast + (int64_t)sp_lo * D, nrec);
+  const __amdgpu_buffer_rsrc_t vrs = row_rsrc(vpast + (int64_t)sp_lo * D, nrec);
 
   // V registers: key 2 t + lane / 32, dims 4 (lane % 32) .. + 3 (8 bytes);
   // written to LDS at row 2 t + lane / 32, chunk (lane % 32) / 2, half lane & 1
@@ -428,42 +451,18 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p, DPlan p
   const int trr = 4 * kq + ((lane & 15) >> 2);
   const uint32_t tro = (uint32_t)(trr * VRB + 16 * (((lane & 3) >> 1)) + 8 * (lane & 1));
   const int trx = trr & 7;
+  // lane byte offsets within a step: K row n, 16-byte piece kq of each 64-byte
+  // k-step; V rows 2 t + vpar, 8 bytes at dim vcol
+  const uint32_t koff = (uint32_t)n * VRB + (uint32_t)kq * 16u;
+  const uint32_t voff = (uint32_t)vpar * VRB + (uint32_t)vcol * (uint32_t)sizeof(T);
+  const int my_steps = n_steps > wave ? (n_steps - wave + 3) / 4 : 0;
 
   auto load_step = [&](int st, uint4 (&kk)[NKS], uint2 (&vv)[kStep / 2]) __attribute__((always_inline)) {
-    const int j0 = base + (wave + 4 * st) * kStep;
-    const bool full = j0 >= sp_lo && j0 + kStep <= sp_hi;
-    if (full && (j0 >= s.src || j0 + kStep <= s.src)) {
-      // the whole step from one source: uniform base + 32-bit lane offsets
-      const bool from_new = j0 >= s.src;
-      const char *kb = (const char *)(from_new ? knew + (int64_t)(j0 - s.src) * p.k_ss
-                                               : kpast + (int64_t)j0 * D);
-      const char *vb = (const char *)(from_new ? vnew + (int64_t)(j0 - s.src) * p.v_ss
-                                               : vpast + (int64_t)j0 * D);
-      const uint32_t krs = (uint32_t)(from_new ? p.k_ss : D) * (uint32_t)sizeof(T);
-      const uint32_t vrs = (uint32_t)(from_new ? p.v_ss : D) * (uint32_t)sizeof(T);
-      const uint32_t koff = (uint32_t)n * krs + (uint32_t)kq * 16u;
+    const uint32_t so = (uint32_t)((wave + 4 * st) * kStep * VRB);
 #pragma unroll
-      for (int s2 = 0; s2 < NKS; ++s2) kk[s2] = ld_stream16(kb + koff + s2 * 64);
-      const uint32_t voff = (uint32_t)vpar * vrs + (uint32_t)vcol * (uint32_t)sizeof(T);
+    for (int s2 = 0; s2 < NKS; ++s2) kk[s2] = ld_buf16(krs, koff + so + s2 * 64);
 #pragma unroll
-      for (int t = 0; t < kStep / 2; ++t) vv[t] = ld_stream8(vb + voff + 2 * t * vrs);
-      return;
-    }
-    // Steps that straddle the range or the past/new boundary: per-lane rows;
-    // rows outside [sp_lo, sp_hi) load row sp_lo (valid memory, finite
-    // values; their scores are masked, so their P is exactly 0).
-    auto row_ptr = [&](const T *pastp, const T *newp, int64_t new_ss, int j) {
-      const int jj = j >= sp_lo && j < sp_hi ? j : sp_lo;
-      const bool nw = jj >= s.src;
-      const int64_t off_new = (int64_t)(jj - s.src) * new_ss, off_past = (int64_t)jj * D;
-      return (nw ? newp : pastp) + (nw ? off_new : off_past);
-    };
-    const T *ks = row_ptr(kpast, knew, p.k_ss, j0 + n);
-#pragma unroll
-    for (int s2 = 0; s2 < NKS; ++s2) kk[s2] = *(const uint4 *)(ks + s2 * 32 + kq * 8);
-#pragma unroll
-    for (int t = 0; t < kStep / 2; ++t)
-      vv[t] = *(const uint2 *)(row_ptr(vpast, vnew, p.v_ss, j0 + 2 * t + vpar) + vcol);
+    for (int t = 0; t < kStep / 2; ++t) vv[t] = ld_buf8(vrs, voff + so + 2 * t * VRB);
   };
 
   float m = kNegInf, l = 0.f;
@@ -472,7 +471,6 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p, DPlan p
   for (int blk = 0; blk < NBLK; ++blk) o[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float sl = p.scale * kLog2e;
 
-  const int my_steps = n_steps > wave ? (n_steps - wave + 3) / 4 : 0;
   uint4 k0[NKS], k1[NKS], k2[NKS];
   uint2 v0[kStep / 2], v1[kStep / 2], v2[kStep / 2];
   char *vl = (char *)vbw[wave];
@@ -537,12 +535,14 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p, DPlan p
       o[blk] = mma16k16(__builtin_bit_cast(vec4, a), pb, o[blk]);
     }
   };
-  if (my_steps > 0) load_step(0, k0, v0);
-  if (my_steps > 1) load_step(1, k1, v1);
-  for (int it = 0; it < my_steps; it += 3) {
-    body(it, k0, v0, k2, v2);
-    if (it + 1 < my_steps) body(it + 1, k1, v1, k0, v0);
-    if (it + 2 < my_steps) body(it + 2, k2, v2, k1, v1);
+  if (n_steps > 0) {
+    if (my_steps > 0) load_step(0, k0, v0);
+    if (my_steps > 1) load_step(1, k1, v1);
+    for (int it = 0; it < my_steps; it += 3) {
+      body(it, k0, v0, k2, v2);
+      if (it + 1 < my_steps) body(it + 1, k1, v1, k0, v0);
+      if (it + 2 < my_steps) body(it + 2, k2, v2, k1, v1);
+    }
   }
 
   // ---- wave partials -> LDS: m, l per slot (from the 4 lanes of each slot) ----
@@ -607,11 +607,12 @@ hipError_t launch_nr(const Params &p, const DPlan &pl, int nr, dim3 grid, hipStr
 
 }  // namespace
 
-// The decode kernel takes every (query, head) row of one KV head in 16 slots.
+// The decode kernel takes every (query, head) row of one KV head in 16 slots;
+// at head size 128 it reads every key from the past buffer (keys_in_past).
 bool decode_supports(const Params &p, int dtype) {
   return (dtype == DT_F16 || dtype == DT_BF16) && p.D == p.Dv && (p.D == 64 || p.D == 128) &&
          p.G * p.S <= 16 && !p.bias && !p.mask && !(p.softcap > 0.f) && p.scale > 0.f &&
-         !p.proj_bias && !p.qk_out;
+         !p.proj_bias && !p.qk_out && (p.D == 64 || p.keys_in_past);
 }
 
 hipError_t launch_decode(const Params &p, int dtype, int split_keys, int n_split, float *ws,
