@@ -210,6 +210,41 @@ def test_fwd_equals_decode_and_is_deterministic():
     np.testing.assert_allclose(y_logical(p, ys[0]), y_logical(p, ys[2]), atol=2e-2)
 
 
+def test_decode_kernel_poisoned_cache_tail():
+    # In-place KV cache whose slots from each batch's past length on hold NaN
+    # (the new step overwrites the first of them).  The decode kernel reads
+    # only the key rows of its splits, so Y is finite, equal to the clean
+    # cache's Y and to the oracle's.
+    p = SMALL["gqa_decode_f16"]
+    inp = make_inputs(p, 92)
+    dev = to_dev(inp)
+    lens = inp["lens"].numpy()
+
+    def cache(poison):
+        pk = torch.zeros((p.B, p.Hkv, p.T, p.D), dtype=p.torch_dtype, device="cuda")
+        pv = torch.zeros((p.B, p.Hkv, p.T, p.Dv), dtype=p.torch_dtype, device="cuda")
+        pk[:, :, : p.P] = dev["past_k"]
+        pv[:, :, : p.P] = dev["past_v"]
+        if poison:
+            for b in range(p.B):
+                past = int(lens[b]) + 1 - p.S
+                pk[b, :, past:] = float("nan")
+                pv[b, :, past:] = float("nan")
+        return pk, pv
+
+    run = {k: v for k, v in dev.items() if k not in ("past_k", "past_v")}
+    ys = []
+    for poison in (False, True):
+        pk, pv = cache(poison)
+        _say(f"[parity] decode kernel, poisoned cache tail={poison}")
+        c = _run(p, run, mode="decode", kv_inplace=True, present_k=pk, present_v=pv)
+        assert olk.olk_last_kernel_name() == "olk_decode_split+combine"
+        ys.append(c.y.clone())
+    assert torch.isfinite(ys[1].float()).all()
+    assert torch.equal(ys[0], ys[1])
+    assert_close(p, y_logical(p, ys[1]), olk_ref.attention(p, inp))
+
+
 def test_poisoned_padding_and_guard_bands():
     # Cache slots beyond each batch's valid past hold NaN; outputs sit inside
     # guard bands.  Y must stay finite and equal the clean run; nothing may be
