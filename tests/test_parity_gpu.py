@@ -198,6 +198,25 @@ def test_decode_inplace_cache_append():
     assert_present_exact(p, inp, c.present_k, c.present_v)
 
 
+@pytest.mark.parametrize("name", ["gqa_decode_f16", "gqa_decode_rows8_bf16",
+                                  "gqa_decode_rows16_f16", "gqa_decode_8k_bf16"])
+def test_small_decode_inplace(name):
+    # in-place KV cache at head size 128: the decode kernel appends the new
+    # rows itself; Y against the oracle, present bit-exact over [0, total_b)
+    p = SMALL[name]
+    inp = make_inputs(p, 700 + list(SMALL).index(name))
+    dev = to_dev(inp)
+    pk = dev["past_k"].new_zeros((p.B, p.Hkv, p.T, p.D))
+    pv = dev["past_v"].new_zeros((p.B, p.Hkv, p.T, p.Dv))
+    pk[:, :, : p.P] = dev.pop("past_k")
+    pv[:, :, : p.P] = dev.pop("past_v")
+    _say(f"[parity] {name} decode in place")
+    c = _run(p, dev, mode="decode", kv_inplace=True, present_k=pk, present_v=pv)
+    assert olk.olk_last_kernel_name() == "olk_decode_split+combine"
+    assert_close(p, y_logical(p, c.y), olk_ref.attention(p, inp))
+    assert_present_exact(p, inp, c.present_k, c.present_v)
+
+
 def test_fwd_equals_decode_and_is_deterministic():
     p = SMALL["gqa_past_f16"]
     inp = make_inputs(p, 77)

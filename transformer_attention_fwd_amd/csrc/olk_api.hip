@@ -21,8 +21,9 @@ hipError_t launch_tiled_split(const Params &p, int dtype, int split_tiles, float
                               hipStream_t st);
 bool tiled_supports(const Params &p, int dtype);
 bool decode_supports(const Params &p, int dtype);
+bool decode_appends(const Params &p, int dtype);
 hipError_t launch_decode(const Params &p, int dtype, int split_keys, int n_split, float *ws,
-                         hipStream_t st);
+                         bool append, hipStream_t st);
 }  // namespace olk
 
 namespace {
@@ -416,8 +417,18 @@ olk_status olk_attention_decode(const olk_attn_desc *desc, const olk_attn_io *io
   // the split-KV partial kernels take no attn_mask: masks go to the generic split
   const bool tiled_ok = olk::tiled_supports(pa, desc->dtype) && !pa.mask;
   if (desc->kernel == OLK_KERNEL_TILED && !tiled_ok) return OLK_E_UNSUPPORTED;
+  // In place at head size 128 the decode kernel appends the new rows itself
+  // (no separate copy launch); every other case appends before the split kernels.
+  bool append_in_decode = false;
+  if (!desc->do_rotary && !kv_bias_path(desc, io) && desc->kernel != OLK_KERNEL_GENERIC &&
+      tiled_ok && p.kv_inplace) {
+    olk::Params pk = p;
+    pk.keys_in_past = 1;
+    append_in_decode = olk::decode_appends(pk, desc->dtype);
+  }
   hipError_t e = desc->do_rotary        ? rotary_prepass(p, desc->dtype, s)
                  : kv_bias_path(desc, io) ? kv_bias_prepass(p, desc->dtype, s)
+                 : append_in_decode       ? hipSuccess
                                           : olk::launch_present(p, desc->dtype, s);
   if (e != hipSuccess) return OLK_E_HIP;
   if (!p.keys_in_past && p.present_k && p.present_v) {
@@ -433,7 +444,8 @@ olk_status olk_attention_decode(const olk_attn_desc *desc, const olk_attn_io *io
   int n_comb = n_split;
   if (desc->kernel != OLK_KERNEL_GENERIC && tiled_ok && olk::decode_supports(p, desc->dtype)) {
     n_comb = n_splits(desc, kDecodeSplitKeys);
-    e = olk::launch_decode(p, desc->dtype, kDecodeSplitKeys, n_comb, (float *)workspace, s);
+    e = olk::launch_decode(p, desc->dtype, kDecodeSplitKeys, n_comb, (float *)workspace,
+                           append_in_decode, s);
     g_last_kernel = "olk_decode_split+combine";
   } else if (desc->kernel != OLK_KERNEL_GENERIC && tiled_ok) {
     e = olk::launch_tiled_split(p, desc->dtype, kSplitKeys / 64, (float *)workspace, s);

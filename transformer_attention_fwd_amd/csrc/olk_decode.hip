@@ -111,6 +111,7 @@ struct DPlan {
   int n_split;     // splits per (batch, KV head)
   int split_keys;  // keys per split (multiple of 4 * kStep)
   float *ws;       // records [m, l, -, -, O[Dv]] per (row, split)
+  int append;      // in-place cache: the kernel writes the new rows itself
 };
 
 // NR: row slots (G * S) rounded up to a power of two <= 16.
@@ -403,6 +404,28 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p, DPlan p
   const Seq s = seq_info(p, b);
   const int nrows = p.G * p.S;
 
+  if (pl.append) {
+    // In-place cache (present is the past buffer): the new rows [past_b,
+    // total_b) that fall in this split's key range are copied from the new
+    // K/V here, and the barrier's workgroup fence makes them visible to the
+    // loads below; one workgroup per (split, b, KV head) owns each row.
+    const int r0 = max(s.past, split * pl.split_keys);
+    const int r1 = min(s.total, (split + 1) * pl.split_keys);
+    if (r0 < r1) {
+      T *kc = (T *)p.past_k + ((int64_t)b * p.Hkv + g) * p.past_rows * D;
+      T *vc = (T *)p.past_v + ((int64_t)b * p.Hkv + g) * p.past_rows * D;
+      for (int t = tid; t < (r1 - r0) * (D / 8); t += kThreads) {
+        const int r = r0 + t / (D / 8), c = 8 * (t % (D / 8));
+        const int64_t i = r - s.past;
+        *(uint4 *)(kc + (int64_t)r * D + c) =
+            *(const uint4 *)((const T *)p.k + b * p.k_sb + i * p.k_ss + g * p.k_sh + c);
+        *(uint4 *)(vc + (int64_t)r * D + c) =
+            *(const uint4 *)((const T *)p.v + b * p.v_sb + i * p.v_ss + g * p.v_sh + c);
+      }
+      __syncthreads();
+    }
+  }
+
   // key range of the workgroup: union over its rows, cut to the split
   const int pos_min = s.qoff, pos_max = s.qoff + p.S - 1;
   int hi = p.pad_add ? s.total : s.valid;
@@ -615,12 +638,20 @@ bool decode_supports(const Params &p, int dtype) {
          !p.proj_bias && !p.qk_out && (p.D == 64 || p.keys_in_past);
 }
 
+// Head size 128 in place (present is the past buffer, every key read from
+// it): the decode kernel can append the new rows itself.
+bool decode_appends(const Params &p, int dtype) {
+  return decode_supports(p, dtype) && p.D == 128 && p.kv_inplace && p.keys_in_past;
+}
+
 hipError_t launch_decode(const Params &p, int dtype, int split_keys, int n_split, float *ws,
-                         hipStream_t st) {
+                         bool append, hipStream_t st) {
+  if (append && !decode_appends(p, dtype)) return hipErrorInvalidValue;
   DPlan pl;
   pl.n_split = n_split;
   pl.split_keys = split_keys;
   pl.ws = ws;
+  pl.append = append ? 1 : 0;
   const int64_t n = (int64_t)p.B * p.Hkv * n_split;
   if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)n);
