@@ -390,7 +390,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p, DPlan p
   typedef typename DV4<T>::v4 vec4;
   constexpr int NKS = D / 32;   // k-steps of QK^T (32 dims each)
   constexpr int NBLK = D / 16;  // 16-dim blocks of O^T
-  constexpr int VRB = D * 2;    // bytes per V row in LDS
+  constexpr int VRB = D * 2;    // bytes per K/V row, in memory and in LDS
   // V rows of the current step, one tile per wavefront
   __shared__ __attribute__((aligned(16))) T vbw[4][kStep * D];
   __shared__ __attribute__((aligned(16))) float mrg_ml[4][2][16];
@@ -454,7 +454,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p, DPlan p
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // Q in registers (vmcnt(0) only)
 
-  // Every key is in the past buffer (the present append ran first). The
+  // Every key is in the past buffer (the present append ran before this
+  // kernel, or above for the in-place cache). The
   // split's rows [sp_lo, sp_hi) are read through buffer descriptors based at
   // row sp_lo and sized to the split: rows at or past sp_hi read as zeros
   // without a memory access (range-checked offsets), so a partial last step
@@ -497,7 +498,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p, DPlan p
   uint4 k0[NKS], k1[NKS], k2[NKS];
   uint2 v0[kStep / 2], v1[kStep / 2], v2[kStep / 2];
   char *vl = (char *)vbw[wave];
-  // this lane's 8-byte V pieces: row 2 t + vpar at byte vwo + 512 t
+  // this lane's 8-byte V pieces are rows 2 t + vpar of the step
   const int vwr = vpar;  // row parity; rows 2 t + vpar have (row & 7) = (2 t + vpar) & 7
   auto body = [&](int it, uint4 (&kr)[NKS], const uint2 (&vr)[kStep / 2], uint4 (&kf)[NKS],
                   uint2 (&vf)[kStep / 2]) __attribute__((always_inline)) {
