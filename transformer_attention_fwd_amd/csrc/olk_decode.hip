@@ -467,26 +467,25 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p, DPlan p
   const __amdgpu_buffer_rsrc_t krs = row_rsrc(kpast + (int64_t)sp_lo * D, nrec);
   const __amdgpu_buffer_rsrc_t vrs = row_rsrc(vpast + (int64_t)sp_lo * D, nrec);
 
-  // V registers: key 2 t + lane / 32, dims 4 (lane % 32) .. + 3 (8 bytes);
-  // written to LDS at row 2 t + lane / 32, chunk (lane % 32) / 2, half lane & 1
-  const int vcol = 4 * (lane & 31), vpar = lane >> 5;
+  // V registers: row 4 t + lane / 16 of the step, 16-byte chunk lane % 16;
+  // written to LDS at that row, slot chunk ^ 2 (row & 7)
   // transposed reads: this lane addresses row 4 (l / 16) + (l % 16) / 4 and
   // dims 16 blk + 4 ((l % 16) & 3), i.e. byte tro + 32 (blk ^ (row & 7))
   const int trr = 4 * kq + ((lane & 15) >> 2);
   const uint32_t tro = (uint32_t)(trr * VRB + 16 * (((lane & 3) >> 1)) + 8 * (lane & 1));
   const int trx = trr & 7;
   // lane byte offsets within a step: K row n, 16-byte piece kq of each 64-byte
-  // k-step; V rows 2 t + vpar, 8 bytes at dim vcol
+  // k-step; V row lane / 16 (+ 4 t), chunk lane % 16
   const uint32_t koff = (uint32_t)n * VRB + (uint32_t)kq * 16u;
-  const uint32_t voff = (uint32_t)vpar * VRB + (uint32_t)vcol * (uint32_t)sizeof(T);
+  const uint32_t voff = (uint32_t)(lane >> 4) * VRB + (uint32_t)(lane & 15) * 16u;
   const int my_steps = n_steps > wave ? (n_steps - wave + 3) / 4 : 0;
 
-  auto load_step = [&](int st, uint4 (&kk)[NKS], uint2 (&vv)[kStep / 2]) __attribute__((always_inline)) {
+  auto load_step = [&](int st, uint4 (&kk)[NKS], uint4 (&vv)[kStep / 4]) __attribute__((always_inline)) {
     const uint32_t so = (uint32_t)((wave + 4 * st) * kStep * VRB);
 #pragma unroll
     for (int s2 = 0; s2 < NKS; ++s2) kk[s2] = ld_buf16(krs, koff + so + s2 * 64);
 #pragma unroll
-    for (int t = 0; t < kStep / 2; ++t) vv[t] = ld_buf8(vrs, voff + so + 2 * t * VRB);
+    for (int t = 0; t < kStep / 4; ++t) vv[t] = ld_buf16(vrs, voff + so + 4 * t * VRB);
   };
 
   float m = kNegInf, l = 0.f;
@@ -496,12 +495,10 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p, DPlan p
   const float sl = p.scale * kLog2e;
 
   uint4 k0[NKS], k1[NKS], k2[NKS];
-  uint2 v0[kStep / 2], v1[kStep / 2], v2[kStep / 2];
+  uint4 v0[kStep / 4], v1[kStep / 4], v2[kStep / 4];
   char *vl = (char *)vbw[wave];
-  // this lane's 8-byte V pieces are rows 2 t + vpar of the step
-  const int vwr = vpar;  // row parity; rows 2 t + vpar have (row & 7) = (2 t + vpar) & 7
-  auto body = [&](int it, uint4 (&kr)[NKS], const uint2 (&vr)[kStep / 2], uint4 (&kf)[NKS],
-                  uint2 (&vf)[kStep / 2]) __attribute__((always_inline)) {
+  auto body = [&](int it, uint4 (&kr)[NKS], const uint4 (&vr)[kStep / 4], uint4 (&kf)[NKS],
+                  uint4 (&vf)[kStep / 4]) __attribute__((always_inline)) {
     if (it + 2 < my_steps) load_step(it + 2, kf, vf);
     const int j0 = base + (wave + 4 * it) * kStep;
     // S^T (16 keys x 16 slots)
@@ -546,10 +543,10 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p, DPlan p
     l += lsum;  // lane-local partial of slot n
     // the step's V rows into this wavefront's LDS tile (swizzled chunks)
 #pragma unroll
-    for (int t = 0; t < kStep / 2; ++t) {
-      const int r = 2 * t + vwr;
-      const int c = (lane & 31) >> 1;
-      *(uint2 *)(vl + r * VRB + 16 * (c ^ (2 * (r & 7))) + 8 * (lane & 1)) = vr[t];
+    for (int t = 0; t < kStep / 4; ++t) {
+      const int r = 4 * t + (lane >> 4);
+      const int c = lane & 15;
+      *(uint4 *)(vl + r * VRB + 16 * (c ^ (2 * (r & 7)))) = vr[t];
     }
     // PV on the matrix cores
 #pragma unroll
