@@ -63,7 +63,7 @@ def allowed_pairs(p, inputs) -> np.ndarray:
             valid = total
         else:
             total = p.T
-            qoff = total - p.S
+            qoff = p.P
             valid = int(tot[b]) if (p.op == "attention" or p.mask_filter_value <= -5000) else total
             if p.op == "mha" and valid == 0:
                 valid = total

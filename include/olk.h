@@ -94,8 +94,14 @@ typedef struct {
   int32_t v_head_size;       /* Dv */
   int32_t q_rank;            /* 3: Q (B,S,Hq*D), Y (B,S,Hq*Dv); 4 (Attention only): Q (B,Hq,S,D), Y (B,Hq,S,Dv) */
   int32_t kv_rank;           /* 3: K (B,L,Hkv*D), V (B,L,Hkv*Dv); 4 (MHA/Attention): K (B,Hkv,L,D), V (B,Hkv,L,Dv) */
-  int32_t causal;            /* 0/1: GQA causal, MHA unidirectional, Attention is_causal;
-                                bottom-right aligned (query i at position past_b + i) */
+  int32_t causal;            /* 0/1: GQA causal, MHA unidirectional, Attention is_causal.
+                                Query i sits at position past_b + i, past_b = the cached
+                                keys in front of the new ones (GQA: seqlens_k + 1 - S;
+                                MHA / Attention: P): every cached key is visible and new
+                                key j iff j <= i, i.e. the mask is aligned to the
+                                upper-left corner of the new keys and shifted by the
+                                cache (reference kernels header page, "class Attention",
+                                is_causal) */
   int32_t local_window_size; /* GroupQueryAttention only: -1 = full; W > 0 attends the
                                 current key and up to W-1 preceding; needs causal = 1 */
   int32_t has_scale;         /* 0: scale = 1/sqrt(D) */
@@ -173,13 +179,26 @@ typedef struct {
 
 /*
  * Host-only check of desc and io (no GPU is touched).  Returns the status the
- * compute entry points would return before launching.
+ * compute entry points would return before launching.  The rejections follow
+ * the operator contracts: local_window_size 0, below -1, or with causal = 0
+ * (onnx-light-cpu Python API page "Custom operators", section "Microsoft
+ * GroupQueryAttention"); MultiHeadAttention takes one head count, rank-3 or
+ * rank-4 K/V and no head_sink, and has no slot for the inputs that section
+ * ("Microsoft MultiHeadAttention") lists as explicitly unsupported (packed
+ * rank-5 inputs, shared-buffer inputs, the qk output); q_num_heads must be a
+ * multiple of kv_num_heads (reference kernels header page, "class
+ * Attention").  OLK_E_NULL for a missing required pointer, OLK_E_ATTR for a
+ * rejected attribute, OLK_E_SHAPE for inconsistent sizes or overlapping
+ * buffers, OLK_E_UNSUPPORTED for valid shapes this library does not take.
  */
 olk_status olk_validate(const olk_attn_desc *desc, const olk_attn_io *io);
 
 /*
  * Bytes of workspace olk_attention_decode needs for this desc (0 when the
- * call needs none).  Depends only on sizes, never on device data.
+ * call needs none): one float record (m, l, O[Dv]) per query row and key chunk
+ * of its split-KV decomposition.  The decomposition is ours (the pages
+ * describe CPU kernels); the size depends only on sizes, never on device data.
+ * Returns 0 for a NULL desc.
  */
 size_t olk_workspace_bytes(const olk_attn_desc *desc);
 
@@ -188,16 +207,23 @@ size_t olk_workspace_bytes(const olk_attn_desc *desc);
  * shapes).  Computes Y and, when requested, present_key/present_value
  * (onnx-light reference kernels header page, "class Attention", comprehensive
  * overload and Result; GroupQueryAttention and MultiHeadAttention sections of
- * the onnx-light-cpu Python API page).  Needs no workspace.
- * `stream` is a hipStream_t.
+ * the onnx-light-cpu Python API page).  Takes no workspace: each kernel it
+ * launches keeps a row's softmax state in registers over all of the row's
+ * keys and writes only Y, present and the qk output, so nothing is left to
+ * merge in memory.  `stream` is a hipStream_t.  Errors: as olk_validate, and
+ * OLK_E_UNSUPPORTED when OLK_KERNEL_TILED is forced on a shape the matrix-core
+ * kernels do not take; OLK_E_HIP reports a failed launch.
  */
 olk_status olk_attention_fwd(const olk_attn_desc *desc, const olk_attn_io *io, void *stream);
 
 /*
  * Same result as olk_attention_fwd, computed split-KV for short query
- * sequences against long key sequences (decode): the keys of each (batch, KV
- * head) are cut into chunks whose partial softmax states are merged by a
- * second kernel.  workspace: device memory of at least
+ * sequences against long key sequences (decode against a KV cache: present =
+ * the entire past cache followed by the current step, and a head_sink logit
+ * adds to the denominator only; onnx-light-cpu Python API page "Custom
+ * operators", section "Microsoft GroupQueryAttention").  The keys of each
+ * (batch, KV head) are cut into chunks whose partial softmax states are merged
+ * by a second kernel, which also adds the sink (the decomposition is ours).  workspace: device memory of at least
  * olk_workspace_bytes(desc) bytes, 16-byte aligned, owned by the caller; its
  * contents on entry do not matter.  `stream` is a hipStream_t.  Errors: as
  * olk_validate; OLK_E_WORKSPACE for a missing, short or misaligned
@@ -240,10 +266,15 @@ size_t olk_bwd_workspace_bytes(const olk_attn_desc *desc);
 olk_status olk_attention_bwd(const olk_attn_desc *desc, const olk_attn_bwd_io *io,
                              void *workspace, size_t workspace_bytes, void *stream);
 
-/* Static string naming a status. */
+/* Static string naming a status (ours); never NULL, "unknown status" for a
+ * value outside olk_status. */
 const char *olk_status_str(olk_status status);
 
-/* Name of the last kernel this thread launched through the library ("" if none). */
+/* Name of the kernels the last call on this thread launched ("" if none), a
+ * static string owned by the library.  It tells which implementation ran, as
+ * each onnx-light-cpu kernel carries a unique name it can record when it runs
+ * (onnx-light-cpu design page "Registering kernels", section "Checking which
+ * kernels are used"); here the record is one per thread, always on. */
 const char *olk_last_kernel_name(void);
 
 #ifdef __cplusplus

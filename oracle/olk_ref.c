@@ -30,8 +30,12 @@
  * Readings where the pages leave a step open (each is listed in the design
  * notes with its support):
  *   R1  GroupQueryAttention seqlens_k[b] = total_b - 1, past_b = total_b - S.
- *   R3  causal alignment is bottom-right: query i sits at absolute position
- *       past_b + i (GQA) or T - S + i (MHA / Attention).
+ *   R3  causal alignment: query i sits at absolute position past_b + i, where
+ *       past_b is the number of cached keys in front of the new ones (GQA:
+ *       the valid past of batch b; MHA / Attention: the past buffer length
+ *       P).  For Attention the header page aligns the causal mask to the
+ *       upper-left corner of the score matrix and shifts it by the cached KV:
+ *       query i attends every cached key and the new keys 0..i.
  *   R4  window W > 0 allows keys j with pos_i - W + 1 <= j <= pos_i.
  *   R5  query head h reads KV head h / (Hq / Hkv).
  *   R6  order: scale, + bias, softcap, then masks as exclusion.
@@ -246,7 +250,7 @@ static int seq_info(const ref_desc *d, const ref_inputs *in, int b, seqinfo *s) 
     /* MHA / Attention: literal concatenation of the whole past buffer. */
     s->total_b = T;
     s->past_b = d->past_seq;
-    s->q_off = T - d->q_seq;
+    s->q_off = d->past_seq; /* R3: upper-left, shifted by the cache */
     s->valid_b = T;
     s->pad_b = T;
     if (in->lens) {

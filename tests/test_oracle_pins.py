@@ -66,7 +66,7 @@ def sdpa_reference(p: Problem, inp) -> np.ndarray:
         K = torch.cat(parts_k, dim=1)[:, :total].repeat_interleave(G, dim=0)
         V = torch.cat(parts_v, dim=1)[:, :total].repeat_interleave(G, dim=0)
         mask = torch.zeros(p.Hq, p.S, total, dtype=torch.float64)
-        pos = (past if p.op == "gqa" else total - p.S) + torch.arange(p.S).view(-1, 1)
+        pos = past + torch.arange(p.S).view(-1, 1)
         j = torch.arange(total).view(1, -1)
         if p.causal:
             mask = mask.masked_fill((j > pos).unsqueeze(0), float("-inf"))
@@ -457,6 +457,110 @@ def test_window_2048_attends_current_and_2047_preceding():
 
 
 # ---------------------------------------------------------------------------
+# R3: causal alignment.  The reference kernels header page ("class Attention",
+# is_causal) aligns the mask to the upper-left corner of the score matrix and
+# accounts for cached keys: every cached key is visible, and among the new keys
+# query i sees keys 0..i.  Without a cache that is the convention of torch's
+# scaled_dot_product_attention(is_causal=True) (a lower triangle from the
+# top-left corner), used here as the library routine.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("op,S,L", [("attention", 5, 9), ("attention", 9, 5),
+                                    ("attention", 6, 6), ("mha", 4, 10), ("mha", 10, 4)])
+def test_causal_without_cache_is_torch_upper_left_is_causal(op, S, L):
+    p = Problem(op=op, dtype="f32", B=2, S=S, L=L, Hq=2, Hkv=2 if op == "mha" else 1,
+                D=8, Dv=8, causal=1, has_lens=False)
+    inp = make_inputs(p, 300 + 10 * S + L)
+    q = _bnsh_q(p, inp["q"])
+    G = p.Hq // p.Hkv
+    k = _bnsh_kv(p, inp["k"], p.D).repeat_interleave(G, dim=1)
+    v = _bnsh_kv(p, inp["v"], p.Dv).repeat_interleave(G, dim=1)
+    want = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True)
+    np.testing.assert_allclose(olk_ref.attention(p, inp), want.permute(0, 2, 1, 3).numpy(),
+                               rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("op,S,L,P", [("attention", 5, 8, 4), ("attention", 8, 3, 6),
+                                      ("mha", 3, 7, 5), ("attention", 1, 1, 9)])
+def test_causal_with_cache_sees_every_cached_key(op, S, L, P):
+    p = Problem(op=op, dtype="f32", B=2, S=S, L=L, P=P, Hq=2, Hkv=2, D=8, Dv=8, causal=1,
+                has_lens=False)
+    inp = make_inputs(p, 400 + S + L + P)
+    q = _bnsh_q(p, inp["q"])
+    k = torch.cat([_f64(inp["past_k"]), _bnsh_kv(p, inp["k"], p.D)], dim=2)
+    v = torch.cat([_f64(inp["past_v"]), _bnsh_kv(p, inp["v"], p.Dv)], dim=2)
+    allow = torch.cat([torch.ones(S, P, dtype=torch.bool),
+                       torch.ones(S, L, dtype=torch.bool).tril()], dim=1)
+    want = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=allow)
+    np.testing.assert_allclose(olk_ref.attention(p, inp), want.permute(0, 2, 1, 3).numpy(),
+                               rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# R7: the head sink is a raw logit (Python API page, GroupQueryAttention
+# head_sink: a virtual softmax logit that adds to the denominator only).  With
+# a tiny softcap every real score saturates to +-cap, so the weights have a
+# closed form that uses z itself, neither scaled nor capped.
+# ---------------------------------------------------------------------------
+
+def test_sink_is_neither_scaled_nor_softcapped():
+    p = Problem(op="gqa", dtype="f32", B=1, S=1, L=1, P=5, Hq=1, Hkv=1, D=4, Dv=4,
+                causal=1, has_sink=True, softcap=0.5, scale=2.0)
+    inp = make_inputs(p, 88, lens=np.array([5]))
+    signs = np.array([1, -1, -1, 1, 1, -1], dtype=np.float64)   # keys 0..5 (5 = new)
+    inp["q"] = torch.tensor([[[100.0, 0.0, 0.0, 0.0]]])
+    pk = torch.zeros(1, 1, 5, 4)
+    pk[0, 0, :, 0] = torch.tensor(signs[:5] * 3.0, dtype=torch.float32)
+    inp["past_k"] = pk
+    inp["k"] = torch.tensor([[[signs[5] * 3.0, 0.0, 0.0, 0.0]]], dtype=torch.float32)
+    inp["sink"] = torch.tensor([3.0])
+    w, sw = olk_ref.row_weights(p, inp, 0, 0, 0)
+    e = np.exp(0.5 * signs)
+    den = e.sum() + math.exp(3.0)
+    np.testing.assert_allclose(w, e / den, rtol=1e-12)
+    np.testing.assert_allclose(sw, math.exp(3.0) / den, rtol=1e-12)
+    # a capped (0.5 tanh 6 ~ 0.49999) or scaled (6) sink would take a share of
+    # about 0.20 or 0.98 instead of 0.75
+    assert 0.74 < sw < 0.76
+
+
+# ---------------------------------------------------------------------------
+# Rounding of element-type tensors the oracle produces itself (R21 biased K/V
+# rows, R18 rotated rows): float32 -> binary16 / bfloat16 round to nearest
+# even, against torch's conversion over every 16-bit pattern of K plus
+# projection-bias values that land on ties, subnormals and overflow.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_element_rounding_of_biased_rows_is_round_to_nearest_even(dt):
+    D = 16
+    p = Problem(op="mha", dtype=dt, B=1, S=1, L=65536 // D, Hq=1, Hkv=1, D=D, Dv=D,
+                kv_rank=3, causal=0, has_lens=False, has_proj_bias=True)
+    inp = make_inputs(p, 90)
+    tdt = p.torch_dtype
+    bits = torch.arange(-32768, 32768, dtype=torch.int32).to(torch.int16)
+    inp["k"] = bits.view(tdt).view(1, p.L, D).contiguous()
+    inp["v"] = bits.flip(0).view(tdt).view(1, p.L, D).contiguous()
+    seg = [0.0, 2.0 ** -11, -2.0 ** -11, 3 * 2.0 ** -12, 2.0 ** -24, -2.0 ** -24, 2.0 ** -14,
+           0.5, 1.5, 32.0, -32.0, 1000.0, 2.0 ** -20, 7.0e-5, 3.0, 2.0 ** -9]
+    if dt == "bf16":
+        seg[4:6] = [2.0 ** -133, -2.0 ** -133]   # bfloat16 subnormals
+        seg[9:11] = [2.0 ** 120, -2.0 ** 120]    # overflow near the float32 range end
+    segv = torch.tensor(seg, dtype=torch.float32).to(tdt)
+    pb = torch.zeros(3 * D, dtype=tdt)
+    pb[D:2 * D] = segv
+    pb[2 * D:] = segv.flip(0)
+    inp["proj_bias"] = pb
+    got_k, got_v = olk_ref.present(p, inp, fill=0.0)
+    for got, x, b in ((got_k, inp["k"], pb[D:2 * D]), (got_v, inp["v"], pb[2 * D:])):
+        want = (x.float() + b.float()).to(tdt).view(1, 1, p.L, D)
+        nan = torch.isnan(want.float())
+        assert torch.equal(torch.isnan(got.float()), nan)
+        gi, wi = got.view(torch.int16)[~nan], want.view(torch.int16)[~nan]
+        assert torch.equal(gi, wi), f"{(gi != wi).sum().item()} elements differ"
+
+
+# ---------------------------------------------------------------------------
 # Rotary embedding (GroupQueryAttention do_rotary; RotaryEmbedding of the
 # reference kernels header page, after arXiv 2104.09864).
 # ---------------------------------------------------------------------------
@@ -689,6 +793,38 @@ def test_qk_output_modes():
     for (b, h, i) in ((0, 0, 0), (1, 3, 6), (0, 2, 4)):
         w, _ = olk_ref.row_weights(p, inp, b, h, i)
         np.testing.assert_allclose(m3[b, h, i, : len(w)], w, rtol=0, atol=0)
+    # The weights Y uses are the softmax, over the allowed keys, of the mode-2
+    # scores (scale, + bias, softcap: the page's stage order), and Y is those
+    # weights applied to V.  A Y path that capped before adding the bias, or
+    # dropped a stage, fails here even though modes 0-2 are right.
+    fin = np.isfinite(m2)
+    top = np.where(fin, m2, -np.inf).max(-1, keepdims=True)
+    e = np.where(fin, np.exp(np.where(fin, m2, 0.0) - top), 0.0)
+    np.testing.assert_allclose(m3, e / e.sum(-1, keepdims=True), rtol=1e-12, atol=1e-15)
+    vt = torch.cat([_f64(inp["past_v"]), _bnsh_kv(p, inp["v"], p.Dv)], dim=2)
+    vt = vt.repeat_interleave(p.Hq // p.Hkv, dim=1)
+    y = np.einsum("bhij,bhjd->bihd", m3, vt.numpy())
+    np.testing.assert_allclose(olk_ref.attention(p, inp), y, rtol=1e-11, atol=1e-13)
+
+
+def test_qk_output_mode3_rejects_cap_before_bias():
+    # with a bias comparable to the cap, capping first would change every weight:
+    # the softmax of c*tanh((s + bias)/c) differs from that of c*tanh(s/c) + bias
+    p = _att(bias_bh=(2, 4), softcap=0.7, has_lens=False)
+    inp = make_inputs(p, 69)
+    inp["bias"] = (inp["bias"].double() * 10.0).to(torch.float32)
+    m0, m3 = olk_ref.qk(p, inp, 0), olk_ref.qk(p, inp, 3)
+    bias = inp["bias"].double().numpy()
+    c = float(np.float32(0.7))   # the attribute is a float32 value
+    right = c * np.tanh((m0 + bias) / c)
+    wrong = c * np.tanh(m0 / c) + bias
+
+    def soft(x):
+        e = np.exp(x - x.max(-1, keepdims=True))
+        return e / e.sum(-1, keepdims=True)
+
+    np.testing.assert_allclose(m3, soft(right), rtol=1e-12, atol=1e-15)
+    assert np.abs(soft(wrong) - soft(right)).max() > 1e-2
 
 
 def test_mha_rank3_projection_bias_is_added_to_new_kv_rows():

@@ -16,7 +16,6 @@ namespace olk {
 hipError_t launch_flash(const Params &p, int dtype, hipStream_t st);
 bool flash_fuses_present(const Params &p);
 bool flash_rotates_q(const Params &p);
-hipError_t launch_tiled(const Params &p, int dtype, hipStream_t st);
 hipError_t launch_tiled_split(const Params &p, int dtype, int split_tiles, float *ws,
                               hipStream_t st);
 bool tiled_supports(const Params &p, int dtype);

@@ -56,7 +56,7 @@ struct Seq {
   int total;  // keys in the concatenated sequence
   int valid;  // keys j < valid may be attended
   int pad;    // keys j >= pad get mfv added (MultiHeadAttention, additive mode)
-  int qoff;   // absolute position of query 0 (bottom-right causal alignment)
+  int qoff;   // absolute position of query 0: the number of cached keys before the new ones
   int src;    // keys j < src are read from the past buffer, the rest from the new K/V
 };
 
@@ -74,7 +74,9 @@ __device__ __forceinline__ Seq seq_info(const Params &p, int b) {
   } else {
     s.past = p.P;
     s.total = p.T;
-    s.qoff = p.T - p.S;
+    // causal mask aligned to the upper-left corner of the new keys, shifted by
+    // the cached keys (every cached key precedes every query)
+    s.qoff = p.P;
     s.valid = p.T;
     s.pad = p.T;
     if (p.seqlens) {

@@ -63,7 +63,6 @@ struct Plan {
   int n_hg;      // head groups per KV head = G / GH
   int QW;        // queries per workgroup = kRows / GH
   int n_qt;      // query tiles = ceil(S / QW)
-  int partial;   // 1: write split partials to ws (combined later); 0: write Y
   int n_split;   // key splits
   int split_tiles;  // key tiles per split
   int xcd_remap;    // 1: place the workgroups of one (b, g) on one XCD
@@ -139,10 +138,8 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_kernel(Params p, Plan pl) {
   int lo = 0;
   if (p.window > 0) lo = max(0, pos_min - p.window + 1);
   int kt0 = lo / kBN, kt1 = (hi + kBN - 1) / kBN;
-  if (pl.partial) {
-    kt0 = max(kt0, split * pl.split_tiles);
-    kt1 = min(kt1, (split + 1) * pl.split_tiles);
-  }
+  kt0 = max(kt0, split * pl.split_tiles);
+  kt1 = min(kt1, (split + 1) * pl.split_tiles);
 
   // ---- this lane's row slot ----
   const int slot = wave * 32 + col;
@@ -372,52 +369,20 @@ __global__ __launch_bounds__(kThreads, 2) void tiled_kernel(Params p, Plan pl) {
   const float l_tot = l + __shfl_xor(l, 32, 64);
   if (!row_ok) return;
   const int64_t yrow_idx = ((int64_t)b * p.S + i) * p.Hq + h;
-  if (pl.partial) {
-    // unnormalised partial in natural-log units: (m, l, O)
-    float *out = pl.ws + (yrow_idx * pl.n_split + split) * (int64_t)(D + 4);
-    if (half == 0) {
-      out[0] = m == kNegInf ? kNegInf : m * kLn2;
-      out[1] = m == kNegInf ? 0.f : l_tot;
-    }
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d = db * 32 + 8 * q4 + 4 * half;
-        float4 v4 = make_float4(o[db][4 * q4], o[db][4 * q4 + 1], o[db][4 * q4 + 2], o[db][4 * q4 + 3]);
-        if (m == kNegInf) v4 = make_float4(0.f, 0.f, 0.f, 0.f);
-        *(float4 *)&out[4 + d] = v4;
-      }
-    return;
+  // unnormalised partial in natural-log units: (m, l, O), combined later
+  float *out = pl.ws + (yrow_idx * pl.n_split + split) * (int64_t)(D + 4);
+  if (half == 0) {
+    out[0] = m == kNegInf ? kNegInf : m * kLn2;
+    out[1] = m == kNegInf ? 0.f : l_tot;
   }
-  float inv = 0.f;
-  if (m != kNegInf) {
-    float lt = l_tot;
-    if (p.sink) {
-      const float z = (float)((const T *)p.sink)[h] * kLog2e;
-      if (z > m) {
-        const float a = fast_exp2(m - z);
-        lt = lt * a + 1.0f;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[db][r] *= a;
-      } else {
-        lt += fast_exp2(z - m);
-      }
-    }
-    inv = 1.0f / lt;
-  }
-  T *yr = (T *)p.y + b * p.y_sb + (int64_t)i * p.y_ss + h * p.y_sh;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const int d = db * 32 + 8 * q4 + 4 * half;
-      typename V8<T>::h v4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v4[e] = (T)(o[db][4 * q4 + e] * inv);
-      *(typename V8<T>::h *)&yr[d] = v4;
+      float4 v4 = make_float4(o[db][4 * q4], o[db][4 * q4 + 1], o[db][4 * q4 + 2], o[db][4 * q4 + 3]);
+      if (m == kNegInf) v4 = make_float4(0.f, 0.f, 0.f, 0.f);
+      *(float4 *)&out[4 + d] = v4;
     }
 }
 
@@ -429,9 +394,8 @@ int heads_per_wg(int G) {
 
 bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15) == 0; }
 
-Plan make_plan(const Params &p, int partial, int n_split, int split_tiles, float *ws) {
+Plan make_plan(const Params &p, int n_split, int split_tiles, float *ws) {
   Plan pl;
-  pl.partial = partial;
   pl.GH = heads_per_wg(p.G);
   pl.n_hg = p.G / pl.GH;
   pl.QW = kRows / pl.GH;
@@ -484,10 +448,6 @@ bool tiled_supports(const Params &p, int dtype) {
   return true;
 }
 
-hipError_t launch_tiled(const Params &p, int dtype, hipStream_t st) {
-  return launch_plan(p, dtype, make_plan(p, 0, 1, 1 << 30, nullptr), st);
-}
-
 int tiled_split_count(const Params &p, int split_tiles) {
   const int tiles = (p.T + kBN - 1) / kBN;
   return max(1, (tiles + split_tiles - 1) / split_tiles);
@@ -496,7 +456,7 @@ int tiled_split_count(const Params &p, int split_tiles) {
 hipError_t launch_tiled_split(const Params &p, int dtype, int split_tiles, float *ws,
                               hipStream_t st) {
   const int n_split = tiled_split_count(p, split_tiles);
-  return launch_plan(p, dtype, make_plan(p, 1, n_split, split_tiles, ws), st);
+  return launch_plan(p, dtype, make_plan(p, n_split, split_tiles, ws), st);
 }
 
 }  // namespace olk
