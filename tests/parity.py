@@ -1,5 +1,5 @@
 """Shared helpers of the GPU parity tests: run the HIP path through the C ABI
-and compare with the oracle element by element (or on sampled rows)."""
+and compare with the oracle element by element."""
 from __future__ import annotations
 
 import numpy as np
@@ -45,24 +45,3 @@ def assert_present_exact(p: Problem, inputs, pk: torch.Tensor, pv: torch.Tensor)
         n = int(tot[b])
         assert torch.equal(gk[b, :, :n].view(iview), ek[b, :, :n].view(iview)), f"present_k b={b}"
         assert torch.equal(gv[b, :, :n].view(iview), ev[b, :, :n].view(iview)), f"present_v b={b}"
-
-
-def sample_rows(p: Problem, n: int, seed: int = 0) -> np.ndarray:
-    """Deterministic (b, h, i) rows: random ones plus tile edges and corners."""
-    rng = np.random.default_rng(seed)
-    rows = [(0, 0, 0), (p.B - 1, p.Hq - 1, p.S - 1), (p.B - 1, 0, p.S - 1), (0, p.Hq - 1, 0)]
-    for i in (1, 15, 16, 31, 32, 63, 64, 127, 128, 255, 256, 511, 512, 513, 1023, 1024,
-              2047, 2048, 4095):
-        if i < p.S:
-            rows.append((int(rng.integers(p.B)), int(rng.integers(p.Hq)), i))
-    while len(rows) < n:
-        rows.append((int(rng.integers(p.B)), int(rng.integers(p.Hq)), int(rng.integers(p.S))))
-    return np.array(sorted(set(rows)), dtype=np.int32)
-
-
-def check_rows(p: Problem, inputs, y: torch.Tensor, rows: np.ndarray):
-    want = olk_ref.attention_rows(p, inputs, rows)
-    yl = y_logical(p, y)
-    got = yl[rows[:, 0], rows[:, 2], rows[:, 1]]
-    assert_close(p, got, want, "Y(sampled rows)")
-    assert np.isfinite(yl).all(), "non-finite values in Y"

@@ -281,7 +281,12 @@ olk::Params make_params(const olk_attn_desc *d, const olk_attn_io *io) {
   p.scale = d->has_scale ? d->scale : 1.0f / sqrtf((float)d->head_size);
   p.softcap = d->softcap;
   p.mfv = d->mask_filter_value;
-  p.pad_add = (d->op == OLK_OP_MHA && io->seqlens) ? 1 : 0;
+  // MultiHeadAttention key padding adds mask_filter_value to the padded keys'
+  // scores.  At -5000 or below, exp of such a score relative to the row's
+  // maximum underflows to exactly 0 in float32 unless it exceeds the largest
+  // real score by thousands, so the padded keys are excluded instead: the
+  // kernels stop at the row's length and never read them.
+  p.pad_add = (d->op == OLK_OP_MHA && io->seqlens && !(d->mask_filter_value <= -5000.f)) ? 1 : 0;
   p.cos_cache = io->cos_cache;
   p.sin_cache = io->sin_cache;
   p.rot_dim = d->rotary_dim > 0 ? d->rotary_dim : d->head_size;

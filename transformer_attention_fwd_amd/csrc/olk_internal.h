@@ -35,7 +35,8 @@ struct Params {
   int B, S, L, P, T, Hq, Hkv, G, D, Dv;
   int past_rows;   // rows per (b, g) of the past buffer: P, or T when the past lives in present
   int op, causal, window;
-  int pad_add;     // MultiHeadAttention: 1 = padded keys get mfv added, 0 = excluded
+  int pad_add;     // MultiHeadAttention lengths: 1 = padded keys get mfv added, 0 = excluded
+                   // (the host excludes them when mfv <= -5000: identical after underflow)
   int kv_inplace;  // present already holds the valid past
   int present_past_only;  // present writer copies only rows j < past_b (the
                           // attention kernel writes the new rows itself)
