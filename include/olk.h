@@ -235,6 +235,25 @@ olk_status olk_attention_fwd(const olk_attn_desc *desc, const olk_attn_io *io, v
 olk_status olk_attention_decode(const olk_attn_desc *desc, const olk_attn_io *io,
                                 void *workspace, size_t workspace_bytes, void *stream);
 
+/* Bytes of the built-in scratch of olk_attention_decode_noalloc (32 MiB). */
+#define OLK_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * olk_attention_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the split partials go to a scratch array built into the
+ * library, one per device, held until the process ends, instead of a caller
+ * workspace.  The call allocates nothing (no hipMalloc, no library allocator);
+ * the first call on a device looks up that device's scratch address.
+ * Arguments, result and errors as olk_attention_decode; OLK_E_WORKSPACE when
+ * olk_workspace_bytes(desc) exceeds OLK_NOALLOC_SCRATCH_BYTES (nothing is
+ * launched).  The scratch keeps the last call's partials and every call on a
+ * device shares it: calls that overlap on one device (on different streams,
+ * or from different threads without ordering) race and give wrong results.
+ */
+olk_status olk_attention_decode_noalloc(const olk_attn_desc *desc, const olk_attn_io *io,
+                                        void *stream);
+
 /*
  * Backward of the GroupQueryAttention forward (onnx-light-cpu C++ API page
  * "Custom operators", RegisterCustomOperatorGradients, GroupQueryAttention

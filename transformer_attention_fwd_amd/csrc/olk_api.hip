@@ -9,6 +9,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/olk.h"
 #include "olk_internal.h"
 
@@ -343,6 +345,34 @@ hipError_t rotary_prepass(olk::Params &p, int dtype, hipStream_t st, bool q_in_k
   return hipSuccess;
 }
 
+// Built-in scratch of olk_attention_decode_noalloc: the split partials that
+// olk_attention_decode keeps in the caller's workspace live here instead.
+// Each device holds its own copy until the process ends.  In host code the
+// name `scratch` is only a host-side handle: kernels get the device address
+// that hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = OLK_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device (null: not yet looked up)
+
+// Device address of the current device's copy of `scratch`, looked up once
+// per device with that device current.
+olk_status scratch_for_current_device(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return OLK_E_HIP;
+  if (dev >= kMaxDevices) return OLK_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return OLK_E_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return OLK_OK;
+}
+
 int n_splits(const olk_attn_desc *d, int split_keys = kSplitKeys) {
   const int64_t T = (int64_t)d->past_seq + d->kv_seq;
   const int64_t n = (T + split_keys - 1) / split_keys;
@@ -462,6 +492,20 @@ olk_status olk_attention_decode(const olk_attn_desc *desc, const olk_attn_io *io
   e = olk::launch_combine(p, desc->dtype, n_comb, (const float *)workspace, s);
   if (e == hipSuccess && p.qk_out) e = olk::launch_qk(p, desc->dtype, s);
   return e == hipSuccess ? OLK_OK : OLK_E_HIP;
+}
+
+olk_status olk_attention_decode_noalloc(const olk_attn_desc *desc, const olk_attn_io *io,
+                                        void *stream) {
+  const olk_status st = validate(desc, io);
+  if (st != OLK_OK) return st;
+  const size_t need = olk_workspace_bytes(desc);
+  if (need > kScratchBytes) return OLK_E_WORKSPACE;
+  void *ws = nullptr;
+  if (need) {
+    const olk_status e = scratch_for_current_device(&ws);
+    if (e != OLK_OK) return e;
+  }
+  return olk_attention_decode(desc, io, ws, need, stream);
 }
 
 size_t olk_bwd_workspace_bytes(const olk_attn_desc *d) {

@@ -72,6 +72,9 @@ _lib.olk_attention_fwd.restype = ctypes.c_int
 _lib.olk_attention_decode.argtypes = [_P(olk_attn_desc), _P(olk_attn_io), ctypes.c_void_p,
                                       ctypes.c_size_t, ctypes.c_void_p]
 _lib.olk_attention_decode.restype = ctypes.c_int
+_lib.olk_attention_decode_noalloc.argtypes = [_P(olk_attn_desc), _P(olk_attn_io),
+                                              ctypes.c_void_p]
+_lib.olk_attention_decode_noalloc.restype = ctypes.c_int
 _lib.olk_bwd_workspace_bytes.argtypes = [_P(olk_attn_desc)]
 _lib.olk_bwd_workspace_bytes.restype = ctypes.c_size_t
 _lib.olk_attention_bwd.argtypes = [_P(olk_attn_desc), _P(olk_attn_bwd_io), ctypes.c_void_p,
@@ -83,8 +86,8 @@ _lib.olk_last_kernel_name.argtypes = []
 _lib.olk_last_kernel_name.restype = ctypes.c_char_p
 
 EXPORTED = ("olk_validate", "olk_workspace_bytes", "olk_attention_fwd", "olk_attention_decode",
-            "olk_bwd_workspace_bytes", "olk_attention_bwd", "olk_status_str",
-            "olk_last_kernel_name")
+            "olk_attention_decode_noalloc", "olk_bwd_workspace_bytes", "olk_attention_bwd",
+            "olk_status_str", "olk_last_kernel_name")
 
 
 class OlkError(RuntimeError):
@@ -115,6 +118,13 @@ def olk_attention_decode(desc: olk_attn_desc, io: olk_attn_io, workspace: int,
                          workspace_bytes: int, stream: int) -> int:
     return _lib.olk_attention_decode(ctypes.byref(desc), ctypes.byref(io), workspace,
                                      workspace_bytes, stream)
+
+
+def olk_attention_decode_noalloc(desc: olk_attn_desc, io: olk_attn_io, stream: int) -> int:
+    return _lib.olk_attention_decode_noalloc(ctypes.byref(desc), ctypes.byref(io), stream)
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 def olk_bwd_workspace_bytes(desc: olk_attn_desc) -> int:
