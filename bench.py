@@ -16,7 +16,6 @@ throughput on a bounded sample, and secondary figures for the other workloads
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -30,8 +29,16 @@ sys.path.insert(0, ROOT)
 MFMA_PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}  # dense, MI355X
 HBM_PEAK_GBS = 8000.0
 HEADLINE = "gqa_prefill_causal_bf16"
+# prefill workloads also timed cache-cold (inputs rotated over several copies)
+ROTATED = ("gqa_prefill_causal_bf16", "gqa_prefill_window_sink_bf16", "mha_cross_f16")
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
-FLASH_SRC = os.path.join(ROOT, "transformer_attention_fwd_amd", "csrc", "olk_flash.hip")
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
+NOMINAL_CLOCK_GHZ = 2.4
+# the kernel a step's roofline is about, by the path the library reports
+DOMINANT = {"olk_tiled_fwd": ("flash_fwd_kernel", "flash_fwd_kernel"),
+            "olk_rope+olk_tiled_fwd": ("flash_fwd_kernel", "rope_vec2_kernel + flash_fwd_kernel"),
+            "olk_decode_split+combine": ("decode_mfma_kernel",
+                                         "decode_mfma_kernel + combine_kernel")}
 
 
 def parse():
@@ -46,6 +53,9 @@ def parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--backward-only", action="store_true",
                     help="time only the GroupQueryAttention backward line (for profiling)")
+    ap.add_argument("--rotate-buffers", type=int, default=4,
+                    help="input/output sets cycled for the cache-cold prefill figures "
+                         "(0: skip them)")
     return ap.parse_args()
 
 
@@ -95,6 +105,29 @@ def flops(p, inputs) -> float:
     return 2.0 * (p.D + p.Dv) * float(allowed_pairs(p, inputs).sum()) * p.Hq
 
 
+def prefill_bytes(p, inputs) -> float:
+    """Least HBM traffic of a prefill call: Q and Y once, every K/V row some
+    query attends once, bias and mask once, present written once
+    (GroupQueryAttention)."""
+    from transformer_attention_fwd_amd.workloads import valid_lengths
+    es = 2 if p.dtype != "f32" else 4
+    qy = p.B * p.S * p.Hq * (p.D + p.Dv) * es
+    tot = valid_lengths(p, inputs)
+    rows = 0.0
+    for b in range(p.B):
+        if p.op == "gqa":
+            rows += float(tot[b])
+        else:
+            valid = int(tot[b]) if (p.op == "attention" or p.mask_filter_value <= -5000) else p.T
+            valid = valid or p.T
+            rows += float(min(valid, p.P + p.S) if p.causal else valid)
+    kv = rows * p.Hkv * (p.D + p.Dv) * es
+    bias = float(inputs["bias"].numel() * es) if "bias" in inputs else 0.0
+    mask = float(inputs["mask"].numel() * inputs["mask"].element_size()) if "mask" in inputs else 0.0
+    present = kv if p.op == "gqa" else 0.0
+    return qy + kv + bias + mask + present
+
+
 def decode_bytes(p, inputs, inplace: bool) -> float:
     """KV bytes read + Q/Y + new K/V + present append (or full copy)."""
     from transformer_attention_fwd_amd.workloads import valid_lengths
@@ -126,19 +159,53 @@ def time_launches(call, steps: int, warmup: int):
     return e0.elapsed_time(e1) / steps, wall
 
 
-def traffic_for(workload: str):
-    """HBM bytes per launch from committed rocprofv3 counters, if they were
-    taken on the current kernel source (else None)."""
+def _profile_record(path: str, workload: str, kernel: str):
+    """The committed rocprofv3 record of `kernel` on `workload`, if it was taken
+    on the kernel's current source (else None)."""
+    from transformer_attention_fwd_amd.prof import kernel_source_sha
     try:
-        with open(PROFILE_TRAFFIC) as f:
-            rec = json.load(f)
-        h = hashlib.sha256(open(FLASH_SRC, "rb").read()).hexdigest()
-        ent = rec.get(workload)
-        if ent and ent.get("kernel_sha256") == h:
-            return float(ent["fetch_bytes"]) + float(ent["write_bytes"])
-    except (OSError, ValueError, KeyError):
-        pass
+        with open(path) as f:
+            ent = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if ent and ent.get("kernel") == kernel and ent.get("kernel_sha256") == kernel_source_sha(kernel):
+        return ent
     return None
+
+
+def traffic_for(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE / WRITE_SIZE
+    counters, or None when they were taken on another version of its source."""
+    ent = _profile_record(PROFILE_TRAFFIC, workload, kernel)
+    return None if ent is None else float(ent["fetch_bytes"]) + float(ent["write_bytes"])
+
+
+def roofline(name, p, res, work: float, bound: str, kernel: str, step_kernels: str):
+    """Roofline of the step's dominant kernel: algorithmic work / the measured
+    step time, against MI355X's published peak; the committed counters add the
+    HBM traffic, the shader clock the kernel ran at and the matrix / vector
+    busy fractions."""
+    ms = res["ms_per_step"]
+    if bound == "mfma":
+        achieved, peak, unit = work / (ms * 1e-3) / 1e12, MFMA_PEAK_TFLOPS[p.dtype], "TFLOP/s"
+    else:
+        achieved, peak, unit = work / (ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
+    r = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+         "frac": round(achieved / peak, 5), "traffic": traffic_for(name, kernel),
+         "kernel": kernel, "step_kernels": step_kernels, "step_ms": round(ms, 5),
+         ("flops_per_launch" if bound == "mfma" else "bytes_per_launch"): work}
+    c = _profile_record(PROFILE_COUNTERS, name, kernel)
+    if c is not None:
+        r["counters"] = {"clock_ghz": round(c["clock_ghz"], 3),
+                         "mfma_busy": round(c["mfma_busy"], 4),
+                         "valu_busy": round(c["valu_busy"], 4),
+                         "valu_per_mfma": round(c["valu_per_mfma"], 3),
+                         "profiled_kernel_us": round(c["mean_duration_us"], 2)}
+        if bound == "mfma":
+            # the same figure against the peak at the clock the kernel ran at
+            r["frac_at_measured_clock"] = round(
+                achieved / (peak * c["clock_ghz"] / NOMINAL_CLOCK_GHZ), 5)
+    return r
 
 
 def cpu_baseline(p, inputs, kind: str, target_s: float):
@@ -191,7 +258,32 @@ def check_rows(p, inputs, y, n=48):
     return float(np.abs(got - want).max())
 
 
-def run_workload(name, steps, warmup, with_cpu, cpu_s, is_headline):
+def time_rotating(p, dev, inputs, sets: int, steps: int, warmup: int, decode: bool):
+    """Cache-cold step time: `sets` copies of the inputs and outputs (a working
+    set beyond the 256 MB MALL) used in turn, so no step finds its data in the
+    caches the previous one filled."""
+    import torch
+    from transformer_attention_fwd_amd import olk
+    calls = []
+    for _ in range(sets):
+        d = {k: v.clone() for k, v in dev.items()}
+        calls.append(olk.Call(p, d, mode="fwd", want_present=(p.op == "gqa")))
+    for i in range(warmup):
+        calls[i % sets].launch()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        calls[i % sets].launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del calls
+    return ms
+
+
+def run_workload(name, steps, warmup, with_cpu, cpu_s, is_headline, rotate=0):
     import torch
     from transformer_attention_fwd_amd import olk
     from transformer_attention_fwd_amd.workloads import workload
@@ -215,27 +307,34 @@ def run_workload(name, steps, warmup, with_cpu, cpu_s, is_headline):
     ms, wall = time_launches(call, steps, warmup)
     res["ms_per_step"] = ms
     res["wall_s"] = wall
+    dom = DOMINANT.get(res["kernel"])
     if decode:
         by = decode_bytes(p, inputs, inplace=True)
         res["value"] = by / (ms * 1e-3) / 1e9
         res["unit"] = "GB/s"
         res["frac_of_peak"] = res["value"] / HBM_PEAK_GBS
         res["bytes_per_step"] = by
+        if dom:
+            res["roofline"] = roofline(name, p, res, by, "hbm", dom[0], dom[1])
     else:
         fl = flops(p, inputs)
         res["value"] = fl / (ms * 1e-3) / 1e12
         res["unit"] = "TFLOP/s"
         res["frac_of_peak"] = res["value"] / MFMA_PEAK_TFLOPS[p.dtype]
         res["flops_per_step"] = fl
-        if is_headline and res["kernel"] == "olk_tiled_fwd":
-            # The prefill path is one launch of the flash kernel (present_key /
-            # present_value are written by the same kernel), so the step time
-            # from the HIP events above is that kernel's average duration.
-            peak = MFMA_PEAK_TFLOPS[p.dtype]
-            res["roofline"] = {"bound": "mfma", "achieved": round(res["value"], 3), "peak": peak,
-                               "unit": "TFLOP/s", "frac": round(res["value"] / peak, 5),
-                               "traffic": traffic_for(name), "kernel": "flash_fwd_kernel",
-                               "kernel_ms": round(ms, 5), "flops_per_launch": fl}
+        by = prefill_bytes(p, inputs)
+        res["hbm_bytes_algorithmic"] = by
+        res["hbm_frac"] = round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 5)
+        if dom:
+            # With present written by the prefill kernel itself the step is one
+            # launch of it, so the HIP-event step time is its launch duration.
+            res["roofline"] = roofline(name, p, res, fl, "mfma", dom[0], dom[1])
+        if rotate > 1:
+            cold = time_rotating(p, dev, inputs, rotate, steps, warmup, decode)
+            res["cold"] = {"sets": rotate, "ms_per_step": round(cold, 5),
+                           "value": round(fl / (cold * 1e-3) / 1e12, 3),
+                           "frac_of_peak": round(fl / (cold * 1e-3) / 1e12 /
+                                                 MFMA_PEAK_TFLOPS[p.dtype], 5)}
     if with_cpu:
         res["cpu_baseline"] = cpu_baseline(p, inputs, "bytes" if decode else "flops", cpu_s)
     del call, dev
@@ -280,7 +379,7 @@ def main():
         return
     t_start = time.perf_counter()
     p, head = run_workload(args.workload, args.steps, args.warmup, not args.no_cpu,
-                           args.cpu_seconds, True)
+                           args.cpu_seconds, True, args.rotate_buffers)
     print(f"[bench] {args.workload}: {head['value']:.1f} {head['unit']} "
           f"({head['ms_per_step']:.3f} ms/step) err={head['max_abs_err_sampled']:.2e}",
           file=sys.stderr, flush=True)
@@ -290,12 +389,14 @@ def main():
         for name in WORKLOAD_ORDER:
             if name == args.workload:
                 continue
-            _, r = run_workload(name, max(5, args.steps // 5), max(2, args.warmup // 5), False,
-                                0, False)
+            rot = args.rotate_buffers if name in ROTATED else 0
+            _, r = run_workload(name, max(10, args.steps // 2), max(3, args.warmup // 2), False,
+                                0, False, rot)
             print(f"[bench] {name}: {r['value']:.1f} {r['unit']} ({r['ms_per_step']:.4f} ms) "
                   f"err={r['max_abs_err_sampled']:.2e}", file=sys.stderr, flush=True)
             secondary[name] = {k: r[k] for k in ("value", "unit", "frac_of_peak", "ms_per_step",
-                                                 "kernel", "max_abs_err_sampled")}
+                                                 "kernel", "max_abs_err_sampled", "roofline",
+                                                 "hbm_frac", "cold") if k in r}
     if not args.no_secondary:
         r = run_backward(max(3, args.steps // 10), 1)
         print(f"[bench] gqa_backward_bf16: {r['value']:.1f} {r['unit']} ({r['ms_per_step']:.3f} ms)",
@@ -322,6 +423,8 @@ def main():
         "kernel": head["kernel"],
         "max_abs_err_sampled": head["max_abs_err_sampled"],
         "roofline": head.get("roofline"),
+        "hbm_frac": head.get("hbm_frac"),
+        "cold": head.get("cold"),
         "cpu_baseline": head.get("cpu_baseline"),
         "secondary": secondary,
         "bench_wall_s": round(time.perf_counter() - t_start, 1),
