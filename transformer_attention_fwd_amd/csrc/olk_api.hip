@@ -475,9 +475,10 @@ olk_status olk_attention_decode(const olk_attn_desc *desc, const olk_attn_io *io
     p.present_k = p.present_v = nullptr;
   }
   const int n_split = n_splits(desc);
-  int n_comb = n_split;
+  int n_comb = n_split, comb_keys = kSplitKeys;
   if (desc->kernel != OLK_KERNEL_GENERIC && tiled_ok && olk::decode_supports(p, desc->dtype)) {
     n_comb = n_splits(desc, kDecodeSplitKeys);
+    comb_keys = kDecodeSplitKeys;
     e = olk::launch_decode(p, desc->dtype, kDecodeSplitKeys, n_comb, (float *)workspace,
                            append_in_decode, s);
     g_last_kernel = "olk_decode_split+combine";
@@ -489,7 +490,7 @@ olk_status olk_attention_decode(const olk_attn_desc *desc, const olk_attn_io *io
     g_last_kernel = "olk_generic_split+combine";
   }
   if (e != hipSuccess) return OLK_E_HIP;
-  e = olk::launch_combine(p, desc->dtype, n_comb, (const float *)workspace, s);
+  e = olk::launch_combine(p, desc->dtype, n_comb, comb_keys, (const float *)workspace, s);
   if (e == hipSuccess && p.qk_out) e = olk::launch_qk(p, desc->dtype, s);
   return e == hipSuccess ? OLK_OK : OLK_E_HIP;
 }

@@ -90,6 +90,10 @@ template <> __device__ __forceinline__ float hi16<f16>(uint32_t w) {
 
 constexpr int kThreads = 256;
 constexpr int kStep = 16;  // keys per wavefront step
+
+// s_waitcnt immediate waiting for vmcnt <= n only (gfx9 encoding: vmcnt bits
+// [3:0] and [15:14], expcnt [6:4] = 7, lgkmcnt [11:8] = 15: no wait on those)
+constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
@@ -140,6 +144,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p, DPlan pl) {
   const int sp_hi = min(hi, (split + 1) * pl.split_keys);
   const int base = (sp_lo / kStep) * kStep;
   const int n_steps = sp_lo < sp_hi ? (sp_hi - base + kStep - 1) / kStep : 0;
+  // a split with no key of the range: no record (the combine reads only the
+  // splits that hold keys of a row's range)
+  if (n_steps == 0) return;
 
   // ---- Q^T operand: column n = lane % 16 is row slot n = (query n / G, head n % G) ----
   const int n = lane & 15, kq = lane >> 4;
@@ -435,6 +442,9 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p, DPlan p
   const int sp_hi = min(hi, (split + 1) * pl.split_keys);
   const int base = sp_lo;  // steps start at the first key of the split
   const int n_steps = sp_lo < sp_hi ? (sp_hi - sp_lo + kStep - 1) / kStep : 0;
+  // a split with no key of the range: no record (the combine reads only the
+  // splits that hold keys of a row's range)
+  if (n_steps == 0) return;
 
   // ---- Q^T operand: column n = lane % 16 is row slot n = (query n / G, head n % G) ----
   const int n = lane & 15, kq = lane >> 4;
@@ -452,7 +462,6 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p, DPlan p
       qreg[ks] = __builtin_bit_cast(vec8, raw);
     }
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // Q in registers (vmcnt(0) only)
 
   // Every key is in the past buffer (the present append ran before this
   // kernel, or above for the in-place cache). The
@@ -556,9 +565,18 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p, DPlan p
       o[blk] = mma16k16(__builtin_bit_cast(vec4, a), pb, o[blk]);
     }
   };
-  if (n_steps > 0) {
-    if (my_steps > 0) load_step(0, k0, v0);
-    if (my_steps > 1) load_step(1, k1, v1);
+  // The first two steps' loads go out behind the Q loads, so the latencies
+  // overlap; then wait for Q alone (the 8 K/V loads of each issued step may
+  // stay in flight: the counter is in order).  Waiting on every path keeps the
+  // wait-count analysis from treating Q as in flight inside the step loop.
+  if (my_steps > 0) load_step(0, k0, v0);
+  if (my_steps > 1) load_step(1, k1, v1);
+  constexpr int kLoadsPerStep = NKS + kStep / 4;
+  static_assert(2 * kLoadsPerStep < 64, "vmcnt holds 6 bits");
+  if (my_steps > 1) __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * kLoadsPerStep));
+  else if (my_steps == 1) __builtin_amdgcn_s_waitcnt(vmcnt_only(kLoadsPerStep));
+  else __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+  {
     for (int it = 0; it < my_steps; it += 3) {
       body(it, k0, v0, k2, v2);
       if (it + 1 < my_steps) body(it + 1, k1, v1, k0, v0);

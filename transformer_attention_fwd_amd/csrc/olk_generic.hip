@@ -195,7 +195,8 @@ __global__ __launch_bounds__(kWave) void generic_split_kernel(Params p, int chun
 constexpr int kMaxSplits = 4096;
 
 template <typename T>
-__global__ __launch_bounds__(kWave) void combine_kernel(Params p, int n_split, const float *ws) {
+__global__ __launch_bounds__(kWave) void combine_kernel(Params p, int n_split, int split_keys,
+                                                        const float *ws) {
   __shared__ float wgt[kMaxSplits];
   const int h = blockIdx.x;
   const int b = blockIdx.y / p.S, i = blockIdx.y % p.S;
@@ -203,8 +204,18 @@ __global__ __launch_bounds__(kWave) void combine_kernel(Params p, int n_split, c
   const int64_t row = ((int64_t)b * p.S + i) * p.Hq + h;
   const int64_t rec = p.Dv + 4;
   const float *part = ws + row * n_split * rec;
+  // Only the splits that hold keys of this row's range [lo, hi) are read:
+  // every partial kernel writes the records of those (a split outside the
+  // range contributes nothing, and the decode kernels write no record there).
+  const Seq s = seq_info(p, b);
+  const int pos = s.qoff + i;
+  int hi = p.pad_add ? s.total : s.valid;
+  if (p.causal) hi = min(hi, pos + 1);
+  const int lo = p.window > 0 ? max(0, pos - p.window + 1) : 0;
+  const int sp0 = lo / split_keys;
+  const int sp1 = hi > lo ? min(n_split, (hi + split_keys - 1) / split_keys) : sp0;
   float M = kNegInf;
-  for (int sp = lane; sp < n_split; sp += kWave) M = fmaxf(M, part[sp * rec]);
+  for (int sp = sp0 + lane; sp < sp1; sp += kWave) M = fmaxf(M, part[sp * rec]);
   M = wave_max(M);
   T *yr = (T *)p.y + b * p.y_sb + (int64_t)i * p.y_ss + h * p.y_sh;
   if (M == kNegInf) {  // no allowed key: zeros
@@ -215,7 +226,7 @@ __global__ __launch_bounds__(kWave) void combine_kernel(Params p, int n_split, c
   if (p.sink) z = to_f32(((const T *)p.sink)[h]);
   const float Mf = fmaxf(M, z);
   float l = 0.f;
-  for (int sp = lane; sp < n_split; sp += kWave) {
+  for (int sp = sp0 + lane; sp < sp1; sp += kWave) {
     const float m = part[sp * rec];
     const float w = m == kNegInf ? 0.f : expf(m - Mf);
     wgt[sp] = w;
@@ -228,7 +239,7 @@ __global__ __launch_bounds__(kWave) void combine_kernel(Params p, int n_split, c
   for (int d = lane; d < p.Dv; d += kWave) {
     float acc = 0.f;
 #pragma unroll 8
-    for (int sp = 0; sp < n_split; ++sp) acc += wgt[sp] * part[sp * rec + 4 + d];
+    for (int sp = sp0; sp < sp1; ++sp) acc += wgt[sp] * part[sp * rec + 4 + d];
     yr[d] = from_f32<T>(acc * inv);
   }
 }
@@ -328,16 +339,17 @@ hipError_t launch_generic_split(const Params &p, int dtype, int chunk, int n_spl
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const Params &p, int dtype, int n_split, const float *ws,
-                          hipStream_t st) {
+hipError_t launch_combine(const Params &p, int dtype, int n_split, int split_keys,
+                          const float *ws, hipStream_t st) {
   if (p.B == 0 || p.S == 0 || p.Hq == 0) return hipSuccess;
+  if (split_keys <= 0 || n_split > kMaxSplits) return hipErrorInvalidValue;
   dim3 grid(p.Hq, p.B * p.S);
   if (dtype == DT_F32)
-    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(kWave), 0, st, p, n_split, ws);
+    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(kWave), 0, st, p, n_split, split_keys, ws);
   else if (dtype == DT_F16)
-    hipLaunchKernelGGL(combine_kernel<f16>, grid, dim3(kWave), 0, st, p, n_split, ws);
+    hipLaunchKernelGGL(combine_kernel<f16>, grid, dim3(kWave), 0, st, p, n_split, split_keys, ws);
   else
-    hipLaunchKernelGGL(combine_kernel<bf16>, grid, dim3(kWave), 0, st, p, n_split, ws);
+    hipLaunchKernelGGL(combine_kernel<bf16>, grid, dim3(kWave), 0, st, p, n_split, split_keys, ws);
   return hipGetLastError();
 }
 

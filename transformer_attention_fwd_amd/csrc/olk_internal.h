@@ -110,8 +110,8 @@ template <typename T> __device__ __forceinline__ T from_f32(float x) { return (T
 hipError_t launch_generic(const Params &p, int dtype, hipStream_t st);
 hipError_t launch_generic_split(const Params &p, int dtype, int chunk, int n_split,
                                 float *ws, hipStream_t st);
-hipError_t launch_combine(const Params &p, int dtype, int n_split, const float *ws,
-                          hipStream_t st);
+hipError_t launch_combine(const Params &p, int dtype, int n_split, int split_keys,
+                          const float *ws, hipStream_t st);
 hipError_t launch_present(const Params &p, int dtype, hipStream_t st);
 hipError_t launch_rope(const Params &p, int dtype, hipStream_t st);
 hipError_t launch_qk(const Params &p, int dtype, hipStream_t st);
