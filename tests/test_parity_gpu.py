@@ -35,6 +35,10 @@ SMALL = {
     "gqa_window_sink_softcap_bf16": Problem(op="gqa", dtype="bf16", B=2, S=300, L=300, Hq=8,
                                             Hkv=2, D=128, Dv=128, causal=1, window=70,
                                             softcap=2.0, has_sink=True),
+    # softcap 30 at head size 128: |s / c| stays under 1/4, so the tiles take
+    # the polynomial tanh (the softcap-2 case above mixes both forms)
+    "gqa_softcap_taylor_bf16": Problem(op="gqa", dtype="bf16", B=2, S=260, L=260, Hq=8, Hkv=2,
+                                       D=128, Dv=128, causal=1, softcap=30.0, has_sink=True),
     "gqa_past_f16": Problem(op="gqa", dtype="f16", B=3, S=37, L=37, P=200, Hq=8, Hkv=2, D=128,
                             Dv=128, causal=1, lens_range=(0, 200)),
     "gqa_decode_f16": Problem(op="gqa", dtype="f16", B=5, S=1, L=1, P=700, Hq=8, Hkv=2,
@@ -71,6 +75,17 @@ SMALL = {
     "mha_unidir_past_bf16": Problem(op="mha", dtype="bf16", B=2, S=90, L=40, P=70, Hq=2, Hkv=2,
                                     D=128, Dv=128, kv_rank=3, causal=1, has_lens=True,
                                     lens_range=(80, 110)),
+    # additive bias with a power-of-two scale (Q pre-scaled, the bias in the
+    # QK^T accumulator): head size 128 with an explicit scale, causal with a
+    # past; MultiHeadAttention with a small filter value (added, not skipped)
+    "attention_bias_pow2_scale_bf16": Problem(op="attention", dtype="bf16", B=2, S=90, L=150,
+                                              P=20, Hq=8, Hkv=2, D=128, Dv=128, causal=1,
+                                              has_lens=True, lens_range=(60, 170),
+                                              bias_bh=(2, 8), scale=0.0625),
+    "mha_filter_bias_f16": Problem(op="mha", dtype="f16", B=2, S=70, L=200, Hq=2, Hkv=2, D=64,
+                                   Dv=64, kv_rank=4, causal=0, has_lens=True,
+                                   lens_range=(50, 200), bias_bh=(1, 2), mask_filter_value=-3.0,
+                                   has_proj_bias=True),
     "mha_self_bias_f32": Problem(op="mha", dtype="f32", B=2, S=33, L=33, P=20, Hq=3, Hkv=3,
                                  D=40, Dv=24, kv_rank=3, causal=1, bias_bh=(2, 3),
                                  has_lens=False),

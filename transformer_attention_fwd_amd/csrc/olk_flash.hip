@@ -131,6 +131,7 @@ __device__ __forceinline__ int quad_slot(int qq) { return ((qq & 1) << 1) | (qq 
 
 struct FPlan {
   int GH, n_hg, QW, n_qt;
+  int qs;            // Q pre-scaled, bias in the accumulator (see flash_fwd_kernel)
   int xcd_remap;
   int bias_vec;
   int mask_vec;      // BOOL mask rows are 4-byte aligned
@@ -142,10 +143,15 @@ struct FPlan {
 // form needs more registers and keeps two), two at head size 128.
 template <int D, int BM> constexpr int kOcc = (D == 64 && BM != 2) ? 3 : 2;
 
-// BM: 0 no bias, 1 attn_bias, 2 BOOL attn_mask (with or without attn_bias)
-template <typename T, int D, int BM, bool SOFTCAP>
+// BM: 0 no bias, 1 attn_bias, 2 BOOL attn_mask (with or without attn_bias).
+// QS (attn_bias without softcap, the scale an exact power of two): Q is
+// multiplied by the scale as it is loaded (exact: a change of exponent) and
+// the bias seeds the QK^T accumulator, so the matrix cores add it and the
+// scores leave the MFMAs as (Q K^T) * scale + bias, in natural-log units.
+template <typename T, int D, int BM, bool SOFTCAP, bool QS = false>
 __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Params p, FPlan pl) {
   typedef typename FV<T>::v8 vec8;
+  static_assert(!QS || (BM == 1 && !SOFTCAP), "the bias seeds the accumulator only without softcap");
   constexpr bool BIAS = BM != 0;   // the score epilogue reads a bias row
   constexpr bool MASK = BM == 2;
   constexpr int CH = D / 8;             // 16-byte chunks per K/V row
@@ -162,7 +168,11 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
   // one.  The forms whose registers do not allow the unrolled body (head
   // size 64 at three wavefronts per SIMD, BOOL mask with softcap) select the
   // buffers at run time and keep that wait.
-  constexpr bool UNROLL2 = D == 128 && !(BM == 2 && SOFTCAP);
+  constexpr bool UNROLL2 = !(BM == 2 && SOFTCAP) && !(D == 64 && SOFTCAP);
+  // polynomial softcap for small |u| (below); the bias, BOOL-mask and
+  // head-size-64 forms keep the exponential form only (their registers do not
+  // hold both)
+  constexpr bool TAYLOR = SOFTCAP && BM == 0 && D == 128;
   __shared__ __attribute__((aligned(16))) T klds0[BN * D];
   __shared__ __attribute__((aligned(16))) T klds1[BN * D];
   __shared__ __attribute__((aligned(16))) T vlds0[BN * D];
@@ -294,6 +304,11 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
       } else {
         qreg[ks] = __builtin_bit_cast(vec8, raw[ks]);
       }
+      if constexpr (QS) {
+        // q * scale, scale = 2^k: only the exponent changes
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qreg[ks][e] = (T)((float)qreg[ks][e] * p.scale);
+      }
     }
   }
   };
@@ -408,15 +423,23 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
       voff[db] = (uint32_t)((4 * half + q) * RB + 16 * ((4 * db + t2) ^ fv(4 * half + q)) + 8 * (j & 1));
   }
 
-  const float sl = p.scale * kLog2e;
+  // exponent factor of raw scores (with QS the scale is already in Q)
+  const float sl = QS ? kLog2e : p.scale * kLog2e;
   const bool scale_pos = p.scale > 0.f;
   // softcap in the log2 domain: c tanh(u) = c - 2c / (e^{2u} + 1) with
   // u = (s scale + bias) / c; e^{2u} = 2^(s cap_a + bias cap_b)
   const float inv_cap = SOFTCAP ? 1.0f / p.softcap : 0.f;
   const float cap_l2 = p.softcap * kLog2e;
   const float cap_b = 2.0f * kLog2e * inv_cap, cap_a = p.scale * cap_b;
+  // u = (s scale + bias) / c; for |u| <= 1/4 the odd Taylor series of tanh
+  // through u^9 is exact to float32 (the next term is below 4e-9):
+  // c tanh(u) log2 e = u (C0 + u^2 (C1 + u^2 (C2 + u^2 (C3 + u^2 C4))))
+  const float u_a = p.scale * inv_cap;
+  const float tc0 = cap_l2, tc1 = cap_l2 * (-1.0f / 3.0f), tc2 = cap_l2 * (2.0f / 15.0f),
+              tc3 = cap_l2 * (-17.0f / 315.0f), tc4 = cap_l2 * (62.0f / 2835.0f);
+  constexpr float kTaylorU = 0.25f;
   const float mfv_l2 = p.mfv * kLog2e;
-  const float mfv_raw = p.mfv / p.scale;  // the same offset before the scale (scale > 0)
+  const float mfv_raw = QS ? p.mfv : p.mfv / p.scale;  // the same offset in raw-score units (scale > 0)
   const T *bias_row = BIAS ? (const T *)p.bias + b * p.bias_sb + row_h * p.bias_sh +
                                  (int64_t)(row_ok ? row_i : 0) * p.bias_si
                            : nullptr;
@@ -446,12 +469,13 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
       if (jb + e < p.mask_cols) w |= (uint32_t)mask_row[jb + e] << (8 * e);
     return w;
   };
-  // At head size 64 with two wavefronts per SIMD the bias of the next tile is
-  // prefetched with its K/V (with three, its registers are not available).
+  // At head size 64 with two wavefronts per SIMD, or with QS (whose scores
+  // need fewer registers), the bias of the next tile is prefetched with its
+  // K/V.
   // Otherwise a tile's bias and mask words are loaded at the start of the
   // tile, before the next tile's K/V loads: the memory counter is in order,
   // so waiting for loads issued after those would wait for them too.
-  constexpr bool BPRE = BIAS && D == 64 && kOcc<D, BM> == 2;
+  constexpr bool BPRE = BIAS && D == 64 && (kOcc<D, BM> == 2 || QS);
   typedef uint2 BiasWords[BIAS ? KB : 1][4];
   typedef uint32_t MaskWords[MASK ? KB : 1][4];
   BiasWords bcur, bnext;
@@ -495,10 +519,10 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
   float m = kNegInf, l = 0.f;
 
-  // S^T of one tile: KB blocks of 32 keys
-  auto qk = [&](const T *kbuf, f32x16 (&sacc)[KB]) __attribute__((always_inline)) {
+  // S^T of one tile: KB blocks of 32 keys; seed: the accumulators' start
+  // (zeros, or with QS the tile's bias values)
+  auto qk = [&](const T *kbuf, f32x16 (&sacc)[KB], const f32x16 (&seed)[KB]) __attribute__((always_inline)) {
     const char *kl = (const char *)kbuf;
-    const f32x16 zero = {};
     // block-major: the first 32 keys' scores are final while the second
     // block's MFMAs run, so their row max can start (each chain keeps its
     // k order, so the sums are the same)
@@ -507,7 +531,7 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const vec8 a = *(const vec8 *)(kl + kb * 32 * RB + koff[ks]);
-        sacc[kb] = mma(a, qreg[ks], ks == 0 ? zero : sacc[kb]);
+        sacc[kb] = mma(a, qreg[ks], ks == 0 ? seed[kb] : sacc[kb]);
       }
     }
     // schedule: four operand reads in flight ahead of the MFMAs
@@ -527,10 +551,10 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
   // masked and unmasked tiles share one body.
   auto softmax_pv = [&](int kt, const T *vbuf, f32x16 (&sacc)[KB], bool masked, const BiasWords &bwt,
                         const MaskWords &mwt) __attribute__((always_inline)) {
-    constexpr bool GENERAL = BIAS || SOFTCAP;
+    constexpr bool GENERAL = (BIAS && !QS) || SOFTCAP;
     const char *vl = (const char *)vbuf;
     const int j0 = kt * BN;
-    if (GENERAL) {
+    if (GENERAL && !TAYLOR) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -542,6 +566,7 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
             bv[0] = lo16<T>(raw.x); bv[1] = hi16<T>(raw.x);
             bv[2] = lo16<T>(raw.y); bv[3] = hi16<T>(raw.y);
           }
+          (void)jb;
           uint32_t mw = 0x01010101u;  // BOOL attn_mask bytes of the 4 keys
           if constexpr (MASK) mw = mwt[kb][q4];
 #pragma unroll
@@ -558,6 +583,52 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
             sacc[kb][4 * q4 + e] = ((mw >> (8 * e)) & 0xffu) ? t : kNegInf;
           }
         }
+    }
+    if constexpr (TAYLOR) {
+      // softcap: u = (s scale + bias) / c in place, then one uniform choice
+      // per tile: the polynomial when every |u| of the wavefront's tile is at
+      // most 1/4, else c - 2c / (e^{2u} + 1) (saturates to +-c without NaN:
+      // rcp of +inf is 0)
+      float amax = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          float bv[4] = {0.f, 0.f, 0.f, 0.f};
+          if (BIAS) {
+            const uint2 raw = BPRE ? bcur[kb][q4] : bwt[kb][q4];
+            bv[0] = lo16<T>(raw.x); bv[1] = hi16<T>(raw.x);
+            bv[2] = lo16<T>(raw.y); bv[3] = hi16<T>(raw.y);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x = sacc[kb][4 * q4 + e];
+            const float u = BIAS ? __builtin_fmaf(x, u_a, bv[e] * inv_cap) : x * u_a;
+            sacc[kb][4 * q4 + e] = u;
+            amax = fmaxf(amax, __builtin_fabsf(u));
+          }
+        }
+      const bool taylor = !__builtin_amdgcn_ballot_w64(!(amax <= kTaylorU));
+      if (taylor) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float u = sacc[kb][r], u2 = u * u;
+            float pp = __builtin_fmaf(tc4, u2, tc3);
+            pp = __builtin_fmaf(pp, u2, tc2);
+            pp = __builtin_fmaf(pp, u2, tc1);
+            pp = __builtin_fmaf(pp, u2, tc0);
+            sacc[kb][r] = u * pp;
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            sacc[kb][r] = __builtin_fmaf(__builtin_amdgcn_rcpf(ex2(sacc[kb][r] * (2.0f * kLog2e)) + 1.0f),
+                                         -2.0f * cap_l2, cap_l2);
+      }
     }
     if (masked) {
       // key of element r of block kb: j0 + 4 half + kb 32 + 8 (r / 4) + r % 4
@@ -671,8 +742,25 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
       // the words have landed once at most the 2 NLD K/V loads issued after
       // them are in flight (the counter is in order)
       if constexpr (BIAS && !BPRE) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 | (2 * NLD));
+      f32x16 seed[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) seed[kb][r] = 0.f;
+        if constexpr (QS) {
+          // bias of keys j0 + kb 32 + 8 q4 + 4 half + e, element 4 q4 + e
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const uint2 raw = BPRE ? bcur[kb][q4] : bwt[kb][q4];
+            seed[kb][4 * q4 + 0] = lo16<T>(raw.x);
+            seed[kb][4 * q4 + 1] = hi16<T>(raw.x);
+            seed[kb][4 * q4 + 2] = lo16<T>(raw.y);
+            seed[kb][4 * q4 + 3] = hi16<T>(raw.y);
+          }
+        }
+      }
       f32x16 sacc[KB];
-      qk(kc, sacc);
+      qk(kc, sacc, seed);
       softmax_pv(kt, vc, sacc, need_mask, bwt, mwt);
     }
     if (more && BPRE) {
@@ -754,6 +842,7 @@ hipError_t launch_td(const Params &p, const FPlan &pl, hipStream_t st) {
   const bool cap = p.softcap > 0.f;
 #define OLK_FLASH(BMV, CAPV) hipLaunchKernelGGL((flash_fwd_kernel<T, D, BMV, CAPV>), grid, block, 0, st, p, pl)
   if (bm == 2) { if (cap) OLK_FLASH(2, true); else OLK_FLASH(2, false); }
+  else if (bm == 1 && pl.qs) hipLaunchKernelGGL((flash_fwd_kernel<T, D, 1, false, true>), grid, block, 0, st, p, pl);
   else if (bm == 1) { if (cap) OLK_FLASH(1, true); else OLK_FLASH(1, false); }
   else { if (cap) OLK_FLASH(0, true); else OLK_FLASH(0, false); }
 #undef OLK_FLASH
@@ -791,6 +880,14 @@ hipError_t launch_flash(const Params &p, int dtype, hipStream_t st) {
   pl.mask_vec = (p.mask_si % 4 == 0 && p.mask_sh % 4 == 0 && p.mask_sb % 4 == 0 &&
                  ((uintptr_t)p.mask & 3) == 0) ? 1 : 0;
   pl.fuse_present = flash_fuses_present(p) ? 1 : 0;
+  // Q pre-scaled (bias in the accumulator): attn_bias without softcap or BOOL
+  // mask, the scale an exact power of two in [2^-8, 1] (1/sqrt(head size) for
+  // head sizes 4, 16, 64, 256), so q * scale is exact for normal q
+  {
+    int ex = 0;
+    const float mant = frexpf(p.scale, &ex);
+    pl.qs = (p.bias && !p.mask && !(p.softcap > 0.f) && mant == 0.5f && ex >= -7 && ex <= 1) ? 1 : 0;
+  }
   if (dtype == DT_BF16)
     return p.D == 64 ? launch_td<bf16, 64>(p, pl, st) : launch_td<bf16, 128>(p, pl, st);
   return p.D == 64 ? launch_td<f16, 64>(p, pl, st) : launch_td<f16, 128>(p, pl, st);
