@@ -35,9 +35,8 @@ SMALL = {
     "gqa_window_sink_softcap_bf16": Problem(op="gqa", dtype="bf16", B=2, S=300, L=300, Hq=8,
                                             Hkv=2, D=128, Dv=128, causal=1, window=70,
                                             softcap=2.0, has_sink=True),
-    # softcap 30 at head size 128: |s / c| stays under 1/4, so the tiles take
-    # the polynomial tanh (the softcap-2 case above mixes both forms)
-    "gqa_softcap_taylor_bf16": Problem(op="gqa", dtype="bf16", B=2, S=260, L=260, Hq=8, Hkv=2,
+    # a large softcap (30) at head size 128 with sinks: tanh far from saturation
+    "gqa_softcap30_sink_bf16": Problem(op="gqa", dtype="bf16", B=2, S=260, L=260, Hq=8, Hkv=2,
                                        D=128, Dv=128, causal=1, softcap=30.0, has_sink=True),
     "gqa_past_f16": Problem(op="gqa", dtype="f16", B=3, S=37, L=37, P=200, Hq=8, Hkv=2, D=128,
                             Dv=128, causal=1, lens_range=(0, 200)),

@@ -169,10 +169,6 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
   // size 64 at three wavefronts per SIMD, BOOL mask with softcap) select the
   // buffers at run time and keep that wait.
   constexpr bool UNROLL2 = !(BM == 2 && SOFTCAP) && !(D == 64 && SOFTCAP);
-  // polynomial softcap for small |u| (below); the bias, BOOL-mask and
-  // head-size-64 forms keep the exponential form only (their registers do not
-  // hold both)
-  constexpr bool TAYLOR = SOFTCAP && BM == 0 && D == 128;
   __shared__ __attribute__((aligned(16))) T klds0[BN * D];
   __shared__ __attribute__((aligned(16))) T klds1[BN * D];
   __shared__ __attribute__((aligned(16))) T vlds0[BN * D];
@@ -431,13 +427,6 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
   const float inv_cap = SOFTCAP ? 1.0f / p.softcap : 0.f;
   const float cap_l2 = p.softcap * kLog2e;
   const float cap_b = 2.0f * kLog2e * inv_cap, cap_a = p.scale * cap_b;
-  // u = (s scale + bias) / c; for |u| <= 1/4 the odd Taylor series of tanh
-  // through u^9 is exact to float32 (the next term is below 4e-9):
-  // c tanh(u) log2 e = u (C0 + u^2 (C1 + u^2 (C2 + u^2 (C3 + u^2 C4))))
-  const float u_a = p.scale * inv_cap;
-  const float tc0 = cap_l2, tc1 = cap_l2 * (-1.0f / 3.0f), tc2 = cap_l2 * (2.0f / 15.0f),
-              tc3 = cap_l2 * (-17.0f / 315.0f), tc4 = cap_l2 * (62.0f / 2835.0f);
-  constexpr float kTaylorU = 0.25f;
   const float mfv_l2 = p.mfv * kLog2e;
   const float mfv_raw = QS ? p.mfv : p.mfv / p.scale;  // the same offset in raw-score units (scale > 0)
   const T *bias_row = BIAS ? (const T *)p.bias + b * p.bias_sb + row_h * p.bias_sh +
@@ -554,7 +543,7 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
     constexpr bool GENERAL = (BIAS && !QS) || SOFTCAP;
     const char *vl = (const char *)vbuf;
     const int j0 = kt * BN;
-    if (GENERAL && !TAYLOR) {
+    if (GENERAL) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -566,7 +555,6 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
             bv[0] = lo16<T>(raw.x); bv[1] = hi16<T>(raw.x);
             bv[2] = lo16<T>(raw.y); bv[3] = hi16<T>(raw.y);
           }
-          (void)jb;
           uint32_t mw = 0x01010101u;  // BOOL attn_mask bytes of the 4 keys
           if constexpr (MASK) mw = mwt[kb][q4];
 #pragma unroll
@@ -583,52 +571,6 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
             sacc[kb][4 * q4 + e] = ((mw >> (8 * e)) & 0xffu) ? t : kNegInf;
           }
         }
-    }
-    if constexpr (TAYLOR) {
-      // softcap: u = (s scale + bias) / c in place, then one uniform choice
-      // per tile: the polynomial when every |u| of the wavefront's tile is at
-      // most 1/4, else c - 2c / (e^{2u} + 1) (saturates to +-c without NaN:
-      // rcp of +inf is 0)
-      float amax = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          float bv[4] = {0.f, 0.f, 0.f, 0.f};
-          if (BIAS) {
-            const uint2 raw = BPRE ? bcur[kb][q4] : bwt[kb][q4];
-            bv[0] = lo16<T>(raw.x); bv[1] = hi16<T>(raw.x);
-            bv[2] = lo16<T>(raw.y); bv[3] = hi16<T>(raw.y);
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float x = sacc[kb][4 * q4 + e];
-            const float u = BIAS ? __builtin_fmaf(x, u_a, bv[e] * inv_cap) : x * u_a;
-            sacc[kb][4 * q4 + e] = u;
-            amax = fmaxf(amax, __builtin_fabsf(u));
-          }
-        }
-      const bool taylor = !__builtin_amdgcn_ballot_w64(!(amax <= kTaylorU));
-      if (taylor) {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float u = sacc[kb][r], u2 = u * u;
-            float pp = __builtin_fmaf(tc4, u2, tc3);
-            pp = __builtin_fmaf(pp, u2, tc2);
-            pp = __builtin_fmaf(pp, u2, tc1);
-            pp = __builtin_fmaf(pp, u2, tc0);
-            sacc[kb][r] = u * pp;
-          }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            sacc[kb][r] = __builtin_fmaf(__builtin_amdgcn_rcpf(ex2(sacc[kb][r] * (2.0f * kLog2e)) + 1.0f),
-                                         -2.0f * cap_l2, cap_l2);
-      }
     }
     if (masked) {
       // key of element r of block kb: j0 + 4 half + kb 32 + 8 (r / 4) + r % 4
