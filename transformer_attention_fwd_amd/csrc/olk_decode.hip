@@ -14,9 +14,11 @@
 //   the split count (split-minor ids put split s on XCD s when the count is a
 //   multiple of 8, and the later splits of short sequences are empty), and
 //   the always-full first splits are dispatched before the short last ones.
-// * QK^T: v_mfma_f32_16x16x32 with K loaded from global memory straight into
-//   the A operand (16 keys x 32 dims, 16 bytes per lane) and Q^T held in VGPRs
-//   as the B operand (16 columns = the row slots (query, head)).
+// * QK^T: v_mfma_f32_16x16x32 with Q^T held in VGPRs as the B operand (16
+//   columns = the row slots (query, head)).  K is loaded as whole rows (4 rows
+//   per instruction) and its A operand (16 keys x 32 dims) read back from a
+//   per-wavefront LDS tile at head size 128; at head size 64 K goes from
+//   memory straight into the A operand (16 bytes per lane).
 // * The S^T accumulator puts each row slot's 16 scores in 4 lanes; the online
 //   softmax (exp2 domain, lazy rescale) reduces across them with lane swaps.
 // * PV: at head size 128 on v_mfma_f32_16x16x16 (decode_mfma_kernel below:
@@ -398,8 +400,9 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p, DPlan p
   constexpr int NKS = D / 32;   // k-steps of QK^T (32 dims each)
   constexpr int NBLK = D / 16;  // 16-dim blocks of O^T
   constexpr int VRB = D * 2;    // bytes per K/V row, in memory and in LDS
-  // V rows of the current step, one tile per wavefront
+  // K and V rows of the current step, one tile each per wavefront
   __shared__ __attribute__((aligned(16))) T vbw[4][kStep * D];
+  __shared__ __attribute__((aligned(16))) T kbw[4][kStep * D];
   __shared__ __attribute__((aligned(16))) float mrg_ml[4][2][16];
   __shared__ __attribute__((aligned(16))) float mrg_o[4][NR][D];
 
@@ -483,16 +486,18 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p, DPlan p
   const int trr = 4 * kq + ((lane & 15) >> 2);
   const uint32_t tro = (uint32_t)(trr * VRB + 16 * (((lane & 3) >> 1)) + 8 * (lane & 1));
   const int trx = trr & 7;
-  // lane byte offsets within a step: K row n, 16-byte piece kq of each 64-byte
-  // k-step; V row lane / 16 (+ 4 t), chunk lane % 16
-  const uint32_t koff = (uint32_t)n * VRB + (uint32_t)kq * 16u;
+  // lane byte offset within a step, for K and V alike: row lane / 16 (+ 4 t),
+  // 16-byte chunk lane % 16, so one load instruction reads 4 whole rows (full
+  // cache lines).  K loaded in the MFMA operand layout instead (16 rows x 64
+  // bytes per instruction) took twice the address work per byte: 218 vs 202 us
+  // on the decode workload.
   const uint32_t voff = (uint32_t)(lane >> 4) * VRB + (uint32_t)(lane & 15) * 16u;
   const int my_steps = n_steps > wave ? (n_steps - wave + 3) / 4 : 0;
 
   auto load_step = [&](int st, uint4 (&kk)[NKS], uint4 (&vv)[kStep / 4]) __attribute__((always_inline)) {
     const uint32_t so = (uint32_t)((wave + 4 * st) * kStep * VRB);
 #pragma unroll
-    for (int s2 = 0; s2 < NKS; ++s2) kk[s2] = ld_buf16(krs, koff + so + s2 * 64);
+    for (int t = 0; t < NKS; ++t) kk[t] = ld_buf16(krs, voff + so + 4 * t * VRB);
 #pragma unroll
     for (int t = 0; t < kStep / 4; ++t) vv[t] = ld_buf16(vrs, voff + so + 4 * t * VRB);
   };
@@ -506,6 +511,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p, DPlan p
   uint4 k0[NKS], k1[NKS], k2[NKS];
   uint4 v0[kStep / 4], v1[kStep / 4], v2[kStep / 4];
   char *vl = (char *)vbw[wave];
+  char *kl = (char *)kbw[wave];
   auto body = [&](int it, uint4 (&kr)[NKS], const uint4 (&vr)[kStep / 4], uint4 (&kf)[NKS],
                   uint4 (&vf)[kStep / 4]) __attribute__((always_inline)) {
     if (it + 2 < my_steps) load_step(it + 2, kf, vf);
@@ -513,7 +519,20 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p, DPlan p
     // S^T (16 keys x 16 slots)
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s2 = 0; s2 < NKS; ++s2) sacc = mma16(__builtin_bit_cast(vec8, kr[s2]), qreg[s2], sacc);
+    for (int t = 0; t < NKS; ++t) {
+      // the step's K rows into this wavefront's LDS tile: chunk c of row r at
+      // slot c ^ (r & 15), so the operand reads below (16 rows at one chunk)
+      // hit distinct banks; one wavefront's LDS operations run in order, so
+      // no barrier is needed
+      const int r = 4 * t + (lane >> 4), c = lane & 15;
+      *(uint4 *)(kl + r * VRB + 16 * (c ^ (r & 15))) = kr[t];
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < NKS; ++s2) {
+      // A operand: key row n, dims 32 s2 + 8 kq + e (chunk 4 s2 + kq)
+      const vec8 a = *(const vec8 *)(kl + n * VRB + 16 * ((4 * s2 + kq) ^ n));
+      sacc = mma16(a, qreg[s2], sacc);
+    }
     // scores of slot n for keys j0 + 4 kq + r, log2 domain, masked
     float t4[4];
     float mx = kNegInf;

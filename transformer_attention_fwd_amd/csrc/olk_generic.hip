@@ -204,7 +204,11 @@ __global__ __launch_bounds__(kWave) void combine_kernel(Params p, int n_split, i
   const int64_t row = ((int64_t)b * p.S + i) * p.Hq + h;
   const int64_t rec = p.Dv + 4;
   const float *part = ws + row * n_split * rec;
-  // Only the splits that hold keys of this row's range [lo, hi) are read:
+  // The first record maxima are loaded before the lengths, so the two loads'
+  // latencies overlap (records of splits the decode kernels skipped hold
+  // stale values, read but never used).
+  const float m_first = lane < n_split ? part[lane * rec] : kNegInf;
+  // Only the splits that hold keys of this row's range [lo, hi) are used:
   // every partial kernel writes the records of those (a split outside the
   // range contributes nothing, and the decode kernels write no record there).
   const Seq s = seq_info(p, b);
@@ -214,8 +218,9 @@ __global__ __launch_bounds__(kWave) void combine_kernel(Params p, int n_split, i
   const int lo = p.window > 0 ? max(0, pos - p.window + 1) : 0;
   const int sp0 = lo / split_keys;
   const int sp1 = hi > lo ? min(n_split, (hi + split_keys - 1) / split_keys) : sp0;
-  float M = kNegInf;
-  for (int sp = sp0 + lane; sp < sp1; sp += kWave) M = fmaxf(M, part[sp * rec]);
+  float M = lane >= sp0 && lane < sp1 ? m_first : kNegInf;
+  for (int sp = kWave + lane; sp < sp1; sp += kWave)
+    if (sp >= sp0) M = fmaxf(M, part[sp * rec]);
   M = wave_max(M);
   T *yr = (T *)p.y + b * p.y_sb + (int64_t)i * p.y_ss + h * p.y_sh;
   if (M == kNegInf) {  // no allowed key: zeros
