@@ -65,6 +65,8 @@ __device__ __forceinline__ f32x16 mma(f16x8 a, f16x8 b, f32x16 c) {
 
 // s_waitcnt immediate for vmcnt(0) only (gfx9 encoding: expcnt 7, lgkmcnt 15)
 constexpr int kWaitVmcnt0 = 0x0F70;
+// s_waitcnt immediate for lgkmcnt(0) only (vmcnt 63, expcnt 7)
+constexpr int kWaitLgkmcnt0 = 0xC07F;
 constexpr int kThreads = 256;
 constexpr int kSlots = 128;  // row slots per workgroup (4 wavefronts x 32)
 constexpr float kLog2e = 1.4426950408889634f;
@@ -464,10 +466,48 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
   // Otherwise a tile's bias and mask words are loaded at the start of the
   // tile, before the next tile's K/V loads: the memory counter is in order,
   // so waiting for loads issued after those would wait for them too.
-  constexpr bool BPRE = BIAS && D == 64 && (kOcc<D, BM> == 2 || QS);
+  // BLDS (QS at head size 64, one query per row slot): the next tile's bias
+  // rows go from memory straight into a per-wavefront LDS tile (8 rows x 128
+  // bytes per instruction) and each lane reads its values from there in the
+  // accumulator layout; gathered per lane they took 8 bytes from each of 32
+  // rows per instruction
+  constexpr bool BLDS = QS && D == 64;
+  constexpr bool BPRE = BIAS && D == 64 && kOcc<D, BM> == 2 && !BLDS;
   typedef uint2 BiasWords[BIAS ? KB : 1][4];
   typedef uint32_t MaskWords[MASK ? KB : 1][4];
   BiasWords bcur, bnext;
+  // BLDS: bias of a wavefront's 32 row slots for one tile, 128 bytes per row;
+  // the 16-byte chunk c of row r sits in slot c ^ ((r >> 1) & 7), so the
+  // 8-byte reads below (32 rows at one chunk) spread over the banks
+  __shared__ __attribute__((aligned(16))) char blds[BLDS ? 4 * 32 * 128 : 16];
+  const T *bias_g = BIAS ? (const T *)p.bias + b * p.bias_sb + (g * p.G + hg * pl.GH) * p.bias_sh
+                         : nullptr;
+  auto bias_rows_whole = [&](int kt) { return pl.bias_vec && kt * BN + BN <= p.bias_cols; };
+  auto load_bias_rows = [&](int kt) __attribute__((always_inline)) {
+    if constexpr (BLDS) {
+      // lane l of instruction t lands in slot l % 8 of row 8 t + l / 8 (one
+      // query per row slot, clamped to the last query)
+      char *bl = blds + wave * 32 * 128;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int r = 8 * t + (lane >> 3);
+        const int ri = min(i0 + wave * 32 + r, p.S - 1);
+        const int c = (lane & 7) ^ ((r >> 1) & 7);
+        load_lds16(bias_g + (int64_t)ri * p.bias_si + kt * BN + 8 * c, bl + t * 1024);
+      }
+    }
+  };
+  auto bias_from_lds = [&]() __attribute__((always_inline)) {
+    if constexpr (BLDS) {
+      const char *bl = blds + wave * 32 * 128 + col * 128;
+      const int f = (col >> 1) & 7;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          bcur[kb][q4] = *(const uint2 *)(bl + 16 * ((4 * kb + q4) ^ f) + 8 * half);
+    }
+  };
   auto load_bias = [&](int kt, BiasWords &bb) __attribute__((always_inline)) {
     if constexpr (BIAS) {
       // one uniform choice for the tile (per-call choices leave the
@@ -649,6 +689,7 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
   if (kt0 < kt1) {
     issue_loads(kt0, klds0, vlds0);
     if (BPRE) load_bias(kt0, bcur);
+    if (BLDS && wave_active && bias_rows_whole(kt0)) load_bias_rows(kt0);
   }
   load_q();
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -665,7 +706,17 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
     BiasWords bwt;
     MaskWords mwt;
     if (wave_active) {
-      if (!BPRE) load_bias(kt, bwt);
+      if constexpr (BLDS) {
+        if (bias_rows_whole(kt)) {
+          bias_from_lds();
+          // the reads are done before the next tile's rows overwrite them
+          __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
+        } else {
+          load_bias(kt, bcur);  // a tile past the bias columns: per key
+        }
+      } else if (!BPRE) {
+        load_bias(kt, bwt);
+      }
       load_mask(kt, mwt);
     }
     // (the empty asm keeps the compiler from issuing the word loads after
@@ -676,6 +727,7 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
     // loads and the wait for the words above can leave these in flight
     issue_loads(more ? kt + 1 : max(kt - 1, kt0), kn, vn);
     if (more && BPRE) load_bias(kt + 1, bnext);
+    if (BLDS && more && wave_active && bias_rows_whole(kt + 1)) load_bias_rows(kt + 1);
     if (wave_active) {
       const int j0 = kt * BN;
       const bool need_mask = (p.causal && j0 + BN - 1 > pos_min) ||
@@ -683,7 +735,7 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
                              j0 < lo || (p.pad_add && j0 + BN > s.pad);
       // the words have landed once at most the 2 NLD K/V loads issued after
       // them are in flight (the counter is in order)
-      if constexpr (BIAS && !BPRE) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 | (2 * NLD));
+      if constexpr (BIAS && !BPRE && !BLDS) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 | (2 * NLD));
       f32x16 seed[KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
@@ -693,7 +745,7 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
           // bias of keys j0 + kb 32 + 8 q4 + 4 half + e, element 4 q4 + e
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
-            const uint2 raw = BPRE ? bcur[kb][q4] : bwt[kb][q4];
+            const uint2 raw = (BPRE || BLDS) ? bcur[kb][q4] : bwt[kb][q4];
             seed[kb][4 * q4 + 0] = lo16<T>(raw.x);
             seed[kb][4 * q4 + 1] = hi16<T>(raw.x);
             seed[kb][4 * q4 + 2] = lo16<T>(raw.y);
@@ -829,6 +881,9 @@ hipError_t launch_flash(const Params &p, int dtype, hipStream_t st) {
     int ex = 0;
     const float mant = frexpf(p.scale, &ex);
     pl.qs = (p.bias && !p.mask && !(p.softcap > 0.f) && mant == 0.5f && ex >= -7 && ex <= 1) ? 1 : 0;
+    // at head size 64 the bias rows go through LDS, which takes one query per
+    // row slot (GH = 1)
+    if (p.D == 64 && pl.GH != 1) pl.qs = 0;
   }
   if (dtype == DT_BF16)
     return p.D == 64 ? launch_td<bf16, 64>(p, pl, st) : launch_td<bf16, 128>(p, pl, st);
