@@ -140,6 +140,19 @@ SMALL = {
     "mha_binary_mask_bst_f16": Problem(op="mha", dtype="f16", B=2, S=17, L=40, Hq=2, Hkv=2,
                                        D=64, Dv=64, kv_rank=4, causal=0, has_lens=False,
                                        mask_kind="int32", mask_bhs=(2, 1, 17)),
+    # binary masks with few ones under a causal mask: many rows are all zeros
+    # (a uniform shift that leaves the softmax as without the mask); rows of
+    # 100 int32 elements take word loads up to the ragged last key tile
+    "mha_binary_mask_sparse_causal_bf16": Problem(op="mha", dtype="bf16", B=2, S=100, L=100,
+                                                  Hq=4, Hkv=4, D=128, Dv=128, kv_rank=4,
+                                                  causal=1, has_lens=False, mask_kind="int32",
+                                                  mask_bhs=(2, 1, 100), mask_p=0.05),
+    # a small filter value: masked keys keep weight, so the added offset shows
+    "mha_binary_mask_small_filter_f16": Problem(op="mha", dtype="f16", B=2, S=50, L=64, Hq=4,
+                                                Hkv=4, D=64, Dv=64, kv_rank=4, causal=0,
+                                                has_lens=False, mask_kind="int32",
+                                                mask_bhs=(2, 1, 1), mask_p=0.5,
+                                                mask_filter_value=-2.0, bias_bh=(2, 4)),
     # MultiHeadAttention rank-3 self-attention with k / v projection-bias
     # segments, unidirectional with a past
     "mha_self_projbias_past_f16": Problem(op="mha", dtype="f16", B=2, S=40, L=40, P=30, Hq=4,
@@ -160,11 +173,11 @@ def _run(p, dev, **kw):
 
 
 def tiled_capable(p, mode="fwd"):
-    # BOOL masks run in the prefill kernel (not in the split-KV partials);
-    # binary masks and the qk output go to the generic kernels
-    if p.mask_kind == "int32" or p.qk_mode is not None:
+    # attn_mask (BOOL and binary) runs in the prefill kernel, not in the
+    # split-KV partials; the qk output goes to the generic kernels
+    if p.qk_mode is not None:
         return False
-    if p.mask_kind == "bool" and mode == "decode":
+    if p.mask_kind and mode == "decode":
         return False
     return p.dtype in ("f16", "bf16") and p.D == p.Dv and p.D in (64, 128)
 
@@ -177,7 +190,7 @@ def test_small_parity(name, mode, kernel):
     p = SMALL[name]
     if kernel == "tiled" and not tiled_capable(p, mode):
         pytest.skip("the tiled kernels cover f16/bf16 with head size 64 or 128 (no "
-                    "binary masks or qk output; BOOL masks in prefill only)")
+                    "qk output; attn_mask in prefill only)")
     inp = make_inputs(p, 500 + list(SMALL).index(name))
     _say(f"[parity] {name} mode={mode} kernel={kernel}")
     c = _run(p, to_dev(inp), mode=mode, kernel=kernel)

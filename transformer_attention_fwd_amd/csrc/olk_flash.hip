@@ -145,7 +145,8 @@ struct FPlan {
 // form needs more registers and keeps two), two at head size 128.
 template <int D, int BM> constexpr int kOcc = (D == 64 && BM != 2) ? 3 : 2;
 
-// BM: 0 no bias, 1 attn_bias, 2 BOOL attn_mask (with or without attn_bias).
+// BM: 0 no bias, 1 attn_bias, 2 attn_mask (BOOL, or MultiHeadAttention's int32
+// binary mask), with or without attn_bias.
 // QS (attn_bias without softcap, the scale an exact power of two): Q is
 // multiplied by the scale as it is loaded (exact: a change of exponent) and
 // the bias seeds the QK^T accumulator, so the matrix cores add it and the
@@ -447,12 +448,28 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
       e4[e] = jb + e < p.bias_cols ? __builtin_bit_cast(uint16_t, bias_row[jb + e]) : (uint16_t)0;
     return make_uint2(e4[0] | ((uint32_t)e4[1] << 16), e4[2] | ((uint32_t)e4[3] << 16));
   };
-  // BOOL attn_mask: bytes of keys jb..jb+3 of this row slot (0 past the mask's columns)
-  const uint8_t *mask_row = MASK ? (const uint8_t *)p.mask + b * p.mask_sb +
-                                                 row_h * p.mask_sh +
-                                                 (int64_t)(row_ok ? row_i : 0) * p.mask_si
-                                           : nullptr;
+  // attn_mask of keys jb..jb+3 of this row slot as 4 flag bytes (nonzero =
+  // attend; 0 past the mask's columns): BOOL masks are bytes, MultiHeadAttention
+  // binary masks int32 (mask_kind 2)
+  const bool mask_i32 = MASK && p.mask_kind == 2;
+  const int64_t mask_e = MASK ? b * p.mask_sb + row_h * p.mask_sh +
+                                    (int64_t)(row_ok ? row_i : 0) * p.mask_si
+                              : 0;
+  const uint8_t *mask_row = MASK ? (const uint8_t *)p.mask + mask_e : nullptr;
+  const int32_t *mask_row32 = MASK ? (const int32_t *)p.mask + mask_e : nullptr;
   auto mask4 = [&](int jb, bool full) {
+    if (mask_i32) {
+      if (full) {
+        const uint4 v = *(const uint4 *)(mask_row32 + jb);
+        return (uint32_t)(v.x != 0) | ((uint32_t)(v.y != 0) << 8) | ((uint32_t)(v.z != 0) << 16) |
+               ((uint32_t)(v.w != 0) << 24);
+      }
+      uint32_t w = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (jb + e < p.mask_cols) w |= (uint32_t)(mask_row32[jb + e] != 0) << (8 * e);
+      return w;
+    }
     if (full) return *(const uint32_t *)(mask_row + jb);
     uint32_t w = 0;
 #pragma unroll
@@ -607,8 +624,9 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
               t = __builtin_fmaf(__builtin_amdgcn_rcpf(ex2(x2) + 1.0f), -2.0f * cap_l2, cap_l2);
             }
             else t = (sacc[kb][4 * q4 + e] * p.scale + bv[e]) * kLog2e;
-            // a false mask element excludes the key after the score pipeline
-            sacc[kb][4 * q4 + e] = ((mw >> (8 * e)) & 0xffu) ? t : kNegInf;
+            // a false BOOL element excludes the key after the score pipeline;
+            // a zero binary (int32) element adds mask_filter_value to it
+            sacc[kb][4 * q4 + e] = ((mw >> (8 * e)) & 0xffu) ? t : (mask_i32 ? t + mfv_l2 : kNegInf);
           }
         }
     }
@@ -871,8 +889,9 @@ hipError_t launch_flash(const Params &p, int dtype, hipStream_t st) {
   pl.xcd_remap = n_bg % 8 == 0 ? 1 : 0;
   pl.bias_vec = (p.bias_si % 4 == 0 && p.bias_sh % 4 == 0 && p.bias_sb % 4 == 0 &&
                  ((uintptr_t)p.bias & 7) == 0) ? 1 : 0;
+  // word loads of 4 mask elements: 4-byte (BOOL) or 16-byte (int32) aligned rows
   pl.mask_vec = (p.mask_si % 4 == 0 && p.mask_sh % 4 == 0 && p.mask_sb % 4 == 0 &&
-                 ((uintptr_t)p.mask & 3) == 0) ? 1 : 0;
+                 ((uintptr_t)p.mask & (p.mask_kind == 2 ? 15 : 3)) == 0) ? 1 : 0;
   pl.fuse_present = flash_fuses_present(p) ? 1 : 0;
   // Q pre-scaled (bias in the accumulator): attn_bias without softcap or BOOL
   // mask, the scale an exact power of two in [2^-8, 1] (1/sqrt(head size) for
