@@ -153,6 +153,18 @@ SMALL = {
                                                 has_lens=False, mask_kind="int32",
                                                 mask_bhs=(2, 1, 1), mask_p=0.5,
                                                 mask_filter_value=-2.0, bias_bh=(2, 4)),
+    # head size 128 without bias or mask: two query heads per KV head with a
+    # variable past and a window; MultiHeadAttention cross-attention with one
+    # head per group and ragged query and key ends; ai.onnx Attention with a
+    # cache, nonpad lengths, softcap and few key tiles
+    "gqa_gh2_past_window_f16": Problem(op="gqa", dtype="f16", B=2, S=150, L=150, P=90, Hq=4,
+                                       Hkv=2, D=128, Dv=128, causal=1, window=100,
+                                       lens_range=(10, 90)),
+    "mha_cross_d128_bf16": Problem(op="mha", dtype="bf16", B=2, S=300, L=333, Hq=2, Hkv=2,
+                                   D=128, Dv=128, kv_rank=4, causal=0, has_lens=False),
+    "attention_cache_softcap_f16": Problem(op="attention", dtype="f16", B=2, S=65, L=60,
+                                           P=31, Hq=8, Hkv=2, D=128, Dv=128, causal=1,
+                                           has_lens=True, lens_range=(40, 91), softcap=5.0),
     # MultiHeadAttention rank-3 self-attention with k / v projection-bias
     # segments, unidirectional with a past
     "mha_self_projbias_past_f16": Problem(op="mha", dtype="f16", B=2, S=40, L=40, P=30, Hq=4,

@@ -126,11 +126,6 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Position of key k (0 <= k < 16) inside its 16-key group of a V^T row: the
-// group stores keys {0-3, 8-11, 4-7, 12-15}, so the 8 keys that lane half h
-// supplies to one 16-key MFMA step (4h..4h+3 and 8+4h..8+4h+3) are contiguous.
-__device__ __forceinline__ int quad_slot(int qq) { return ((qq & 1) << 1) | (qq >> 1); }
-
 struct FPlan {
   int GH, n_hg, QW, n_qt;
   int qs;            // Q pre-scaled, bias in the accumulator (see flash_fwd_kernel)
