@@ -165,6 +165,18 @@ SMALL = {
     "attention_cache_softcap_f16": Problem(op="attention", dtype="f16", B=2, S=65, L=60,
                                            P=31, Hq=8, Hkv=2, D=128, Dv=128, causal=1,
                                            has_lens=True, lens_range=(40, 91), softcap=5.0),
+    # more head-size-128 cases without bias or mask: two query heads per KV
+    # head with a window and a ragged end (no past), MultiHeadAttention
+    # cross-attention with key-padding lengths (excluded), ai.onnx Attention
+    # with nonpad lengths under a causal mask
+    "gqa_gh2_window_f16": Problem(op="gqa", dtype="f16", B=2, S=150, L=150, Hq=4, Hkv=2,
+                                  D=128, Dv=128, causal=1, window=100),
+    "mha_cross_lens_d128_f16": Problem(op="mha", dtype="f16", B=2, S=90, L=200, Hq=4, Hkv=4,
+                                       D=128, Dv=128, kv_rank=4, causal=0, has_lens=True,
+                                       lens_range=(50, 200)),
+    "attention_nonpad_d128_bf16": Problem(op="attention", dtype="bf16", B=2, S=100, L=130,
+                                          Hq=8, Hkv=2, D=128, Dv=128, causal=1, has_lens=True,
+                                          lens_range=(60, 130)),
     # MultiHeadAttention rank-3 self-attention with k / v projection-bias
     # segments, unidirectional with a past
     "mha_self_projbias_past_f16": Problem(op="mha", dtype="f16", B=2, S=40, L=40, P=30, Hq=4,
