@@ -420,7 +420,9 @@ olk_status olk_attention_fwd(const olk_attn_desc *desc, const olk_attn_io *io, v
   } else if (kv_bias_path(desc, io)) {
     e = kv_bias_prepass(p, desc->dtype, s);
   } else {
-    if (use_tiled && olk::flash_fuses_present(p)) p.present_past_only = 1;
+    // the attention kernel writes the present rows of the new keys itself
+    // (the generic kernel always, the prefill kernel for GroupQueryAttention)
+    if (!use_tiled || olk::flash_fuses_present(p)) p.present_past_only = 1;
     e = olk::launch_present(p, desc->dtype, s);
   }
   if (e != hipSuccess) return OLK_E_HIP;

@@ -156,6 +156,19 @@ __global__ __launch_bounds__(kWave) void generic_kernel(Params p) {
     const int d = threadIdx.x + k * kWave;
     if (d < p.Dv) yr[d] = from_f32<T>(st.o[k] * inv);
   }
+  // present rows of the new keys (the present writer copied only the past):
+  // the workgroup of the first query head of each KV group writes new rows
+  // i, i + S, ... of that group, bits copied (positions past_b + j)
+  if (p.present_past_only && p.present_k && p.present_v && h % p.G == 0) {
+    const int g = h / p.G;
+    for (int j = i; j < p.L; j += p.S) {
+      const int64_t pos = ((int64_t)b * p.Hkv + g) * p.T + s.past + j;
+      const T *kr = (const T *)p.k + b * p.k_sb + (int64_t)j * p.k_ss + g * p.k_sh;
+      const T *vr = (const T *)p.v + b * p.v_sb + (int64_t)j * p.v_ss + g * p.v_sh;
+      for (int c = threadIdx.x; c < p.D; c += kWave) ((T *)p.present_k)[pos * p.D + c] = kr[c];
+      for (int c = threadIdx.x; c < p.Dv; c += kWave) ((T *)p.present_v)[pos * p.Dv + c] = vr[c];
+    }
+  }
 }
 
 // Split-KV partial: block (h, b*S + i, split) handles keys
