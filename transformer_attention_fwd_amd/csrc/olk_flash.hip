@@ -133,6 +133,7 @@ struct FPlan {
   int bias_vec;
   int mask_vec;      // BOOL mask rows are 4-byte aligned
   int fuse_present;
+  int fixm;          // softcap with bf16 P: fixed exponent offset 0 instead of a running max
 };
 
 // Wavefronts per SIMD the register budget is sized for: three at head size 64
@@ -558,7 +559,12 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
-  float m = kNegInf, l = 0.f;
+  // With softcap every score lies in [-c, c] (log2 units: +-c log2 e), so for
+  // c log2 e <= 100 the exponentials 2^s need no running max: bf16 / fp32
+  // hold 2^-100..2^100 and a row sum of them (fixm; the result is the same
+  // weighted mean, only the common factor differs).
+  const bool fixm = SOFTCAP && pl.fixm;
+  float m = fixm ? 0.f : kNegInf, l = 0.f;
 
   // S^T of one tile: KB blocks of 32 keys; seed: the accumulators' start
   // (zeros, or with QS the tile's bias values)
@@ -590,9 +596,16 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
   // are rewritten into the log2 domain; otherwise they stay raw (scale > 0,
   // folded into the exponent's FMA) and masking only writes -inf in place, so
   // masked and unmasked tiles share one body.
+  // With softcap the scores are kept as r = 1 / (e^{2u} + 1) in [0, 1]: the
+  // capped score is t = c' - 2 c' r (c' = c log2 e), decreasing in r, so the
+  // row max is taken as a min over r (masked keys: r = +inf, t = -inf) and
+  // the exponent t - m folds into one FMA, fma(r, -2c', c' - m).  (Softcap
+  // never meets MultiHeadAttention's additive filter value: that operator
+  // has no softcap.)
   auto softmax_pv = [&](int kt, const T *vbuf, f32x16 (&sacc)[KB], bool masked, const BiasWords &bwt,
                         const MaskWords &mwt) __attribute__((always_inline)) {
     constexpr bool GENERAL = (BIAS && !QS) || SOFTCAP;
+    constexpr float kOut = SOFTCAP ? __builtin_huge_valf() : kNegInf;  // an excluded key
     const char *vl = (const char *)vbuf;
     const int j0 = kt * BN;
     if (GENERAL) {
@@ -615,13 +628,13 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
             if (SOFTCAP) {
               const float x2 = BIAS ? __builtin_fmaf(sacc[kb][4 * q4 + e], cap_a, bv[e] * cap_b)
                                     : sacc[kb][4 * q4 + e] * cap_a;
-              // saturates to +-c without NaN (rcp of +inf is 0)
-              t = __builtin_fmaf(__builtin_amdgcn_rcpf(ex2(x2) + 1.0f), -2.0f * cap_l2, cap_l2);
+              // r in [0, 1] without NaN (rcp of +inf is 0)
+              t = __builtin_amdgcn_rcpf(ex2(x2) + 1.0f);
             }
             else t = (sacc[kb][4 * q4 + e] * p.scale + bv[e]) * kLog2e;
             // a false BOOL element excludes the key after the score pipeline;
             // a zero binary (int32) element adds mask_filter_value to it
-            sacc[kb][4 * q4 + e] = ((mw >> (8 * e)) & 0xffu) ? t : (mask_i32 ? t + mfv_l2 : kNegInf);
+            sacc[kb][4 * q4 + e] = ((mw >> (8 * e)) & 0xffu) ? t : (mask_i32 ? t + mfv_l2 : kOut);
           }
         }
     }
@@ -642,27 +655,40 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          sacc[kb][r] = (uint32_t)(jr + kb * 32 + 8 * (r >> 2) + (r & 3)) < a_w ? sacc[kb][r] : kNegInf;
+          sacc[kb][r] = (uint32_t)(jr + kb * 32 + 8 * (r >> 2) + (r & 3)) < a_w ? sacc[kb][r] : kOut;
     }
-    float mx = kNegInf;
+    if (!fixm) {
+      float mx;
+      if (SOFTCAP) {
+        float mn = kOut;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = max_halves(mx);
-    if (!GENERAL) mx *= sl;
-    const float m_new = fmaxf(m, mx);
-    const bool grow = m_new > m + kRescale;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-      const float alpha = grow ? ex2(m - m_new) : 1.0f;
-      m = grow ? m_new : m;
-      l *= alpha;
+          for (int r = 0; r < 16; ++r) mn = fminf(mn, sacc[kb][r]);
+        mx = __builtin_fmaf(mn, -2.0f * cap_l2, cap_l2);
+      } else {
+        mx = kNegInf;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+      }
+      mx = max_halves(mx);
+      if (!GENERAL) mx *= sl;
+      const float m_new = fmaxf(m, mx);
+      const bool grow = m_new > m + kRescale;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float alpha = grow ? ex2(m - m_new) : 1.0f;
+        m = grow ? m_new : m;
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      }
     }
     const float mu = m == kNegInf ? 0.f : m;
+    const float cap_off = cap_l2 - mu;  // softcap: exponent fma(r, -2c', c' - m)
     // P in 16-key steps, each feeding its PV MFMAs at once, so the matrix
     // core starts while the VALU computes the next step's exponentials.
     // Lane half h supplies keys 16st + {4h..4h+3, 8+4h..8+4h+3}.  The row
@@ -674,7 +700,8 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float x = sacc[st >> 1][8 * (st & 1) + e];
-        pb[e] = (T)(GENERAL ? ex2(x - mu) : ex2(__builtin_fmaf(x, sl, -mu)));
+        pb[e] = (T)(SOFTCAP ? ex2(__builtin_fmaf(x, -2.0f * cap_l2, cap_off))
+                            : GENERAL ? ex2(x - mu) : ex2(__builtin_fmaf(x, sl, -mu)));
       }
       lsum2[st & 1] = add8(pb, lsum2[st & 1]);
 #pragma unroll
@@ -819,7 +846,7 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
         lt += ex2(z - m);
       }
     }
-    inv = 1.0f / lt;
+    inv = lt > 0.f ? 1.0f / lt : 0.f;  // (fixm: every key masked leaves lt = 0)
   }
   T *yr = (T *)p.y + b * p.y_sb + (int64_t)row_i * p.y_ss + row_h * p.y_sh;
 #pragma unroll
@@ -888,6 +915,10 @@ hipError_t launch_flash(const Params &p, int dtype, hipStream_t st) {
   pl.mask_vec = (p.mask_si % 4 == 0 && p.mask_sh % 4 == 0 && p.mask_sb % 4 == 0 &&
                  ((uintptr_t)p.mask & (p.mask_kind == 2 ? 15 : 3)) == 0) ? 1 : 0;
   pl.fuse_present = flash_fuses_present(p) ? 1 : 0;
+  // fixed exponent offset: softcap bounds the scores to +-c; bf16 P (f16 would
+  // overflow), and no additive filter value after the cap
+  pl.fixm = (dtype == DT_BF16 && p.softcap > 0.f && p.softcap * 1.4426950408889634f <= 100.f &&
+             !p.pad_add && p.mask_kind != 2) ? 1 : 0;
   // Q pre-scaled (bias in the accumulator): attn_bias without softcap or BOOL
   // mask, the scale an exact power of two in [2^-8, 1] (1/sqrt(head size) for
   // head sizes 4, 16, 64, 256), so q * scale is exact for normal q
