@@ -829,7 +829,6 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
 
   // ---- epilogue: combine halves, sink, normalise, store ----
   const float l_tot = sum_halves(l);
-  if (!row_ok) return;
   float inv = 0.f;
   if (m != kNegInf) {
     float lt = l_tot;
@@ -848,17 +847,33 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
     }
     inv = lt > 0.f ? 1.0f / lt : 0.f;  // (fixm: every key masked leaves lt = 0)
   }
-  T *yr = (T *)p.y + b * p.y_sb + (int64_t)row_i * p.y_ss + row_h * p.y_sh;
+  // Y goes through LDS so that whole rows are stored: each wavefront writes
+  // its 32 rows (row-major, 16-byte chunks XOR-swizzled by the row) into its
+  // own 32 RB bytes of the K buffers, then CH lanes store one row (16 bytes
+  // each), 64 / CH rows per instruction (lane-per-row stores of 8 bytes at a
+  // time were measured to take ~4k clocks per workgroup).  Rows past S are
+  // staged but not stored.
+  if (fuse_end && kt0 < kt1) __syncthreads();  // the present copy read the K/V buffers
+  char *ys = (char *)(wave < 2 ? klds0 : klds1) + (wave & 1) * 32 * RB;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      const int d = db * 32 + 8 * q4 + 4 * half;
       typename FV<T>::v4 v4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) v4[e] = (T)(o[db][4 * q4 + e] * inv);
-      *(typename FV<T>::v4 *)&yr[d] = v4;
+      const int c = db * 4 + q4;  // 16-byte chunk of dims 8c..8c+7; this lane's half: 4 half..
+      *(typename FV<T>::v4 *)(ys + col * RB + 16 * (c ^ (col & (CH - 1))) + 8 * half) = v4;
     }
+  constexpr int RPI = 64 / CH;  // rows per store instruction
+#pragma unroll
+  for (int k = 0; k < 32 / RPI; ++k) {
+    const int r = k * RPI + lane / CH, c = lane % CH;
+    const uint4 v = *(const uint4 *)(ys + r * RB + 16 * (c ^ (r & (CH - 1))));
+    const int sl = wave * 32 + r;
+    const int ri = i0 + sl / pl.GH, rh = g * p.G + hg * pl.GH + sl % pl.GH;
+    if (ri < p.S) *(uint4 *)((T *)p.y + b * p.y_sb + (int64_t)ri * p.y_ss + rh * p.y_sh + c * 8) = v;
+  }
 }
 
 int gh_for(int G) {
