@@ -16,8 +16,9 @@
 //   accumulator layout a lane owns one row slot and half of a tile's keys, so
 //   the softmax max/sum are in-lane plus one exchange with lane ^ 32, and P^T
 //   is already the B operand of the PV MFMA.
-// * K and V tiles go from memory straight into LDS (global_load_lds_dwordx4:
-//   16 bytes per lane, no staging registers), unpadded rows with the 16-byte
+// * K and V tiles go from memory straight into LDS (buffer_load_dwordx4 ...
+//   lds for tiles from one source, else global_load_lds_dwordx4: 16 bytes per
+//   lane, no staging registers), unpadded rows with the 16-byte
 //   chunks of each row XOR-swizzled by a function of the row, one function
 //   for K (the QK^T operand reads 16 rows at one chunk per 16 lanes) and one
 //   for V.  The V^T operand of PV is read with ds_read_b64_tr_b16 from the
@@ -107,6 +108,24 @@ __device__ __forceinline__ float add8(const f16x8 &p, float acc) {
 // lds + 16 l (the LDS address is the same for every lane of the instruction)
 __device__ __forceinline__ void load_lds16(const void *g, void *lds) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+
+// The same through a buffer descriptor (buffer_load_dwordx4 ... lds): lane
+// l's 16 bytes from byte off (per lane) of the descriptor's range land at
+// lds + 16 l.  Unlike global_load_lds this form issues without waiting while
+// MFMAs stream elsewhere on the CU.  Written as inline asm (the builtin for it
+// is taken to alias every LDS access and made the compiler wait for these
+// loads ahead of unrelated LDS reads): the compiler does not count these
+// loads, so every read of their destination follows the kernel's own
+// vmcnt(0) wait and barrier.  M0 holds the LDS base; the ISA asks for one wait
+// state between an M0 write and a load into LDS.
+__device__ __forceinline__ void buf_lds16(__amdgpu_buffer_rsrc_t r, uint32_t off, const void *lds) {
+  const uint32_t la = (uint32_t)(size_t)(__attribute__((address_space(3))) const void *)lds;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(off), "s"(r), "s"(la) : "memory", "m0");
+}
+// raw buffer descriptor at base: no stride, 2^31 - 1 bytes, 32-bit data format
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void *base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, 0x7fffffff, 0x00020000);
 }
 
 // two floats rounded (RNE) to the element type, packed low / high
@@ -357,24 +376,24 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
     char *vl = (char *)vdst + wave * NLD * 1024;
     const bool full = j0 >= lo && j0 + BN <= hi;
     if (full && (j0 >= s.src || j0 + BN <= s.src)) {
-      // the whole tile from one source: uniform base plus the fixed 32-bit
-      // lane offsets of that source
+      // the whole tile from one source: a descriptor based at the tile's
+      // first row plus the fixed 32-bit lane offsets of that source
       if (j0 >= s.src) {
-        const char *kb = (const char *)(knew + (int64_t)(j0 - s.src) * p.k_ss);
-        const char *vb = (const char *)(vnew + (int64_t)(j0 - s.src) * p.v_ss);
+        const __amdgpu_buffer_rsrc_t rk = rsrc_of(knew + (int64_t)(j0 - s.src) * p.k_ss);
+        const __amdgpu_buffer_rsrc_t rv = rsrc_of(vnew + (int64_t)(j0 - s.src) * p.v_ss);
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
-          load_lds16(kb + kon[i], kl + i * 1024);
-          load_lds16(vb + von[i], vl + i * 1024);
+          buf_lds16(rk, kon[i], kl + i * 1024);
+          buf_lds16(rv, von[i], vl + i * 1024);
         }
       } else {
-        const char *kb = (const char *)(kpast + (int64_t)j0 * D);
-        const char *vb = (const char *)(vpast + (int64_t)j0 * D);
+        const __amdgpu_buffer_rsrc_t rk = rsrc_of(kpast + (int64_t)j0 * D);
+        const __amdgpu_buffer_rsrc_t rv = rsrc_of(vpast + (int64_t)j0 * D);
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
           const uint32_t ro = (uint32_t)lrow[i] * (uint32_t)(D * sizeof(T));  // past rows are dense
-          load_lds16(kb + ro + kcb[i], kl + i * 1024);
-          load_lds16(vb + ro + vcb[i], vl + i * 1024);
+          buf_lds16(rk, ro + kcb[i], kl + i * 1024);
+          buf_lds16(rv, ro + vcb[i], vl + i * 1024);
         }
       }
     } else {
@@ -501,12 +520,13 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
       // lane l of instruction t lands in slot l % 8 of row 8 t + l / 8 (one
       // query per row slot, clamped to the last query)
       char *bl = blds + wave * 32 * 128;
+      const __amdgpu_buffer_rsrc_t rb = rsrc_of(bias_g + kt * BN);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int r = 8 * t + (lane >> 3);
         const int ri = min(i0 + wave * 32 + r, p.S - 1);
         const int c = (lane & 7) ^ ((r >> 1) & 7);
-        load_lds16(bias_g + (int64_t)ri * p.bias_si + kt * BN + 8 * c, bl + t * 1024);
+        buf_lds16(rb, (uint32_t)(((int64_t)ri * p.bias_si + 8 * c) * (int64_t)sizeof(T)), bl + t * 1024);
       }
     }
   };
@@ -942,8 +962,8 @@ hipError_t launch_flash(const Params &p, int dtype, hipStream_t st) {
     const float mant = frexpf(p.scale, &ex);
     pl.qs = (p.bias && !p.mask && !(p.softcap > 0.f) && mant == 0.5f && ex >= -7 && ex <= 1) ? 1 : 0;
     // at head size 64 the bias rows go through LDS, which takes one query per
-    // row slot (GH = 1)
-    if (p.D == 64 && pl.GH != 1) pl.qs = 0;
+    // row slot (GH = 1), with 32-bit byte offsets inside one (b, head) slab
+    if (p.D == 64 && (pl.GH != 1 || (int64_t)p.S * p.bias_si * 2 >= (int64_t)1 << 31)) pl.qs = 0;
   }
   if (dtype == DT_BF16)
     return p.D == 64 ? launch_td<bf16, 64>(p, pl, st) : launch_td<bf16, 128>(p, pl, st);
