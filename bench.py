@@ -53,6 +53,9 @@ def parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--backward-only", action="store_true",
                     help="time only the GroupQueryAttention backward line (for profiling)")
+    ap.add_argument("--settle-seconds", type=float, default=0.4,
+                    help="after the timed steps, launch for this long and time the steps again "
+                         "at the settled clock (reported as `steady`; 0: skip)")
     ap.add_argument("--rotate-buffers", type=int, default=4,
                     help="input/output sets cycled for the cache-cold prefill figures "
                          "(0: skip them)")
@@ -157,6 +160,22 @@ def time_launches(call, steps: int, warmup: int):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return e0.elapsed_time(e1) / steps, wall
+
+
+def time_steady(call, steps: int, settle_s: float):
+    """Step time once the shader clock has settled: launches back to back for
+    at least settle_s seconds of wall time (the clock rises over the first
+    ~30 ms of sustained work after an idle spell), then `steps` timed launches.
+    Returns (ms per step, seconds spent settling)."""
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < settle_s:
+        for _ in range(20):
+            call.launch()
+        torch.cuda.synchronize()
+    settled = time.perf_counter() - t0
+    ms, _ = time_launches(call, steps, 0)
+    return ms, settled
 
 
 def _profile_record(path: str, workload: str, kernel: str):
@@ -283,7 +302,7 @@ def time_rotating(p, dev, inputs, sets: int, steps: int, warmup: int, decode: bo
     return ms
 
 
-def run_workload(name, steps, warmup, with_cpu, cpu_s, is_headline, rotate=0):
+def run_workload(name, steps, warmup, with_cpu, cpu_s, is_headline, rotate=0, settle_s=0.0):
     import torch
     from transformer_attention_fwd_amd import olk
     from transformer_attention_fwd_amd.workloads import workload
@@ -307,6 +326,7 @@ def run_workload(name, steps, warmup, with_cpu, cpu_s, is_headline, rotate=0):
     ms, wall = time_launches(call, steps, warmup)
     res["ms_per_step"] = ms
     res["wall_s"] = wall
+    steady = time_steady(call, max(steps, 50), settle_s) if settle_s > 0 else None
     dom = DOMINANT.get(res["kernel"])
     if decode:
         by = decode_bytes(p, inputs, inplace=True)
@@ -316,6 +336,11 @@ def run_workload(name, steps, warmup, with_cpu, cpu_s, is_headline, rotate=0):
         res["bytes_per_step"] = by
         if dom:
             res["roofline"] = roofline(name, p, res, by, "hbm", dom[0], dom[1])
+        if steady:
+            v = by / (steady[0] * 1e-3) / 1e9
+            res["steady"] = {"settle_s": round(steady[1], 3), "steps": max(steps, 50),
+                             "ms_per_step": round(steady[0], 5), "value": round(v, 3),
+                             "frac_of_peak": round(v / HBM_PEAK_GBS, 5)}
     else:
         fl = flops(p, inputs)
         res["value"] = fl / (ms * 1e-3) / 1e12
@@ -329,6 +354,11 @@ def run_workload(name, steps, warmup, with_cpu, cpu_s, is_headline, rotate=0):
             # With present written by the prefill kernel itself the step is one
             # launch of it, so the HIP-event step time is its launch duration.
             res["roofline"] = roofline(name, p, res, fl, "mfma", dom[0], dom[1])
+        if steady:
+            v = fl / (steady[0] * 1e-3) / 1e12
+            res["steady"] = {"settle_s": round(steady[1], 3), "steps": max(steps, 50),
+                             "ms_per_step": round(steady[0], 5), "value": round(v, 3),
+                             "frac_of_peak": round(v / MFMA_PEAK_TFLOPS[p.dtype], 5)}
         if rotate > 1:
             cold = time_rotating(p, dev, inputs, rotate, steps, warmup, decode)
             res["cold"] = {"sets": rotate, "ms_per_step": round(cold, 5),
@@ -379,7 +409,7 @@ def main():
         return
     t_start = time.perf_counter()
     p, head = run_workload(args.workload, args.steps, args.warmup, not args.no_cpu,
-                           args.cpu_seconds, True, args.rotate_buffers)
+                           args.cpu_seconds, True, args.rotate_buffers, args.settle_seconds)
     print(f"[bench] {args.workload}: {head['value']:.1f} {head['unit']} "
           f"({head['ms_per_step']:.3f} ms/step) err={head['max_abs_err_sampled']:.2e}",
           file=sys.stderr, flush=True)
@@ -391,12 +421,12 @@ def main():
                 continue
             rot = args.rotate_buffers if name in ROTATED else 0
             _, r = run_workload(name, max(10, args.steps // 2), max(3, args.warmup // 2), False,
-                                0, False, rot)
+                                0, False, rot, args.settle_seconds)
             print(f"[bench] {name}: {r['value']:.1f} {r['unit']} ({r['ms_per_step']:.4f} ms) "
                   f"err={r['max_abs_err_sampled']:.2e}", file=sys.stderr, flush=True)
             secondary[name] = {k: r[k] for k in ("value", "unit", "frac_of_peak", "ms_per_step",
                                                  "kernel", "max_abs_err_sampled", "roofline",
-                                                 "hbm_frac", "cold") if k in r}
+                                                 "hbm_frac", "cold", "steady") if k in r}
     if not args.no_secondary:
         r = run_backward(max(3, args.steps // 10), 1)
         print(f"[bench] gqa_backward_bf16: {r['value']:.1f} {r['unit']} ({r['ms_per_step']:.3f} ms)",
@@ -425,6 +455,7 @@ def main():
         "roofline": head.get("roofline"),
         "hbm_frac": head.get("hbm_frac"),
         "cold": head.get("cold"),
+        "steady": head.get("steady"),
         "cpu_baseline": head.get("cpu_baseline"),
         "secondary": secondary,
         "bench_wall_s": round(time.perf_counter() - t_start, 1),
