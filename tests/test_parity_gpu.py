@@ -186,6 +186,27 @@ SMALL = {
     "mha_self_projbias_bf16": Problem(op="mha", dtype="bf16", B=2, S=100, L=100, Hq=4, Hkv=4,
                                       D=128, Dv=128, kv_rank=3, causal=0, has_lens=False,
                                       has_proj_bias=True, sigma_proj=0.3, bias_bh=(2, 1)),
+    # decode-sized calls (at most 16 rows per KV head) through the decode
+    # kernel's general score pipeline: a short BOOL mask over a cache, bias +
+    # softcap with nonpad lengths at head size 64, a MultiHeadAttention int32
+    # binary mask with projection bias and a past, softcap + sink + window
+    "attention_decode_boolmask_bf16": Problem(op="attention", dtype="bf16", B=3, S=1, L=1,
+                                              P=300, Hq=8, Hkv=2, D=128, Dv=128, causal=0,
+                                              has_lens=False, mask_kind="bool",
+                                              mask_bhs=(3, 1, 1), mask_cols=250),
+    "attention_decode_bias_softcap_f16": Problem(op="attention", dtype="f16", B=2, S=2, L=2,
+                                                 P=200, Hq=8, Hkv=2, D=64, Dv=64, causal=1,
+                                                 has_lens=True, lens_range=(100, 202),
+                                                 bias_bh=(2, 8), softcap=5.0),
+    "mha_decode_binary_mask_projbias_f16": Problem(op="mha", dtype="f16", B=2, S=3, L=3, P=120,
+                                                   Hq=4, Hkv=4, D=128, Dv=128, kv_rank=3,
+                                                   causal=1, has_lens=False, mask_kind="int32",
+                                                   mask_bhs=(2, 1, 1), mask_p=0.5,
+                                                   mask_filter_value=-3.0, has_proj_bias=True,
+                                                   sigma_proj=0.3),
+    "gqa_decode_softcap_sink_bf16": Problem(op="gqa", dtype="bf16", B=3, S=1, L=1, P=500, Hq=16,
+                                            Hkv=2, D=128, Dv=128, causal=1, window=200,
+                                            softcap=30.0, has_sink=True, lens_range=(1, 500)),
 }
 
 
@@ -197,11 +218,12 @@ def _run(p, dev, **kw):
 
 
 def tiled_capable(p, mode="fwd"):
-    # attn_mask (BOOL and binary) runs in the prefill kernel, not in the
+    # attn_mask (BOOL and binary) runs in the prefill kernel and, for calls of
+    # at most 16 rows per KV head, in the decode kernel, not in the tiled
     # split-KV partials; the qk output goes to the generic kernels
     if p.qk_mode is not None:
         return False
-    if p.mask_kind and mode == "decode":
+    if p.mask_kind and mode == "decode" and (p.Hq // p.Hkv) * p.S > 16:
         return False
     return p.dtype in ("f16", "bf16") and p.D == p.Dv and p.D in (64, 128)
 
@@ -221,6 +243,10 @@ def test_small_parity(name, mode, kernel):
     name_ran = olk.olk_last_kernel_name()
     if kernel != "generic" and tiled_capable(p, mode):
         assert "generic" not in name_ran, name_ran
+        if mode == "decode" and (p.Hq // p.Hkv) * p.S <= 16 and (p.scale is None or p.scale > 0):
+            # up to 16 rows per KV head: the decode kernel, bias / softcap /
+            # masks through its general score pipeline
+            assert name_ran == "olk_decode_split+combine", name_ran
     want = olk_ref.attention(p, inp)
     assert_close(p, y_logical(p, c.y), want)
     assert_present_exact(p, inp, c.present_k, c.present_v)

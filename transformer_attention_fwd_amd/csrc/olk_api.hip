@@ -450,14 +450,20 @@ olk_status olk_attention_decode(const olk_attn_desc *desc, const olk_attn_io *io
   hipStream_t s = (hipStream_t)stream;
   olk::Params pa = p;
   if (desc->do_rotary) { pa.q = pa.y; pa.q_sb = pa.y_sb; pa.q_ss = pa.y_ss; pa.q_sh = pa.y_sh; }
-  // the split-KV partial kernels take no attn_mask: masks go to the generic split
-  const bool tiled_ok = olk::tiled_supports(pa, desc->dtype) && !pa.mask;
-  if (desc->kernel == OLK_KERNEL_TILED && !tiled_ok) return OLK_E_UNSUPPORTED;
+  // Matrix-core paths: the decode kernel (up to 16 rows per KV head; its key
+  // source is the past buffer, or present once the new rows are appended
+  // there), else the tiled split partials, which take no attn_mask.
+  const bool tiled_ok = olk::tiled_supports(pa, desc->dtype);
+  olk::Params pchk = p;
+  if (pchk.present_k && pchk.present_v) pchk.keys_in_past = 1;
+  const bool decode_ok = tiled_ok && olk::decode_supports(pchk, desc->dtype);
+  const bool split_ok = tiled_ok && !pa.mask;
+  if (desc->kernel == OLK_KERNEL_TILED && !decode_ok && !split_ok) return OLK_E_UNSUPPORTED;
   // In place at head size 128 the decode kernel appends the new rows itself
   // (no separate copy launch); every other case appends before the split kernels.
   bool append_in_decode = false;
   if (!desc->do_rotary && !kv_bias_path(desc, io) && desc->kernel != OLK_KERNEL_GENERIC &&
-      tiled_ok && p.kv_inplace) {
+      decode_ok && p.kv_inplace) {
     olk::Params pk = p;
     pk.keys_in_past = 1;
     append_in_decode = olk::decode_appends(pk, desc->dtype);
@@ -478,13 +484,13 @@ olk_status olk_attention_decode(const olk_attn_desc *desc, const olk_attn_io *io
   }
   const int n_split = n_splits(desc);
   int n_comb = n_split, comb_keys = kSplitKeys;
-  if (desc->kernel != OLK_KERNEL_GENERIC && tiled_ok && olk::decode_supports(p, desc->dtype)) {
+  if (desc->kernel != OLK_KERNEL_GENERIC && decode_ok && olk::decode_supports(p, desc->dtype)) {
     n_comb = n_splits(desc, kDecodeSplitKeys);
     comb_keys = kDecodeSplitKeys;
     e = olk::launch_decode(p, desc->dtype, kDecodeSplitKeys, n_comb, (float *)workspace,
                            append_in_decode, s);
     g_last_kernel = "olk_decode_split+combine";
-  } else if (desc->kernel != OLK_KERNEL_GENERIC && tiled_ok) {
+  } else if (desc->kernel != OLK_KERNEL_GENERIC && split_ok) {
     e = olk::launch_tiled_split(p, desc->dtype, kSplitKeys / 64, (float *)workspace, s);
     g_last_kernel = "olk_tiled_split+combine";
   } else {

@@ -29,6 +29,12 @@
 //   and never transposed.
 // * The K and V of the next two steps are in flight while a step computes;
 //   the stream is read once, with non-temporal loads.
+// * Scores with an additive bias, softcap or attn_mask (EPI instantiations)
+//   take the general score pipeline per key, in the order of the contracts:
+//   (Q K^T) * scale, + bias, softcap, + mask_filter_value at MultiHeadAttention
+//   padded keys and at zeros of its int32 binary mask; a false BOOL element
+//   excludes the key.  The MultiHeadAttention Q projection bias is added as Q
+//   loads (the K/V segments go through a pre-pass into present).
 // * The 4 wavefronts merge (m, l, O) through LDS and write one partial record
 //   [m (natural log), l, -, -, O[Dv]] per (row, split); the combine kernel
 //   merges the splits and adds the sink.
@@ -120,8 +126,40 @@ struct DPlan {
   int append;      // in-place cache: the kernel writes the new rows itself
 };
 
+// Score of row (row_q, row_h) and key j in the log2 domain through the
+// general pipeline (onnx-light reference kernels header page, "class
+// Attention": scale, + bias, softcap; Python API "Custom operators",
+// "Microsoft MultiHeadAttention": mask_filter_value added at padded keys and
+// at zeros of the int32 binary mask); a false BOOL mask element clears ok.
+// Called only for keys inside the row's range (below the bias / BOOL-mask
+// columns).  cap_in = 2 log2(e) / softcap: c tanh(x / c) = c - 2c / (2^(x cap_in) + 1).
+template <typename T>
+__device__ __forceinline__ float score_general(const Params &p, const Seq &s, float dot, int b,
+                                               int row_q, int row_h, int j, float cap_in,
+                                               bool &ok) {
+  float sc = dot * p.scale;
+  if (p.bias)
+    sc += (float)((const T *)p.bias)[b * p.bias_sb + row_h * p.bias_sh + (int64_t)row_q * p.bias_si + j];
+  if (p.softcap > 0.f)
+    sc = p.softcap - 2.0f * p.softcap * __builtin_amdgcn_rcpf(ex2(sc * cap_in) + 1.0f);
+  if (p.pad_add && j >= s.pad) sc += p.mfv;
+  if (p.mask_kind == 2 && !mask_at(p, b, row_h, row_q, j)) sc += p.mfv;
+  if (p.mask_kind == 1 && !mask_at(p, b, row_h, row_q, j)) ok = false;
+  return sc * kLog2e;
+}
+
+// Q row chunk (8 elements) plus the MultiHeadAttention Q projection bias,
+// each sum rounded once to the element type.
+template <typename T, typename V>
+__device__ __forceinline__ V add_qbias(uint4 raw, const T *pb) {
+  V v = __builtin_bit_cast(V, raw);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (T)((float)v[e] + (float)pb[e]);
+  return v;
+}
+
 // NR: row slots (G * S) rounded up to a power of two <= 16.
-template <typename T, int D, int NR>
+template <typename T, int D, int NR, bool EPI>
 __global__ __launch_bounds__(kThreads) void decode_kernel(Params p, DPlan pl) {
   typedef typename DV<T>::v8 vec8;
   constexpr int NKS = D / 32;  // k-steps of QK^T (32 dims each)
@@ -141,6 +179,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p, DPlan pl) {
   const int pos_min = s.qoff, pos_max = s.qoff + p.S - 1;
   int hi = p.pad_add ? s.total : s.valid;
   if (p.causal) hi = min(hi, pos_max + 1);
+  // a short bias or BOOL mask excludes the keys beyond its columns
+  if (EPI && p.bias) hi = min(hi, p.bias_cols);
+  if (EPI && p.mask_kind == 1) hi = min(hi, p.mask_cols);
   int lo = p.window > 0 ? max(0, pos_min - p.window + 1) : 0;
   const int sp_lo = max(lo, split * pl.split_keys);
   const int sp_hi = min(hi, (split + 1) * pl.split_keys);
@@ -163,7 +204,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p, DPlan pl) {
     for (int ks = 0; ks < NKS; ++ks) {
       uint4 raw = make_uint4(0, 0, 0, 0);
       if (col_ok) raw = *(const uint4 *)(qr + ks * 32 + kq * 8);
-      qreg[ks] = __builtin_bit_cast(vec8, raw);
+      qreg[ks] = (p.proj_bias && col_ok)
+                     ? add_qbias<T, vec8>(raw, (const T *)p.proj_bias + row_h * D + ks * 32 + kq * 8)
+                     : __builtin_bit_cast(vec8, raw);
     }
   }
   // Q is in registers from here on: wait for its loads on every path, so the
@@ -233,6 +276,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p, DPlan pl) {
 #pragma unroll
     for (int e = 0; e < DPL; ++e) o[r][e] = 0.f;
   const float sl = p.scale * kLog2e;
+  const float cap_in = p.softcap > 0.f ? 2.0f * kLog2e / p.softcap : 0.f;
 
   const int my_steps = n_steps > wave ? (n_steps - wave + 3) / 4 : 0;
   // Three register buffers rotate so the loads of step it + 2 are in flight
@@ -253,11 +297,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p, DPlan pl) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int j = j0 + 4 * kq + r;
-      float t = sacc[r] * sl;
       bool ok = j >= sp_lo && j < sp_hi;
       if (p.causal && j > col_pos) ok = false;
       if (p.window > 0 && j < col_pos - p.window + 1) ok = false;
-      if (p.pad_add && j >= s.pad) t += p.mfv * kLog2e;
+      float t;
+      if constexpr (EPI) {
+        t = (ok && col_ok) ? score_general<T>(p, s, sacc[r], b, row_q, row_h, j, cap_in, ok) : 0.f;
+      } else {
+        t = sacc[r] * sl;
+        if (p.pad_add && j >= s.pad) t += p.mfv * kLog2e;
+      }
       t4[r] = ok ? t : kNegInf;
       mx = fmaxf(mx, t4[r]);
     }
@@ -392,7 +441,7 @@ template <typename T> __device__ __forceinline__ uint32_t pack2p(float a, float 
   return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
 
-template <typename T, int NR>
+template <typename T, int NR, bool EPI>
 __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p, DPlan pl) {
   constexpr int D = 128;
   typedef typename DV<T>::v8 vec8;
@@ -440,6 +489,9 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p, DPlan p
   const int pos_min = s.qoff, pos_max = s.qoff + p.S - 1;
   int hi = p.pad_add ? s.total : s.valid;
   if (p.causal) hi = min(hi, pos_max + 1);
+  // a short bias or BOOL mask excludes the keys beyond its columns
+  if (EPI && p.bias) hi = min(hi, p.bias_cols);
+  if (EPI && p.mask_kind == 1) hi = min(hi, p.mask_cols);
   int lo = p.window > 0 ? max(0, pos_min - p.window + 1) : 0;
   const int sp_lo = max(lo, split * pl.split_keys);
   const int sp_hi = min(hi, (split + 1) * pl.split_keys);
@@ -462,7 +514,9 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p, DPlan p
     for (int ks = 0; ks < NKS; ++ks) {
       uint4 raw = make_uint4(0, 0, 0, 0);
       if (col_ok) raw = *(const uint4 *)(qr + ks * 32 + kq * 8);
-      qreg[ks] = __builtin_bit_cast(vec8, raw);
+      qreg[ks] = (p.proj_bias && col_ok)
+                     ? add_qbias<T, vec8>(raw, (const T *)p.proj_bias + row_h * D + ks * 32 + kq * 8)
+                     : __builtin_bit_cast(vec8, raw);
     }
   }
 
@@ -507,6 +561,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p, DPlan p
 #pragma unroll
   for (int blk = 0; blk < NBLK; ++blk) o[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float sl = p.scale * kLog2e;
+  const float cap_in = p.softcap > 0.f ? 2.0f * kLog2e / p.softcap : 0.f;
 
   uint4 k0[NKS], k1[NKS], k2[NKS];
   uint4 v0[kStep / 4], v1[kStep / 4], v2[kStep / 4];
@@ -539,11 +594,16 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p, DPlan p
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int j = j0 + 4 * kq + r;
-      float t = sacc[r] * sl;
       bool ok = j >= sp_lo && j < sp_hi;
       if (p.causal && j > col_pos) ok = false;
       if (p.window > 0 && j < col_pos - p.window + 1) ok = false;
-      if (p.pad_add && j >= s.pad) t += p.mfv * kLog2e;
+      float t;
+      if constexpr (EPI) {
+        t = (ok && col_ok) ? score_general<T>(p, s, sacc[r], b, row_q, row_h, j, cap_in, ok) : 0.f;
+      } else {
+        t = sacc[r] * sl;
+        if (p.pad_add && j >= s.pad) t += p.mfv * kLog2e;
+      }
       t4[r] = ok ? t : kNegInf;
       mx = fmaxf(mx, t4[r]);
     }
@@ -648,18 +708,25 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p, DPlan p
   }
 }
 
-template <typename T, int D>
-hipError_t launch_nr(const Params &p, const DPlan &pl, int nr, dim3 grid, hipStream_t st) {
+template <typename T, int D, bool EPI>
+void launch_nr_epi(const Params &p, const DPlan &pl, int nr, dim3 grid, hipStream_t st) {
   if constexpr (D == 128) {
     // head size 128: PV on the matrix cores
-    if (nr <= 4) hipLaunchKernelGGL((decode_mfma_kernel<T, 4>), grid, dim3(kThreads), 0, st, p, pl);
-    else if (nr <= 8) hipLaunchKernelGGL((decode_mfma_kernel<T, 8>), grid, dim3(kThreads), 0, st, p, pl);
-    else hipLaunchKernelGGL((decode_mfma_kernel<T, 16>), grid, dim3(kThreads), 0, st, p, pl);
+    if (nr <= 4) hipLaunchKernelGGL((decode_mfma_kernel<T, 4, EPI>), grid, dim3(kThreads), 0, st, p, pl);
+    else if (nr <= 8) hipLaunchKernelGGL((decode_mfma_kernel<T, 8, EPI>), grid, dim3(kThreads), 0, st, p, pl);
+    else hipLaunchKernelGGL((decode_mfma_kernel<T, 16, EPI>), grid, dim3(kThreads), 0, st, p, pl);
   } else {
-    if (nr <= 4) hipLaunchKernelGGL((decode_kernel<T, D, 4>), grid, dim3(kThreads), 0, st, p, pl);
-    else if (nr <= 8) hipLaunchKernelGGL((decode_kernel<T, D, 8>), grid, dim3(kThreads), 0, st, p, pl);
-    else hipLaunchKernelGGL((decode_kernel<T, D, 16>), grid, dim3(kThreads), 0, st, p, pl);
+    if (nr <= 4) hipLaunchKernelGGL((decode_kernel<T, D, 4, EPI>), grid, dim3(kThreads), 0, st, p, pl);
+    else if (nr <= 8) hipLaunchKernelGGL((decode_kernel<T, D, 8, EPI>), grid, dim3(kThreads), 0, st, p, pl);
+    else hipLaunchKernelGGL((decode_kernel<T, D, 16, EPI>), grid, dim3(kThreads), 0, st, p, pl);
   }
+}
+
+template <typename T, int D>
+hipError_t launch_nr(const Params &p, const DPlan &pl, int nr, dim3 grid, hipStream_t st) {
+  // bias, softcap or attn_mask: the general score pipeline
+  if (p.bias || p.mask || p.softcap > 0.f) launch_nr_epi<T, D, true>(p, pl, nr, grid, st);
+  else launch_nr_epi<T, D, false>(p, pl, nr, grid, st);
   return hipGetLastError();
 }
 
@@ -669,8 +736,7 @@ hipError_t launch_nr(const Params &p, const DPlan &pl, int nr, dim3 grid, hipStr
 // at head size 128 it reads every key from the past buffer (keys_in_past).
 bool decode_supports(const Params &p, int dtype) {
   return (dtype == DT_F16 || dtype == DT_BF16) && p.D == p.Dv && (p.D == 64 || p.D == 128) &&
-         p.G * p.S <= 16 && !p.bias && !p.mask && !(p.softcap > 0.f) && p.scale > 0.f &&
-         !p.proj_bias && !p.qk_out && (p.D == 64 || p.keys_in_past);
+         p.G * p.S <= 16 && p.scale > 0.f && !p.qk_out && (p.D == 64 || p.keys_in_past);
 }
 
 // Head size 128 in place (present is the past buffer, every key read from
