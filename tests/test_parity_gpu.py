@@ -466,14 +466,37 @@ def test_qk_matmul_output(mode, dtype):
     p = Problem(op="attention", dtype=dtype, B=2, S=24, L=40, P=9, Hq=4, Hkv=2, D=64, Dv=64,
                 causal=1, has_lens=True, lens_range=(20, 49), mask_kind="bool",
                 mask_bhs=(2, 1, 24), bias_bh=(1, 4), softcap=4.0, qk_mode=mode)
-    inp = make_inputs(p, 700 + mode)
-    _say(f"[parity] qk mode={mode} dtype={dtype}")
-    for run in ("fwd", "decode"):
-        c = _run(p, to_dev(inp), mode=run)
+    _check_qk(p, 700 + mode, ("fwd", "decode"))
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2, 3])
+def test_qk_matmul_output_tiles_d128(mode):
+    # head size 128, several key tiles with T a multiple of 4 (16-byte rows)
+    # and more than one 128-row query tile, through the matrix-core qk kernel
+    # and the generic one
+    p = Problem(op="attention", dtype="f16", B=2, S=150, L=130, P=30, Hq=4, Hkv=2, D=128,
+                Dv=128, causal=1, has_lens=True, lens_range=(100, 160), mask_kind="bool",
+                mask_bhs=(2, 4, 150), bias_bh=(2, 1), softcap=6.0, qk_mode=mode)
+    _check_qk(p, 720 + mode, ("fwd", "decode", "fwd-generic"))
+
+
+def _check_qk(p, seed, runs):
+    inp = make_inputs(p, seed)
+    for run in runs:
+        mode_ = "decode" if run == "decode" else "fwd"
+        kernel = "generic" if run.endswith("generic") else "auto"
+        _say(f"[parity] qk mode={p.qk_mode} dtype={p.dtype} D={p.D} {run}")
+        c = _run(p, to_dev(inp), mode=mode_, kernel=kernel)
+        name = olk.olk_last_kernel_name()
+        if p.dtype in ("f16", "bf16") and p.D in (64, 128) and kernel != "generic":
+            assert name.endswith("+olk_qk_mfma"), name
+        else:
+            assert name.endswith("+olk_qk"), name
+        mode = p.qk_mode
         got = c.qk.detach().cpu().double().numpy()
         want = olk_ref.qk(p, inp, mode)
         fin = np.isfinite(want)
         assert np.array_equal(np.isfinite(got), fin)
-        tol = 1e-4 if mode == 3 else (2e-4 if dtype == "f32" else 2e-3)
+        tol = 1e-4 if mode == 3 else (2e-4 if p.dtype == "f32" else 2e-3)
         np.testing.assert_allclose(got[fin], want[fin], rtol=0, atol=tol)
         assert_close(p, y_logical(p, c.y), olk_ref.attention(p, inp))

@@ -7,6 +7,7 @@
 // uses one head count, rank-3 or rank-4 K/V, and rejects what it does not
 // model ("Microsoft MultiHeadAttention").  Nothing here reads device memory.
 #include <math.h>
+#include <stdio.h>
 #include <string.h>
 
 #include <mutex>
@@ -25,11 +26,25 @@ bool decode_supports(const Params &p, int dtype);
 bool decode_appends(const Params &p, int dtype);
 hipError_t launch_decode(const Params &p, int dtype, int split_keys, int n_split, float *ws,
                          bool append, hipStream_t st);
+bool qk_mfma_supports(const Params &p, int dtype);
+hipError_t launch_qk_mfma(const Params &p, int dtype, hipStream_t st);
 }  // namespace olk
 
 namespace {
 
 thread_local const char *g_last_kernel = "";
+thread_local char g_name_buf[96];
+
+// qk_matmul_output after the attention kernels: on the matrix cores where the
+// shapes allow (not with the generic kernel forced), else the VALU kernel; the
+// last-kernel name gains the qk kernel's.
+hipError_t launch_qk_output(const olk::Params &p, const olk_attn_desc *desc, hipStream_t s) {
+  const bool mf = desc->kernel != OLK_KERNEL_GENERIC && olk::qk_mfma_supports(p, desc->dtype);
+  const hipError_t e = mf ? olk::launch_qk_mfma(p, desc->dtype, s) : olk::launch_qk(p, desc->dtype, s);
+  snprintf(g_name_buf, sizeof(g_name_buf), "%s+%s", g_last_kernel, mf ? "olk_qk_mfma" : "olk_qk");
+  g_last_kernel = g_name_buf;
+  return e;
+}
 
 // Keys per split of the decode path (both kernel families; a multiple of the
 // tiled kernel's 64-key tile).
@@ -433,7 +448,7 @@ olk_status olk_attention_fwd(const olk_attn_desc *desc, const olk_attn_io *io, v
     e = olk::launch_generic(p, desc->dtype, s);
     g_last_kernel = desc->do_rotary ? "olk_rope+olk_generic_fwd" : "olk_generic_fwd";
   }
-  if (e == hipSuccess && p.qk_out) e = olk::launch_qk(p, desc->dtype, s);
+  if (e == hipSuccess && p.qk_out) e = launch_qk_output(p, desc, s);
   return e == hipSuccess ? OLK_OK : OLK_E_HIP;
 }
 
@@ -499,7 +514,7 @@ olk_status olk_attention_decode(const olk_attn_desc *desc, const olk_attn_io *io
   }
   if (e != hipSuccess) return OLK_E_HIP;
   e = olk::launch_combine(p, desc->dtype, n_comb, comb_keys, (const float *)workspace, s);
-  if (e == hipSuccess && p.qk_out) e = olk::launch_qk(p, desc->dtype, s);
+  if (e == hipSuccess && p.qk_out) e = launch_qk_output(p, desc, s);
   return e == hipSuccess ? OLK_OK : OLK_E_HIP;
 }
 

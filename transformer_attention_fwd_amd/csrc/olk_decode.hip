@@ -736,7 +736,7 @@ hipError_t launch_nr(const Params &p, const DPlan &pl, int nr, dim3 grid, hipStr
 // at head size 128 it reads every key from the past buffer (keys_in_past).
 bool decode_supports(const Params &p, int dtype) {
   return (dtype == DT_F16 || dtype == DT_BF16) && p.D == p.Dv && (p.D == 64 || p.D == 128) &&
-         p.G * p.S <= 16 && p.scale > 0.f && !p.qk_out && (p.D == 64 || p.keys_in_past);
+         p.G * p.S <= 16 && p.scale > 0.f && (p.D == 64 || p.keys_in_past);
 }
 
 // Head size 128 in place (present is the past buffer, every key read from

@@ -438,9 +438,8 @@ bool tiled_supports(const Params &p, int dtype) {
   if (dtype != DT_F16 && dtype != DT_BF16) return false;
   if (p.D != p.Dv || (p.D != 64 && p.D != 128)) return false;
   // attn_mask (BOOL, and MultiHeadAttention's int32 binary mask) runs in the
-  // prefill kernel's mask path (the split-KV entry keeps masks on the generic
-  // kernels); the qk output is served by the generic kernels
-  if (p.qk_out) return false;
+  // prefill kernel's mask path and the decode kernels (not in the tiled split
+  // partials); the qk output is a separate launch after the attention
   if (!aligned16(p.q) || !aligned16(p.k) || !aligned16(p.v) || !aligned16(p.y)) return false;
   if (p.P > 0 && (!aligned16(p.past_k) || !aligned16(p.past_v))) return false;
   if (p.proj_bias && !aligned16(p.proj_bias)) return false;
