@@ -62,6 +62,9 @@ __device__ void row_range(const Params &p, const Seq &s, int b, int h, int i, in
     if (j < j_hi) {
       const T *kr = kv_row<T>(p, s, b, g, j, false);
       float dot = 0.f;
+      // unrolled so that several of the row's loads are in flight at once
+      // (the sum keeps its order)
+#pragma unroll 8
       for (int c = 0; c < p.D; ++c) dot = fmaf(qs[c], to_f32(kr[c]), dot);
       sc = dot * p.scale;
       if (p.bias) {  // j < bias_cols: the caller's range stops there
@@ -91,7 +94,28 @@ __device__ void row_range(const Params &p, const Seq &s, int b, int h, int i, in
 #pragma unroll
     for (int k = 0; k < 4; ++k) st.o[k] *= alpha;
     const int nj = min(kWave, j_hi - j0);
-    for (int jj = 0; jj < nj; ++jj) {
+    // four keys at a time, their V loads issued together; a zero weight (a
+    // masked key) leaves the sums as they are, whatever its V row holds
+    int jj = 0;
+    for (; jj + 4 <= nj; jj += 4) {
+      float w[4], x[4][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        w[u] = ps[jj + u];
+        const T *vr = kv_row<T>(p, s, b, g, j0 + jj + u, true);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int d = lane + k * kWave;
+          x[u][k] = d < p.Dv ? to_f32(vr[d]) : 0.f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          st.o[k] = w[u] != 0.f ? fmaf(w[u], x[u][k], st.o[k]) : st.o[k];
+    }
+    for (; jj < nj; ++jj) {
       const float w = ps[jj];
       if (w == 0.f) continue;
       const T *vr = kv_row<T>(p, s, b, g, j0 + jj, true);
