@@ -147,6 +147,7 @@ __device__ __forceinline__ float sum_halves(float x) {
 
 struct FPlan {
   int GH, n_hg, QW, n_qt;
+  int ghs;           // log2 GH (GH is a power of two)
   int qs;            // Q pre-scaled, bias in the accumulator (see flash_fwd_kernel)
   int xcd_remap;
   int bias_vec;
@@ -228,8 +229,8 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
 
   // ---- this lane's row slot ----
   const int slot = wave * 32 + col;
-  const int row_i = i0 + slot / pl.GH;
-  const int row_h = g * p.G + hg * pl.GH + slot % pl.GH;
+  const int row_i = i0 + (slot >> pl.ghs);
+  const int row_h = g * p.G + hg * pl.GH + (slot & (pl.GH - 1));
   const bool row_ok = row_i < p.S;
   const int row_pos = s.qoff + row_i;
   // the keys this row slot may attend form one interval [a_lo, a_lo + a_w):
@@ -237,7 +238,7 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
   const int a_lo = p.window > 0 ? max(lo, row_pos - p.window + 1) : lo;
   const int a_hi = p.causal ? min(hi, row_pos + 1) : hi;
   const uint32_t a_w = a_hi > a_lo ? (uint32_t)(a_hi - a_lo) : 0u;
-  const bool wave_active = i0 + (wave * 32) / pl.GH < p.S;
+  const bool wave_active = i0 + ((wave * 32) >> pl.ghs) < p.S;
 
   // ---- Q^T operand (B of S^T = K Q^T): slot col, d = 16 ks + 8 half + e ----
   vec8 qreg[NKS];  // filled by load_q below, after the first tile's loads are issued
@@ -891,7 +892,7 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
     const int r = k * RPI + lane / CH, c = lane % CH;
     const uint4 v = *(const uint4 *)(ys + r * RB + 16 * (c ^ (r & (CH - 1))));
     const int sl = wave * 32 + r;
-    const int ri = i0 + sl / pl.GH, rh = g * p.G + hg * pl.GH + sl % pl.GH;
+    const int ri = i0 + (sl >> pl.ghs), rh = g * p.G + hg * pl.GH + (sl & (pl.GH - 1));
     if (ri < p.S) *(uint4 *)((T *)p.y + b * p.y_sb + (int64_t)ri * p.y_ss + rh * p.y_sh + c * 8) = v;
   }
 }
@@ -939,6 +940,7 @@ bool flash_fuses_present(const Params &p) {
 hipError_t launch_flash(const Params &p, int dtype, hipStream_t st) {
   FPlan pl;
   pl.GH = gh_for(p.G);
+  pl.ghs = __builtin_ctz((unsigned)pl.GH);
   pl.n_hg = p.G / pl.GH;
   pl.QW = kSlots / pl.GH;
   pl.n_qt = (p.S + pl.QW - 1) / pl.QW;
