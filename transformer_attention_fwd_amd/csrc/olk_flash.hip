@@ -783,10 +783,11 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
     // (the empty asm keeps the compiler from issuing the word loads after
     // the K/V loads below)
     asm volatile("" ::: "memory");
-    // the next tile's K/V; the last tile reloads the previous one into the
-    // buffers that hold it (unread meanwhile), so every tile issues the same
-    // loads and the wait for the words above can leave these in flight
-    issue_loads(more ? kt + 1 : max(kt - 1, kt0), kn, vn);
+    // the next tile's K/V; with bias or mask words the last tile reloads the
+    // previous one into the buffers that hold it (unread meanwhile), so every
+    // tile issues the same loads and the wait for the words below can leave
+    // these in flight
+    if (more || BIAS) issue_loads(more ? kt + 1 : max(kt - 1, kt0), kn, vn);
     if (more && BPRE) load_bias(kt + 1, bnext);
     if (BLDS && more && wave_active && bias_rows_whole(kt + 1)) load_bias_rows(kt + 1);
     if (wave_active) {
