@@ -769,13 +769,7 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
     MaskWords mwt;
     if (wave_active) {
       if constexpr (BLDS) {
-        if (bias_rows_whole(kt)) {
-          bias_from_lds();
-          // the reads are done before the next tile's rows overwrite them
-          __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
-        } else {
-          load_bias(kt, bcur);  // a tile past the bias columns: per key
-        }
+        if (!bias_rows_whole(kt)) load_bias(kt, bcur);  // a tile past the bias columns: per key
       } else if (!BPRE) {
         load_bias(kt, bwt);
       }
@@ -790,6 +784,11 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
     // these in flight
     if (more || BIAS) issue_loads(more ? kt + 1 : max(kt - 1, kt0), kn, vn);
     if (more && BPRE) load_bias(kt + 1, bnext);
+    if (BLDS && wave_active && bias_rows_whole(kt)) {
+      bias_from_lds();
+      // the reads are done before the next tile's rows overwrite them
+      __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
+    }
     if (BLDS && more && wave_active && bias_rows_whole(kt + 1)) load_bias_rows(kt + 1);
     if (wave_active) {
       const int j0 = kt * BN;
