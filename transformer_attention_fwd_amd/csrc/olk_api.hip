@@ -346,6 +346,9 @@ hipError_t rotary_prepass(olk::Params &p, int dtype, hipStream_t st, bool q_in_k
   hipError_t e = olk::launch_present(pp, dtype, st);
   if (e != hipSuccess) return e;
   p.rot_q = q_in_kernel ? 1 : 0;
+  // with Q rotated in the prefill kernel, that kernel also takes the new V
+  // rows from V and writes their present rows (the pre-pass writes only K)
+  p.rot_skip_v = q_in_kernel ? 1 : 0;
   e = olk::launch_rope(p, dtype, st);
   if (e != hipSuccess) return e;
   if (!q_in_kernel) {
@@ -356,7 +359,12 @@ hipError_t rotary_prepass(olk::Params &p, int dtype, hipStream_t st, bool q_in_k
   p.past_v = p.present_v;
   p.past_rows = p.T;
   p.keys_in_past = 1;
-  p.present_k = p.present_v = nullptr;
+  p.present_k = nullptr;
+  if (q_in_kernel) {
+    p.v_new_rows = 1;  // present_v stays set: the new V rows are written there
+  } else {
+    p.present_v = nullptr;
+  }
   return hipSuccess;
 }
 

@@ -376,7 +376,22 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
     char *kl = (char *)kdst + wave * NLD * 1024;
     char *vl = (char *)vdst + wave * NLD * 1024;
     const bool full = j0 >= lo && j0 + BN <= hi;
-    if (full && (j0 >= s.src || j0 + BN <= s.src)) {
+    if (full && s.vsrc != s.src && (j0 >= s.src || j0 + BN <= s.src) &&
+        (j0 >= s.vsrc || j0 + BN <= s.vsrc)) {
+      // K and V from different sources (V of the new keys still in V, every
+      // K row in the past buffer): each tile from one source per matrix
+      const bool kn = j0 >= s.src, vn = j0 >= s.vsrc;
+      const __amdgpu_buffer_rsrc_t rk =
+          rsrc_of(kn ? knew + (int64_t)(j0 - s.src) * p.k_ss : kpast + (int64_t)j0 * D);
+      const __amdgpu_buffer_rsrc_t rv =
+          rsrc_of(vn ? vnew + (int64_t)(j0 - s.vsrc) * p.v_ss : vpast + (int64_t)j0 * D);
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        const uint32_t ro = (uint32_t)lrow[i] * (uint32_t)(D * sizeof(T));
+        buf_lds16(rk, kn ? kon[i] : ro + kcb[i], kl + i * 1024);
+        buf_lds16(rv, vn ? von[i] : ro + vcb[i], vl + i * 1024);
+      }
+    } else if (full && s.vsrc == s.src && (j0 >= s.src || j0 + BN <= s.src)) {
       // the whole tile from one source: a descriptor based at the tile's
       // first row plus the fixed 32-bit lane offsets of that source
       if (j0 >= s.src) {
@@ -402,22 +417,25 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
       for (int i = 0; i < NLD; ++i) {
         const int j = j0 + lrow[i];
         const int jj = j < lo ? lo : (j >= hi ? hi - 1 : j);
-        const bool nw = jj >= s.src;
+        const bool nw = jj >= s.src, nwv = jj >= s.vsrc;
         const char *kr = (const char *)(nw ? knew + (int64_t)(jj - s.src) * p.k_ss : kpast + (int64_t)jj * D);
-        const char *vr = (const char *)(nw ? vnew + (int64_t)(jj - s.src) * p.v_ss : vpast + (int64_t)jj * D);
+        const char *vr = (const char *)(nwv ? vnew + (int64_t)(jj - s.vsrc) * p.v_ss : vpast + (int64_t)jj * D);
         load_lds16(kr + kcb[i], kl + i * 1024);
         load_lds16(vr + vcb[i], vl + i * 1024);
       }
     }
   };
-  // present rows of the owned keys of tile kt (resident in kbuf / vbuf)
+  // present rows of the owned keys of tile kt (resident in kbuf / vbuf);
+  // only V when K is already there (the rotary pre-pass wrote the rotated K)
+  const bool pres_k_on = p.present_k != nullptr;
   auto copy_owned = [&](int kt, const T *kbuf, const T *vbuf) __attribute__((always_inline)) {
     const int j0 = kt * BN;
     const int a = max(own_lo, j0), e = min(own_hi, j0 + BN);
     for (int t = tid; t < (e - a) * CH; t += kThreads) {
       const int j = a + t / CH, cc = t % CH, r = j - j0;
-      *(uint4 *)((char *)pres_k + ((uint32_t)j * D + cc * 8u) * sizeof(T)) =
-          *(const uint4 *)((const char *)kbuf + r * RB + 16 * (cc ^ fk(r)));
+      if (pres_k_on)
+        *(uint4 *)((char *)pres_k + ((uint32_t)j * D + cc * 8u) * sizeof(T)) =
+            *(const uint4 *)((const char *)kbuf + r * RB + 16 * (cc ^ fk(r)));
       *(uint4 *)((char *)pres_v + ((uint32_t)j * D + cc * 8u) * sizeof(T)) =
           *(const uint4 *)((const char *)vbuf + r * RB + 16 * (cc ^ fv(r)));
     }
@@ -933,9 +951,10 @@ bool flash_rotates_q(const Params &p) {
   return p.rot_dim == p.D && (p.rot_dim / 2) % 8 == 0;
 }
 
-// Whether the prefill kernel writes the present rows of the new keys itself.
+// Whether the prefill kernel writes the present rows of the new keys itself
+// (K and V, or V alone when the rotary pre-pass has written the rotated K).
 bool flash_fuses_present(const Params &p) {
-  return p.op == OP_GQA && p.present_k != nullptr && p.present_v != nullptr;
+  return p.op == OP_GQA && p.present_v != nullptr && (p.present_k != nullptr || p.v_new_rows);
 }
 
 hipError_t launch_flash(const Params &p, int dtype, hipStream_t st) {

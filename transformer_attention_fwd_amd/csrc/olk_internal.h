@@ -49,6 +49,9 @@ struct Params {
   const void *cos_cache, *sin_cache;
   int rot_dim, rot_inter, rot_max;
   int rot_q;  // the prefill kernel rotates Q as it loads it (the pre-pass skips Q)
+  int rot_skip_v;  // the pre-pass leaves V alone (the prefill kernel copies the new V rows)
+  int v_new_rows;  // with keys_in_past: V rows of the new keys still come from the new V
+                   // (keys j >= past_b), only K is read from the past buffer throughout
 };
 
 // Per-batch sequence bookkeeping (integer; read once per workgroup).
@@ -59,6 +62,7 @@ struct Seq {
   int pad;    // keys j >= pad get mfv added (MultiHeadAttention, additive mode)
   int qoff;   // absolute position of query 0: the number of cached keys before the new ones
   int src;    // keys j < src are read from the past buffer, the rest from the new K/V
+  int vsrc;   // the same boundary for V (differs from src only with v_new_rows)
 };
 
 __device__ __forceinline__ Seq seq_info(const Params &p, int b) {
@@ -92,6 +96,7 @@ __device__ __forceinline__ Seq seq_info(const Params &p, int b) {
     }
   }
   s.src = p.keys_in_past ? s.total : s.past;
+  s.vsrc = (p.keys_in_past && !p.v_new_rows) ? s.total : s.past;
   return s;
 }
 

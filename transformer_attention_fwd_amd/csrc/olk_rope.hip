@@ -12,7 +12,9 @@
 //     by a later kernel.  With rot_q the prefill kernel rotates Q itself as
 //     it loads it, with the same arithmetic, and this pass skips Q;
 //   * the Hkv new key heads are rotated into present_k[b, g, past_b + i];
-//   * the new value heads are copied (bits) into present_v[b, g, past_b + i].
+//   * the new value heads are copied (bits) into present_v[b, g, past_b + i],
+//     unless rot_skip_v: then the prefill kernel reads them from V and
+//     writes those present rows itself.
 // The attention kernels then take every key from present.
 //
 // A pair (x1, x2) with cosine c and sine s becomes (x1*c - x2*s, x2*c + x1*s),
@@ -149,7 +151,7 @@ __global__ __launch_bounds__(kThreads) void rope_vec_kernel(Params p) {
   if (j >= p.T) return;
   const int pos = j < p.rot_max ? j : p.rot_max - 1;
   const int nt = vec_tasks<T>(p), vt = p.Dv / 8;
-  const int nq = p.rot_q ? 0 : p.Hq * nt, nk = p.Hkv * nt, nv = p.Hkv * vt;
+  const int nq = p.rot_q ? 0 : p.Hq * nt, nk = p.Hkv * nt, nv = p.rot_skip_v ? 0 : p.Hkv * vt;
   const T *qrow = (const T *)p.q + b * p.q_sb + (int64_t)i * p.q_ss;
   T *yrow = (T *)p.y + b * p.y_sb + (int64_t)i * p.y_ss;
   for (int t = threadIdx.x; t < nq + nk + nv; t += kThreads) {
@@ -181,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void rope_vec2_kernel(Params p) {
   const int b = blockIdx.y;
   const Seq s = seq_info(p, b);
   const int nt = vec_tasks<T>(p), vt = p.Dv / 8;
-  const int nq = p.rot_q ? 0 : p.Hq * nt, nk = p.Hkv * nt, nv = p.Hkv * vt;
+  const int nq = p.rot_q ? 0 : p.Hq * nt, nk = p.Hkv * nt, nv = p.rot_skip_v ? 0 : p.Hkv * vt;
   const int per_row = nq + nk + nv;
   const int i0 = blockIdx.x * kRowsPerWg;
   const int total = min(kRowsPerWg, p.S - i0) * per_row;
@@ -296,7 +298,7 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(Params p) {
   const int j = s.past + i;  // absolute position of query i and of new key i
   if (j >= p.T) return;
   const int pos = j < p.rot_max ? j : p.rot_max - 1;
-  const int nq = p.rot_q ? 0 : p.Hq * p.D, nk = p.Hkv * p.D, nv = p.Hkv * p.Dv;
+  const int nq = p.rot_q ? 0 : p.Hq * p.D, nk = p.Hkv * p.D, nv = p.rot_skip_v ? 0 : p.Hkv * p.Dv;
   const T *qrow = (const T *)p.q + b * p.q_sb + (int64_t)i * p.q_ss;
   T *yrow = (T *)p.y + b * p.y_sb + (int64_t)i * p.y_ss;
   for (int t = threadIdx.x; t < nq + nk + nv; t += kThreads) {
