@@ -207,6 +207,18 @@ SMALL = {
     "gqa_decode_softcap_sink_bf16": Problem(op="gqa", dtype="bf16", B=3, S=1, L=1, P=500, Hq=16,
                                             Hkv=2, D=128, Dv=128, causal=1, window=200,
                                             softcap=30.0, has_sink=True, lens_range=(1, 500)),
+    # head size 256 in the prefill kernel (one wavefront per SIMD): causal GQA
+    # with ragged tiles, Attention with a cache, nonpad lengths, bias and
+    # softcap, and a BOOL mask per query row
+    "gqa_d256_causal_bf16": Problem(op="gqa", dtype="bf16", B=2, S=150, L=150, Hq=8, Hkv=2,
+                                    D=256, Dv=256, causal=1),
+    "attention_d256_bias_softcap_f16": Problem(op="attention", dtype="f16", B=2, S=70, L=100,
+                                               P=20, Hq=4, Hkv=2, D=256, Dv=256, causal=1,
+                                               has_lens=True, lens_range=(50, 120),
+                                               bias_bh=(2, 4), softcap=8.0),
+    "attention_d256_boolmask_bf16": Problem(op="attention", dtype="bf16", B=1, S=65, L=90, Hq=4,
+                                            Hkv=1, D=256, Dv=256, causal=0, has_lens=False,
+                                            mask_kind="bool", mask_bhs=(1, 1, 65)),
 }
 
 
@@ -225,7 +237,10 @@ def tiled_capable(p, mode="fwd"):
         return False
     if p.mask_kind and mode == "decode" and (p.Hq // p.Hkv) * p.S > 16:
         return False
-    return p.dtype in ("f16", "bf16") and p.D == p.Dv and p.D in (64, 128)
+    # head size 256: the prefill kernel only (the split-KV partials take 64 / 128)
+    if p.D == 256 and mode == "decode":
+        return False
+    return p.dtype in ("f16", "bf16") and p.D == p.Dv and p.D in (64, 128, 256)
 
 
 @pytest.mark.parametrize("name", list(SMALL))

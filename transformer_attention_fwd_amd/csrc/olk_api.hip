@@ -480,7 +480,7 @@ olk_status olk_attention_decode(const olk_attn_desc *desc, const olk_attn_io *io
   olk::Params pchk = p;
   if (pchk.present_k && pchk.present_v) pchk.keys_in_past = 1;
   const bool decode_ok = tiled_ok && olk::decode_supports(pchk, desc->dtype);
-  const bool split_ok = tiled_ok && !pa.mask;
+  const bool split_ok = tiled_ok && !pa.mask && pa.D != 256;  // the split partials: 64 or 128
   if (desc->kernel == OLK_KERNEL_TILED && !decode_ok && !split_ok) return OLK_E_UNSUPPORTED;
   // In place at head size 128 the decode kernel appends the new rows itself
   // (no separate copy launch); every other case appends before the split kernels.

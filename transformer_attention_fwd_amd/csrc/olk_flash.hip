@@ -1,5 +1,5 @@
-// Prefill attention forward for gfx950 (CDNA4): f16/bf16 inputs, head size 64
-// or 128, fp32 accumulation.
+// Prefill attention forward for gfx950 (CDNA4): f16/bf16 inputs, head size 64,
+// 128 or 256, fp32 accumulation.
 //
 // Computes Y = Softmax((Q K^T) * scale + bias) V with grouped KV heads, causal /
 // local-window / length masks, softcap, head_sink and the present outputs of
@@ -158,8 +158,9 @@ struct FPlan {
 
 // Wavefronts per SIMD the register budget is sized for: three at head size 64
 // (more workgroups resident when a grid holds few query tiles; the BOOL-mask
-// form needs more registers and keeps two), two at head size 128.
-template <int D, int BM> constexpr int kOcc = (D == 64 && BM != 2) ? 3 : 2;
+// form needs more registers and keeps two), two at head size 128, one at 256
+// (whose K/V double buffers take 128 KB of LDS: one workgroup per CU).
+template <int D, int BM> constexpr int kOcc = D == 256 ? 1 : (D == 64 && BM != 2) ? 3 : 2;
 
 // BM: 0 no bias, 1 attn_bias, 2 attn_mask (BOOL, or MultiHeadAttention's int32
 // binary mask), with or without attn_bias.
@@ -185,9 +186,9 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
   // can tell the loads landing in one buffer from the reads of the other and
   // does not wait for the next tile's loads before the first read of this
   // one.  The forms whose registers do not allow the unrolled body (head
-  // size 64 at three wavefronts per SIMD, BOOL mask with softcap) select the
-  // buffers at run time and keep that wait.
-  constexpr bool UNROLL2 = !(BM == 2 && SOFTCAP) && !(D == 64 && SOFTCAP);
+  // size 64 at three wavefronts per SIMD, BOOL mask with softcap, bias or
+  // mask at head size 256) select the buffers at run time and keep that wait.
+  constexpr bool UNROLL2 = !(BM == 2 && SOFTCAP) && !(D == 64 && SOFTCAP) && !(D == 256 && BM != 0);
   __shared__ __attribute__((aligned(16))) T klds0[BN * D];
   __shared__ __attribute__((aligned(16))) T klds1[BN * D];
   __shared__ __attribute__((aligned(16))) T vlds0[BN * D];
@@ -340,8 +341,8 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
   // finite; their scores are masked, so their P is exactly 0).
   constexpr int RPL = 1024 / RB;        // rows per load instruction
   constexpr int NLD = BN / (4 * RPL);   // load instructions per wavefront per tile and matrix
-  auto fk = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
-  auto fv = [](int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); };
+  auto fk = [](int r) { return D >= 128 ? (r & 15) : ((r >> 1) & 7); };
+  auto fv = [](int r) { return D >= 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); };
   // per lane: tile row and byte offsets inside a tile of new K/V rows
   // (strides k_ss / v_ss), fixed for the kernel
   int lrow[NLD];
@@ -988,8 +989,10 @@ hipError_t launch_flash(const Params &p, int dtype, hipStream_t st) {
     if (p.D == 64 && (pl.GH != 1 || (int64_t)p.S * p.bias_si * 2 >= (int64_t)1 << 31)) pl.qs = 0;
   }
   if (dtype == DT_BF16)
-    return p.D == 64 ? launch_td<bf16, 64>(p, pl, st) : launch_td<bf16, 128>(p, pl, st);
-  return p.D == 64 ? launch_td<f16, 64>(p, pl, st) : launch_td<f16, 128>(p, pl, st);
+    return p.D == 64 ? launch_td<bf16, 64>(p, pl, st)
+           : p.D == 128 ? launch_td<bf16, 128>(p, pl, st) : launch_td<bf16, 256>(p, pl, st);
+  return p.D == 64 ? launch_td<f16, 64>(p, pl, st)
+         : p.D == 128 ? launch_td<f16, 128>(p, pl, st) : launch_td<f16, 256>(p, pl, st);
 }
 
 }  // namespace olk

@@ -434,9 +434,11 @@ hipError_t launch_plan(const Params &p, int dtype, const Plan &pl, hipStream_t s
 
 }  // namespace
 
+// The matrix-core prefill kernel (head size 64, 128 or 256) and, at head size
+// 64 or 128, the tiled split partials (launch_tiled_split refuses 256).
 bool tiled_supports(const Params &p, int dtype) {
   if (dtype != DT_F16 && dtype != DT_BF16) return false;
-  if (p.D != p.Dv || (p.D != 64 && p.D != 128)) return false;
+  if (p.D != p.Dv || (p.D != 64 && p.D != 128 && p.D != 256)) return false;
   // attn_mask (BOOL, and MultiHeadAttention's int32 binary mask) runs in the
   // prefill kernel's mask path and the decode kernels (not in the tiled split
   // partials); the qk output is a separate launch after the attention
@@ -455,6 +457,7 @@ int tiled_split_count(const Params &p, int split_tiles) {
 
 hipError_t launch_tiled_split(const Params &p, int dtype, int split_tiles, float *ws,
                               hipStream_t st) {
+  if (p.D != 64 && p.D != 128) return hipErrorInvalidValue;
   const int n_split = tiled_split_count(p, split_tiles);
   return launch_plan(p, dtype, make_plan(p, n_split, split_tiles, ws), st);
 }
