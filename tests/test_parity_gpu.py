@@ -219,6 +219,12 @@ SMALL = {
     "attention_d256_boolmask_bf16": Problem(op="attention", dtype="bf16", B=1, S=65, L=90, Hq=4,
                                             Hkv=1, D=256, Dv=256, causal=0, has_lens=False,
                                             mask_kind="bool", mask_bhs=(1, 1, 65)),
+    # head size 256 in the decode kernel: a variable past, and bias + softcap
+    "gqa_decode_d256_bf16": Problem(op="gqa", dtype="bf16", B=3, S=1, L=1, P=700, Hq=8, Hkv=2,
+                                    D=256, Dv=256, causal=1, lens_range=(0, 700)),
+    "attention_decode_d256_softcap_f16": Problem(op="attention", dtype="f16", B=2, S=2, L=2,
+                                                 P=300, Hq=8, Hkv=2, D=256, Dv=256, causal=1,
+                                                 has_lens=False, bias_bh=(2, 8), softcap=5.0),
 }
 
 
@@ -237,8 +243,9 @@ def tiled_capable(p, mode="fwd"):
         return False
     if p.mask_kind and mode == "decode" and (p.Hq // p.Hkv) * p.S > 16:
         return False
-    # head size 256: the prefill kernel only (the split-KV partials take 64 / 128)
-    if p.D == 256 and mode == "decode":
+    # head size 256 in decode: the decode kernel (up to 16 rows per KV head);
+    # the tiled split partials take 64 / 128 only
+    if p.D == 256 and mode == "decode" and (p.Hq // p.Hkv) * p.S > 16:
         return False
     return p.dtype in ("f16", "bf16") and p.D == p.Dv and p.D in (64, 128, 256)
 
@@ -319,7 +326,8 @@ def test_decode_workload_out_of_place():
 
 
 @pytest.mark.parametrize("name", ["gqa_decode_f16", "gqa_decode_rows8_bf16",
-                                  "gqa_decode_rows16_f16", "gqa_decode_8k_bf16"])
+                                  "gqa_decode_rows16_f16", "gqa_decode_8k_bf16",
+                                  "gqa_decode_d256_bf16"])
 def test_small_decode_inplace(name):
     # in-place KV cache at head size 128: the decode kernel appends the new
     # rows itself; Y against the oracle, present bit-exact over [0, total_b)

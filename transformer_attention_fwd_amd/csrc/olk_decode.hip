@@ -1,5 +1,5 @@
-// Split-KV decode for gfx950: a few query rows (G heads x S queries <= 16 per
-// KV head) against a long key sequence.  HBM-bound: every cached key row is
+// Split-KV decode for gfx950 (head size 64, 128 or 256): a few query rows (G
+// heads x S queries <= 16 per KV head) against a long key sequence.  HBM-bound: every cached key row is
 // read once per (batch, KV head) and serves all G query heads of the group.
 //
 // Same result as the prefill path (onnx-light-cpu Python API "Custom
@@ -17,11 +17,11 @@
 // * QK^T: v_mfma_f32_16x16x32 with Q^T held in VGPRs as the B operand (16
 //   columns = the row slots (query, head)).  K is loaded as whole rows (4 rows
 //   per instruction) and its A operand (16 keys x 32 dims) read back from a
-//   per-wavefront LDS tile at head size 128; at head size 64 K goes from
+//   per-wavefront LDS tile at head size 128 / 256; at head size 64 K goes from
 //   memory straight into the A operand (16 bytes per lane).
 // * The S^T accumulator puts each row slot's 16 scores in 4 lanes; the online
 //   softmax (exp2 domain, lazy rescale) reduces across them with lane swaps.
-// * PV: at head size 128 on v_mfma_f32_16x16x16 (decode_mfma_kernel below:
+// * PV: at head size 128 / 256 on v_mfma_f32_16x16x16 (decode_mfma_kernel below:
 //   P^T straight from the score accumulator, V^T by transposed LDS reads);
 //   at head size 64 on the VALU: P goes through a 1 KB LDS buffer per
 //   wavefront and is read back as broadcasts; lanes own 4 head dimensions of
@@ -411,7 +411,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p, DPlan pl) {
 }
 
 
-// ---- head size 128: PV on the matrix cores ----
+// ---- head size 128 and 256: PV on the matrix cores ----
 // O^T += V^T P^T runs on v_mfma_f32_16x16x16: P^T (the B operand: lane l
 // holds keys 4 (l / 16) + i of slot l % 16) is the S^T accumulator itself,
 // and V^T (the A operand: lane l holds keys 4 (l / 16) + i of dim 16 blk +
@@ -441,15 +441,22 @@ template <typename T> __device__ __forceinline__ uint32_t pack2p(float a, float 
   return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
 
-template <typename T, int NR, bool EPI>
+template <typename T, int D, int NR, bool EPI>
 __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p, DPlan pl) {
-  constexpr int D = 128;
+  static_assert(D == 128 || D == 256, "head size 128 or 256");
   typedef typename DV<T>::v8 vec8;
   typedef typename DV4<T>::v4 vec4;
   constexpr int NKS = D / 32;   // k-steps of QK^T (32 dims each)
   constexpr int NBLK = D / 16;  // 16-dim blocks of O^T
   constexpr int VRB = D * 2;    // bytes per K/V row, in memory and in LDS
-  // K and V rows of the current step, one tile each per wavefront
+  constexpr int CHR = D / 8;    // 16-byte chunks per row
+  constexpr int RPI = 64 / CHR; // whole rows per load instruction
+  constexpr int NV = kStep / RPI;  // V load instructions per step (K: NKS = kStep / RPI too)
+  static_assert(NKS * RPI == kStep, "one K load per k-step");
+  // K and V rows of the current step, one tile each per wavefront (separate
+  // variables: the compiler then orders one's writes freely against the
+  // other's reads), and the wavefronts' partials for the merge (128 KB in all
+  // at head size 256, where the registers allow one workgroup per CU anyway)
   __shared__ __attribute__((aligned(16))) T vbw[4][kStep * D];
   __shared__ __attribute__((aligned(16))) T kbw[4][kStep * D];
   __shared__ __attribute__((aligned(16))) float mrg_ml[4][2][16];
@@ -533,27 +540,27 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p, DPlan p
   const __amdgpu_buffer_rsrc_t krs = row_rsrc(kpast + (int64_t)sp_lo * D, nrec);
   const __amdgpu_buffer_rsrc_t vrs = row_rsrc(vpast + (int64_t)sp_lo * D, nrec);
 
-  // V registers: row 4 t + lane / 16 of the step, 16-byte chunk lane % 16;
+  // V registers: row RPI t + lane / CHR of the step, 16-byte chunk lane % CHR;
   // written to LDS at that row, slot chunk ^ 2 (row & 7)
   // transposed reads: this lane addresses row 4 (l / 16) + (l % 16) / 4 and
   // dims 16 blk + 4 ((l % 16) & 3), i.e. byte tro + 32 (blk ^ (row & 7))
   const int trr = 4 * kq + ((lane & 15) >> 2);
   const uint32_t tro = (uint32_t)(trr * VRB + 16 * (((lane & 3) >> 1)) + 8 * (lane & 1));
   const int trx = trr & 7;
-  // lane byte offset within a step, for K and V alike: row lane / 16 (+ 4 t),
-  // 16-byte chunk lane % 16, so one load instruction reads 4 whole rows (full
-  // cache lines).  K loaded in the MFMA operand layout instead (16 rows x 64
-  // bytes per instruction) took twice the address work per byte: 218 vs 202 us
-  // on the decode workload.
-  const uint32_t voff = (uint32_t)(lane >> 4) * VRB + (uint32_t)(lane & 15) * 16u;
+  // lane byte offset within a step, for K and V alike: row lane / CHR (+ RPI
+  // t), 16-byte chunk lane % CHR, so one load instruction reads RPI whole rows
+  // (full cache lines).  K loaded in the MFMA operand layout instead (16 rows x
+  // 64 bytes per instruction) took twice the address work per byte: 218 vs
+  // 202 us on the decode workload.
+  const uint32_t voff = (uint32_t)(lane / CHR) * VRB + (uint32_t)(lane % CHR) * 16u;
   const int my_steps = n_steps > wave ? (n_steps - wave + 3) / 4 : 0;
 
-  auto load_step = [&](int st, uint4 (&kk)[NKS], uint4 (&vv)[kStep / 4]) __attribute__((always_inline)) {
+  auto load_step = [&](int st, uint4 (&kk)[NKS], uint4 (&vv)[NV]) __attribute__((always_inline)) {
     const uint32_t so = (uint32_t)((wave + 4 * st) * kStep * VRB);
 #pragma unroll
-    for (int t = 0; t < NKS; ++t) kk[t] = ld_buf16(krs, voff + so + 4 * t * VRB);
+    for (int t = 0; t < NKS; ++t) kk[t] = ld_buf16(krs, voff + so + RPI * t * VRB);
 #pragma unroll
-    for (int t = 0; t < kStep / 4; ++t) vv[t] = ld_buf16(vrs, voff + so + 4 * t * VRB);
+    for (int t = 0; t < NV; ++t) vv[t] = ld_buf16(vrs, voff + so + RPI * t * VRB);
   };
 
   float m = kNegInf, l = 0.f;
@@ -564,11 +571,11 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p, DPlan p
   const float cap_in = p.softcap > 0.f ? 2.0f * kLog2e / p.softcap : 0.f;
 
   uint4 k0[NKS], k1[NKS], k2[NKS];
-  uint4 v0[kStep / 4], v1[kStep / 4], v2[kStep / 4];
+  uint4 v0[NV], v1[NV], v2[NV];
   char *vl = (char *)vbw[wave];
   char *kl = (char *)kbw[wave];
-  auto body = [&](int it, uint4 (&kr)[NKS], const uint4 (&vr)[kStep / 4], uint4 (&kf)[NKS],
-                  uint4 (&vf)[kStep / 4]) __attribute__((always_inline)) {
+  auto body = [&](int it, uint4 (&kr)[NKS], const uint4 (&vr)[NV], uint4 (&kf)[NKS],
+                  uint4 (&vf)[NV]) __attribute__((always_inline)) {
     if (it + 2 < my_steps) load_step(it + 2, kf, vf);
     const int j0 = base + (wave + 4 * it) * kStep;
     // S^T (16 keys x 16 slots)
@@ -579,7 +586,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p, DPlan p
       // slot c ^ (r & 15), so the operand reads below (16 rows at one chunk)
       // hit distinct banks; one wavefront's LDS operations run in order, so
       // no barrier is needed
-      const int r = 4 * t + (lane >> 4), c = lane & 15;
+      const int r = RPI * t + lane / CHR, c = lane % CHR;
       *(uint4 *)(kl + r * VRB + 16 * (c ^ (r & 15))) = kr[t];
     }
 #pragma unroll
@@ -631,9 +638,9 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p, DPlan p
     l += lsum;  // lane-local partial of slot n
     // the step's V rows into this wavefront's LDS tile (swizzled chunks)
 #pragma unroll
-    for (int t = 0; t < kStep / 4; ++t) {
-      const int r = 4 * t + (lane >> 4);
-      const int c = lane & 15;
+    for (int t = 0; t < NV; ++t) {
+      const int r = RPI * t + lane / CHR;
+      const int c = lane % CHR;
       *(uint4 *)(vl + r * VRB + 16 * (c ^ (2 * (r & 7)))) = vr[t];
     }
     // PV on the matrix cores
@@ -650,7 +657,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p, DPlan p
   // wait-count analysis from treating Q as in flight inside the step loop.
   if (my_steps > 0) load_step(0, k0, v0);
   if (my_steps > 1) load_step(1, k1, v1);
-  constexpr int kLoadsPerStep = NKS + kStep / 4;
+  constexpr int kLoadsPerStep = NKS + NV;
   static_assert(2 * kLoadsPerStep < 64, "vmcnt holds 6 bits");
   if (my_steps > 1) __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * kLoadsPerStep));
   else if (my_steps == 1) __builtin_amdgcn_s_waitcnt(vmcnt_only(kLoadsPerStep));
@@ -710,11 +717,11 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p, DPlan p
 
 template <typename T, int D, bool EPI>
 void launch_nr_epi(const Params &p, const DPlan &pl, int nr, dim3 grid, hipStream_t st) {
-  if constexpr (D == 128) {
-    // head size 128: PV on the matrix cores
-    if (nr <= 4) hipLaunchKernelGGL((decode_mfma_kernel<T, 4, EPI>), grid, dim3(kThreads), 0, st, p, pl);
-    else if (nr <= 8) hipLaunchKernelGGL((decode_mfma_kernel<T, 8, EPI>), grid, dim3(kThreads), 0, st, p, pl);
-    else hipLaunchKernelGGL((decode_mfma_kernel<T, 16, EPI>), grid, dim3(kThreads), 0, st, p, pl);
+  if constexpr (D >= 128) {
+    // head size 128 or 256: PV on the matrix cores
+    if (nr <= 4) hipLaunchKernelGGL((decode_mfma_kernel<T, D, 4, EPI>), grid, dim3(kThreads), 0, st, p, pl);
+    else if (nr <= 8) hipLaunchKernelGGL((decode_mfma_kernel<T, D, 8, EPI>), grid, dim3(kThreads), 0, st, p, pl);
+    else hipLaunchKernelGGL((decode_mfma_kernel<T, D, 16, EPI>), grid, dim3(kThreads), 0, st, p, pl);
   } else {
     if (nr <= 4) hipLaunchKernelGGL((decode_kernel<T, D, 4, EPI>), grid, dim3(kThreads), 0, st, p, pl);
     else if (nr <= 8) hipLaunchKernelGGL((decode_kernel<T, D, 8, EPI>), grid, dim3(kThreads), 0, st, p, pl);
@@ -733,16 +740,17 @@ hipError_t launch_nr(const Params &p, const DPlan &pl, int nr, dim3 grid, hipStr
 }  // namespace
 
 // The decode kernel takes every (query, head) row of one KV head in 16 slots;
-// at head size 128 it reads every key from the past buffer (keys_in_past).
+// at head size 128 / 256 it reads every key from the past buffer (keys_in_past).
 bool decode_supports(const Params &p, int dtype) {
-  return (dtype == DT_F16 || dtype == DT_BF16) && p.D == p.Dv && (p.D == 64 || p.D == 128) &&
-         p.G * p.S <= 16 && p.scale > 0.f && (p.D == 64 || p.keys_in_past);
+  return (dtype == DT_F16 || dtype == DT_BF16) && p.D == p.Dv &&
+         (p.D == 64 || p.D == 128 || p.D == 256) && p.G * p.S <= 16 && p.scale > 0.f &&
+         (p.D == 64 || p.keys_in_past);
 }
 
-// Head size 128 in place (present is the past buffer, every key read from
-// it): the decode kernel can append the new rows itself.
+// Head size 128 or 256 in place (present is the past buffer, every key read
+// from it): the decode kernel can append the new rows itself.
 bool decode_appends(const Params &p, int dtype) {
-  return decode_supports(p, dtype) && p.D == 128 && p.kv_inplace && p.keys_in_past;
+  return decode_supports(p, dtype) && p.D >= 128 && p.kv_inplace && p.keys_in_past;
 }
 
 hipError_t launch_decode(const Params &p, int dtype, int split_keys, int n_split, float *ws,
@@ -758,8 +766,10 @@ hipError_t launch_decode(const Params &p, int dtype, int split_keys, int n_split
   const dim3 grid((unsigned)n);
   const int nr = p.G * p.S;
   if (dtype == DT_BF16)
-    return p.D == 64 ? launch_nr<bf16, 64>(p, pl, nr, grid, st) : launch_nr<bf16, 128>(p, pl, nr, grid, st);
-  return p.D == 64 ? launch_nr<f16, 64>(p, pl, nr, grid, st) : launch_nr<f16, 128>(p, pl, nr, grid, st);
+    return p.D == 64 ? launch_nr<bf16, 64>(p, pl, nr, grid, st)
+           : p.D == 128 ? launch_nr<bf16, 128>(p, pl, nr, grid, st) : launch_nr<bf16, 256>(p, pl, nr, grid, st);
+  return p.D == 64 ? launch_nr<f16, 64>(p, pl, nr, grid, st)
+         : p.D == 128 ? launch_nr<f16, 128>(p, pl, nr, grid, st) : launch_nr<f16, 256>(p, pl, nr, grid, st);
 }
 
 }  // namespace olk
