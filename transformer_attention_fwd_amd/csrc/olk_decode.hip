@@ -1,6 +1,7 @@
 // Split-KV decode for gfx950 (head size 64, 128 or 256): a few query rows (G
-// heads x S queries <= 16 per KV head) against a long key sequence.  HBM-bound: every cached key row is
-// read once per (batch, KV head) and serves all G query heads of the group.
+// heads x S queries <= 16 per KV head) against a long key sequence.
+// HBM-bound: every cached key row is read once per (batch, KV head) and
+// serves all G query heads of the group.
 //
 // Same result as the prefill path (onnx-light-cpu Python API "Custom
 // operators", "Microsoft GroupQueryAttention": grouped heads, causal / local
