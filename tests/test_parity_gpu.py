@@ -493,12 +493,13 @@ def test_qk_matmul_output(mode, dtype):
 
 
 @pytest.mark.parametrize("mode", [0, 1, 2, 3])
-def test_qk_matmul_output_tiles_d128(mode):
-    # head size 128, several key tiles with T a multiple of 4 (16-byte rows)
-    # and more than one 128-row query tile, through the matrix-core qk kernel
-    # and the generic one
-    p = Problem(op="attention", dtype="f16", B=2, S=150, L=130, P=30, Hq=4, Hkv=2, D=128,
-                Dv=128, causal=1, has_lens=True, lens_range=(100, 160), mask_kind="bool",
+@pytest.mark.parametrize("D", [128, 256])
+def test_qk_matmul_output_tiles(mode, D):
+    # head sizes 128 and 256, several key tiles with T a multiple of 4 (16-byte
+    # rows) and more than one 128-row query tile, through the matrix-core qk
+    # kernel and the generic one
+    p = Problem(op="attention", dtype="f16", B=2, S=150, L=130, P=30, Hq=4, Hkv=2, D=D,
+                Dv=D, causal=1, has_lens=True, lens_range=(100, 160), mask_kind="bool",
                 mask_bhs=(2, 4, 150), bias_bh=(2, 1), softcap=6.0, qk_mode=mode)
     _check_qk(p, 720 + mode, ("fwd", "decode", "fwd-generic"))
 
@@ -511,7 +512,7 @@ def _check_qk(p, seed, runs):
         _say(f"[parity] qk mode={p.qk_mode} dtype={p.dtype} D={p.D} {run}")
         c = _run(p, to_dev(inp), mode=mode_, kernel=kernel)
         name = olk.olk_last_kernel_name()
-        if p.dtype in ("f16", "bf16") and p.D in (64, 128) and kernel != "generic":
+        if p.dtype in ("f16", "bf16") and p.D in (64, 128, 256) and kernel != "generic":
             assert name.endswith("+olk_qk_mfma"), name
         else:
             assert name.endswith("+olk_qk"), name

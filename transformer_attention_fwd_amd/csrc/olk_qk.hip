@@ -1,5 +1,5 @@
 // qk_matmul_output of ai.onnx Attention on the matrix cores (gfx950): f16/bf16
-// inputs, head size 64 or 128, float32 output (B, Hq, S, T).
+// inputs, head size 64, 128 or 256, float32 output (B, Hq, S, T).
 //
 // What is written follows the onnx-light reference kernels header page,
 // "class Attention" (qk_matmul_output_mode 0: (Q K^T) * scale for every key;
@@ -189,11 +189,11 @@ __global__ __launch_bounds__(kThreads, 2) void qk_mfma_kernel(Params p, int n_qt
 
 }  // namespace
 
-// The matrix-core qk output: f16/bf16, head size 64 or 128 (D == Dv not
+// The matrix-core qk output: f16/bf16, head size 64, 128 or 256 (D == Dv not
 // needed: V is not read), 16-byte aligned Q and key rows.
 bool qk_mfma_supports(const Params &p, int dtype) {
   if (dtype != DT_F16 && dtype != DT_BF16) return false;
-  if (p.D != 64 && p.D != 128) return false;
+  if (p.D != 64 && p.D != 128 && p.D != 256) return false;
   auto al = [](const void *x) { return ((uintptr_t)x & 15) == 0; };
   if (!al(p.q) || !al(p.k) || (p.past_k && !al(p.past_k))) return false;
   const int es = 2;
@@ -208,10 +208,12 @@ hipError_t launch_qk_mfma(const Params &p, int dtype, hipStream_t st) {
   const dim3 grid((unsigned)((int64_t)p.B * p.Hq * n_qt)), block(kThreads);
   if (dtype == DT_BF16) {
     if (p.D == 64) hipLaunchKernelGGL((qk_mfma_kernel<bf16, 64>), grid, block, 0, st, p, n_qt);
-    else hipLaunchKernelGGL((qk_mfma_kernel<bf16, 128>), grid, block, 0, st, p, n_qt);
+    else if (p.D == 128) hipLaunchKernelGGL((qk_mfma_kernel<bf16, 128>), grid, block, 0, st, p, n_qt);
+    else hipLaunchKernelGGL((qk_mfma_kernel<bf16, 256>), grid, block, 0, st, p, n_qt);
   } else {
     if (p.D == 64) hipLaunchKernelGGL((qk_mfma_kernel<f16, 64>), grid, block, 0, st, p, n_qt);
-    else hipLaunchKernelGGL((qk_mfma_kernel<f16, 128>), grid, block, 0, st, p, n_qt);
+    else if (p.D == 128) hipLaunchKernelGGL((qk_mfma_kernel<f16, 128>), grid, block, 0, st, p, n_qt);
+    else hipLaunchKernelGGL((qk_mfma_kernel<f16, 256>), grid, block, 0, st, p, n_qt);
   }
   return hipGetLastError();
 }
