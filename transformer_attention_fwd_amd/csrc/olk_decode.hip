@@ -443,7 +443,7 @@ template <typename T> __device__ __forceinline__ uint32_t pack2p(float a, float 
 }
 
 template <typename T, int D, int NR, bool EPI>
-__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(Params p, DPlan pl) {
+__global__ __launch_bounds__(kThreads, (D == 128 ? 2 : 1)) void decode_mfma_kernel(Params p, DPlan pl) {
   static_assert(D == 128 || D == 256, "head size 128 or 256");
   typedef typename DV<T>::v8 vec8;
   typedef typename DV4<T>::v4 vec4;
