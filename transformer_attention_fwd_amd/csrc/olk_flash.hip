@@ -9,7 +9,7 @@
 //
 // * A workgroup is 4 wavefronts x 32 row slots; two workgroups share a CU
 //   (two wavefronts per SIMD, so one wave's MFMAs overlap the other's softmax;
-//   three at head size 64).
+//   three at head size 64, and for the plain form at head size 128).
 //   Slots pack the GH query heads sharing one KV head with consecutive queries
 //   (slot -> (query, head)): every K/V tile in LDS serves the whole head group.
 // * S^T = K Q^T and O^T += V^T P^T run on v_mfma_f32_32x32x16.  In the S^T
@@ -24,7 +24,8 @@
 //   for V.  The V^T operand of PV is read with ds_read_b64_tr_b16 from the
 //   row-major V tile: each transposed read hands a lane 4 consecutive keys of
 //   its head dimension, in the k order in which the accumulator supplies P^T.
-// * Keys advance in tiles of 64, double-buffered in LDS with one barrier per
+// * Keys advance in tiles of 64 (32 for the plain form at head size 128, so
+//   that three workgroups fit a CU's LDS), double-buffered in LDS with one barrier per
 //   tile; the next tile's loads are in flight while the current tile
 //   computes.  The buffers are separate LDS variables and the key loop is
 //   unrolled by two, so the compiler can tell the loads landing in one
@@ -158,9 +159,13 @@ struct FPlan {
 
 // Wavefronts per SIMD the register budget is sized for: three at head size 64
 // (more workgroups resident when a grid holds few query tiles; the BOOL-mask
-// form needs more registers and keeps two), two at head size 128, one at 256
-// (whose K/V double buffers take 128 KB of LDS: one workgroup per CU).
-template <int D, int BM> constexpr int kOcc = D == 256 ? 1 : (D == 64 && BM != 2) ? 3 : 2;
+// form needs more registers and keeps two); at head size 128 three for the
+// plain form (no bias, mask or softcap: 168 registers, with 32-key tiles so
+// that three workgroups' K/V buffers fit the LDS; measured 1-2 % faster than
+// two with 64-key tiles) and two otherwise; one at 256 (whose K/V double
+// buffers take 128 KB of LDS: one workgroup per CU).
+template <int D, int BM, bool CAP>
+constexpr int kOcc = D == 256 ? 1 : ((D == 64 && BM != 2) || (D == 128 && BM == 0 && !CAP)) ? 3 : 2;
 
 // BM: 0 no bias, 1 attn_bias, 2 attn_mask (BOOL, or MultiHeadAttention's int32
 // binary mask), with or without attn_bias.
@@ -169,13 +174,13 @@ template <int D, int BM> constexpr int kOcc = D == 256 ? 1 : (D == 64 && BM != 2
 // the bias seeds the QK^T accumulator, so the matrix cores add it and the
 // scores leave the MFMAs as (Q K^T) * scale + bias, in natural-log units.
 template <typename T, int D, int BM, bool SOFTCAP, bool QS = false>
-__global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Params p, FPlan pl) {
+__global__ __launch_bounds__(kThreads, (kOcc<D, BM, SOFTCAP>)) void flash_fwd_kernel(Params p, FPlan pl) {
   typedef typename FV<T>::v8 vec8;
   static_assert(!QS || (BM == 1 && !SOFTCAP), "the bias seeds the accumulator only without softcap");
   constexpr bool BIAS = BM != 0;   // the score epilogue reads a bias row
   constexpr bool MASK = BM == 2;
   constexpr int CH = D / 8;             // 16-byte chunks per K/V row
-  constexpr int BN = 64;                // keys per tile
+  constexpr int BN = (D == 128 && kOcc<D, BM, SOFTCAP> == 3) ? 32 : 64;  // keys per tile
   constexpr int KB = BN / 32;           // 32-key blocks per tile
   constexpr int NST = BN / 16;          // 16-key PV steps per tile
   constexpr int NKS = D / 16;           // QK^T k-steps
@@ -524,7 +529,7 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
   // accumulator layout; gathered per lane they took 8 bytes from each of 32
   // rows per instruction
   constexpr bool BLDS = QS && D == 64;
-  constexpr bool BPRE = BIAS && D == 64 && kOcc<D, BM> == 2 && !BLDS;
+  constexpr bool BPRE = BIAS && D == 64 && kOcc<D, BM, SOFTCAP> == 2 && !BLDS;
   typedef uint2 BiasWords[BIAS ? KB : 1][4];
   typedef uint32_t MaskWords[MASK ? KB : 1][4];
   BiasWords bcur, bnext;
@@ -890,12 +895,14 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM>)) void flash_fwd_kernel(Para
   }
   // Y goes through LDS so that whole rows are stored: each wavefront writes
   // its 32 rows (row-major, 16-byte chunks XOR-swizzled by the row) into its
-  // own 32 RB bytes of the K buffers, then CH lanes store one row (16 bytes
+  // own 32 RB bytes of the K buffers (of the K and V buffers with 32-key
+  // tiles, one buffer each), then CH lanes store one row (16 bytes
   // each), 64 / CH rows per instruction (lane-per-row stores of 8 bytes at a
   // time were measured to take ~4k clocks per workgroup).  Rows past S are
   // staged but not stored.
   if (fuse_end && kt0 < kt1) __syncthreads();  // the present copy read the K/V buffers
-  char *ys = (char *)(wave < 2 ? klds0 : klds1) + (wave & 1) * 32 * RB;
+  char *ys = BN == 32 ? (char *)(wave == 0 ? klds0 : wave == 1 ? klds1 : wave == 2 ? vlds0 : vlds1)
+                      : (char *)(wave < 2 ? klds0 : klds1) + (wave & 1) * 32 * RB;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
