@@ -159,13 +159,13 @@ struct FPlan {
 
 // Wavefronts per SIMD the register budget is sized for: three at head size 64
 // (more workgroups resident when a grid holds few query tiles; the BOOL-mask
-// form needs more registers and keeps two); at head size 128 three for the
-// plain form (no bias, mask or softcap: 168 registers, with 32-key tiles so
-// that three workgroups' K/V buffers fit the LDS; measured 1-2 % faster than
-// two with 64-key tiles) and two otherwise; one at 256 (whose K/V double
-// buffers take 128 KB of LDS: one workgroup per CU).
+// form needs more registers and keeps two); at head size 128 three without
+// bias or mask (at most 168 registers, with 32-key tiles so that three
+// workgroups' K/V buffers fit the LDS; measured 1-2 % faster than two with
+// 64-key tiles, 8 % with softcap) and two otherwise; one at 256 (whose K/V
+// double buffers take 128 KB of LDS: one workgroup per CU).
 template <int D, int BM, bool CAP>
-constexpr int kOcc = D == 256 ? 1 : ((D == 64 && BM != 2) || (D == 128 && BM == 0 && !CAP)) ? 3 : 2;
+constexpr int kOcc = D == 256 ? 1 : ((D == 64 && BM != 2) || (D == 128 && BM == 0)) ? 3 : 2;
 
 // BM: 0 no bias, 1 attn_bias, 2 attn_mask (BOOL, or MultiHeadAttention's int32
 // binary mask), with or without attn_bias.
@@ -446,7 +446,15 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM, SOFTCAP>)) void flash_fwd_ke
           *(const uint4 *)((const char *)vbuf + r * RB + 16 * (cc ^ fv(r)));
     }
   };
-  // K operand offsets inside a tile (row kb * 32 + col; fk does not depend on kb)
+  // K operand offsets inside a tile (row kb * 32 + col; fk does not depend on kb).
+  // The swizzle XORs the chunk index and the k-step picks chunk 2 ks + half,
+  // so koff[ks] = koff[0] ^ 32 ks (the chunk bits lie below the row's byte
+  // offset); likewise voff[db] = voff[0] ^ 64 db.  XOFF forms keep only the
+  // first offset live and form the others with one XOR per read: fewer
+  // registers (the softcap form at head size 128 then fits three wavefronts
+  // per SIMD, and the head-size-256 bias / mask forms stop spilling) for a
+  // few VALU instructions, which cost 1-3 % where registers were not short.
+  constexpr bool XOFF = (D == 128 && BM == 0 && SOFTCAP) || (D == 256 && BM != 0 && !QS);
   uint32_t koff[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) koff[ks] = (uint32_t)(col * RB + 16 * ((2 * ks + half) ^ fk(col)));
@@ -615,6 +623,9 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM, SOFTCAP>)) void flash_fwd_ke
   // (zeros, or with QS the tile's bias values)
   auto qk = [&](const T *kbuf, f32x16 (&sacc)[KB], const f32x16 (&seed)[KB]) __attribute__((always_inline)) {
     const char *kl = (const char *)kbuf;
+    uint32_t koff0 = koff[0];
+    // (an opaque copy per tile, so the XORs are not hoisted out of the loop)
+    if constexpr (XOFF) asm volatile("" : "+v"(koff0));
     // block-major: the first 32 keys' scores are final while the second
     // block's MFMAs run, so their row max can start (each chain keeps its
     // k order, so the sums are the same)
@@ -622,7 +633,7 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM, SOFTCAP>)) void flash_fwd_ke
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const vec8 a = *(const vec8 *)(kl + kb * 32 * RB + koff[ks]);
+        const vec8 a = *(const vec8 *)(kl + kb * 32 * RB + (XOFF ? koff0 ^ (32u * ks) : koff[ks]));
         sacc[kb] = mma(a, qreg[ks], ks == 0 ? seed[kb] : sacc[kb]);
       }
     }
@@ -654,6 +665,9 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM, SOFTCAP>)) void flash_fwd_ke
     constexpr float kOut = SOFTCAP ? __builtin_huge_valf() : kNegInf;  // an excluded key
     const char *vl = (const char *)vbuf;
     const int j0 = kt * BN;
+    uint32_t voff0 = voff[0];
+    if constexpr (XOFF) asm volatile("" : "+v"(voff0));
+    const auto vo = [&](int db) { return XOFF ? voff0 ^ (64u * db) : voff[db]; };
     if (GENERAL) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -756,9 +770,9 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM, SOFTCAP>)) void flash_fwd_ke
         typedef short s16x4 __attribute__((ext_vector_type(4)));
         typedef __attribute__((address_space(3))) s16x4 *tr_ptr;
         const uint2 lo = __builtin_bit_cast(
-            uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((tr_ptr)(vl + 16 * st * RB + voff[db])));
+            uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((tr_ptr)(vl + 16 * st * RB + vo(db))));
         const uint2 hi = __builtin_bit_cast(
-            uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((tr_ptr)(vl + (16 * st + 8) * RB + voff[db])));
+            uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((tr_ptr)(vl + (16 * st + 8) * RB + vo(db))));
         const vec8 a = __builtin_bit_cast(vec8, make_uint4(lo.x, lo.y, hi.x, hi.y));
         o[db] = mma(a, pb, o[db]);
       }
