@@ -225,6 +225,15 @@ SMALL = {
     "attention_decode_d256_softcap_f16": Problem(op="attention", dtype="f16", B=2, S=2, L=2,
                                                  P=300, Hq=8, Hkv=2, D=256, Dv=256, causal=1,
                                                  has_lens=False, bias_bh=(2, 8), softcap=5.0),
+    # head-size-64 softcap prefill without bias or mask (four wavefronts per
+    # SIMD): window + sink with bf16 (fixed exponent offset), a cache and
+    # nonpad lengths with f16 (running max)
+    "gqa_d64_window_sink_softcap_bf16": Problem(op="gqa", dtype="bf16", B=2, S=200, L=200, Hq=8,
+                                                Hkv=2, D=64, Dv=64, causal=1, window=90,
+                                                softcap=3.0, has_sink=True),
+    "attention_d64_cache_softcap_f16": Problem(op="attention", dtype="f16", B=2, S=150, L=150,
+                                               P=40, Hq=4, Hkv=2, D=64, Dv=64, causal=1,
+                                               has_lens=True, lens_range=(60, 191), softcap=5.0),
 }
 
 

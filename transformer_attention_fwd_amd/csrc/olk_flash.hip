@@ -158,14 +158,17 @@ struct FPlan {
 };
 
 // Wavefronts per SIMD the register budget is sized for: three at head size 64
-// (more workgroups resident when a grid holds few query tiles; the BOOL-mask
-// form needs more registers and keeps two); at head size 128 three without
-// bias or mask (at most 168 registers, with 32-key tiles so that three
-// workgroups' K/V buffers fit the LDS; measured 1-2 % faster than two with
-// 64-key tiles, 8 % with softcap) and two otherwise; one at 256 (whose K/V
-// double buffers take 128 KB of LDS: one workgroup per CU).
+// (more workgroups resident when a grid holds few query tiles; four for the
+// softcap form without bias or mask, 128 registers: 5 % faster than three;
+// the BOOL-mask form needs more registers and keeps two); at head size 128
+// three without bias or mask (at most 168 registers, with 32-key tiles so
+// that three workgroups' K/V buffers fit the LDS; measured 1-2 % faster than
+// two with 64-key tiles, 8 % with softcap) and two otherwise; one at 256
+// (whose K/V double buffers take 128 KB of LDS: one workgroup per CU).
 template <int D, int BM, bool CAP>
-constexpr int kOcc = D == 256 ? 1 : ((D == 64 && BM != 2) || (D == 128 && BM == 0)) ? 3 : 2;
+constexpr int kOcc = D == 256                   ? 1
+                     : (D == 64 && BM == 0 && CAP) ? 4
+                     : ((D == 64 && BM != 2) || (D == 128 && BM == 0)) ? 3 : 2;
 
 // BM: 0 no bias, 1 attn_bias, 2 attn_mask (BOOL, or MultiHeadAttention's int32
 // binary mask), with or without attn_bias.
@@ -451,10 +454,10 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM, SOFTCAP>)) void flash_fwd_ke
   // so koff[ks] = koff[0] ^ 32 ks (the chunk bits lie below the row's byte
   // offset); likewise voff[db] = voff[0] ^ 64 db.  XOFF forms keep only the
   // first offset live and form the others with one XOR per read: fewer
-  // registers (the softcap form at head size 128 then fits three wavefronts
-  // per SIMD, and the head-size-256 bias / mask forms stop spilling) for a
+  // registers (the softcap forms at head sizes 128 and 64 then fit three and
+  // four wavefronts per SIMD, and the head-size-256 bias / mask forms stop spilling) for a
   // few VALU instructions, which cost 1-3 % where registers were not short.
-  constexpr bool XOFF = (D == 128 && BM == 0 && SOFTCAP) || (D == 256 && BM != 0 && !QS);
+  constexpr bool XOFF = (D <= 128 && BM == 0 && SOFTCAP) || (D == 256 && BM != 0 && !QS);
   uint32_t koff[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) koff[ks] = (uint32_t)(col * RB + 16 * ((2 * ks + half) ^ fk(col)));
