@@ -171,7 +171,8 @@ constexpr int kOcc = D == 256                   ? 1
                      : ((D == 64 && BM != 2) || (D == 128 && BM == 0)) ? 3 : 2;
 
 // BM: 0 no bias, 1 attn_bias, 2 attn_mask (BOOL, or MultiHeadAttention's int32
-// binary mask), with or without attn_bias.
+// binary mask) with attn_bias, 3 attn_mask without attn_bias (no bias terms in
+// the score pipeline).
 // QS (attn_bias without softcap, the scale an exact power of two): Q is
 // multiplied by the scale as it is loaded (exact: a change of exponent) and
 // the bias seeds the QK^T accumulator, so the matrix cores add it and the
@@ -180,8 +181,9 @@ template <typename T, int D, int BM, bool SOFTCAP, bool QS = false>
 __global__ __launch_bounds__(kThreads, (kOcc<D, BM, SOFTCAP>)) void flash_fwd_kernel(Params p, FPlan pl) {
   typedef typename FV<T>::v8 vec8;
   static_assert(!QS || (BM == 1 && !SOFTCAP), "the bias seeds the accumulator only without softcap");
-  constexpr bool BIAS = BM != 0;   // the score epilogue reads a bias row
-  constexpr bool MASK = BM == 2;
+  constexpr bool BIAS = BM == 1 || BM == 2;  // the score epilogue reads a bias row
+  constexpr bool MASK = BM >= 2;
+  constexpr bool WORDS = BM != 0;            // bias or mask words per tile
   constexpr int CH = D / 8;             // 16-byte chunks per K/V row
   constexpr int BN = (D == 128 && kOcc<D, BM, SOFTCAP> == 3) ? 32 : 64;  // keys per tile
   constexpr int KB = BN / 32;           // 32-key blocks per tile
@@ -196,7 +198,7 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM, SOFTCAP>)) void flash_fwd_ke
   // one.  The forms whose registers do not allow the unrolled body (head
   // size 64 at three wavefronts per SIMD, BOOL mask with softcap, bias or
   // mask at head size 256) select the buffers at run time and keep that wait.
-  constexpr bool UNROLL2 = !(BM == 2 && SOFTCAP) && !(D == 64 && SOFTCAP) && !(D == 256 && BM != 0);
+  constexpr bool UNROLL2 = !(MASK && SOFTCAP) && !(D == 64 && SOFTCAP) && !(D == 256 && BM != 0);
   __shared__ __attribute__((aligned(16))) T klds0[BN * D];
   __shared__ __attribute__((aligned(16))) T klds1[BN * D];
   __shared__ __attribute__((aligned(16))) T vlds0[BN * D];
@@ -228,9 +230,8 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM, SOFTCAP>)) void flash_fwd_ke
   const int pos_min = s.qoff + i0, pos_max = s.qoff + i_last;
   int hi = p.pad_add ? s.total : s.valid;
   if (p.causal) hi = min(hi, pos_max + 1);
-  // short masks exclude the keys beyond their columns (BIAS instantiations
-  // also serve BOOL attn_mask, with or without a bias)
-  if (BM == 1 || (MASK && p.bias)) hi = min(hi, p.bias_cols);
+  // short masks (a bias row, a mask row) exclude the keys beyond their columns
+  if (BIAS && p.bias) hi = min(hi, p.bias_cols);
   if (MASK) hi = min(hi, p.mask_cols);
   const int lo = p.window > 0 ? max(0, pos_min - p.window + 1) : 0;
   // no key tile at all when no key is allowed (every row then outputs 0)
@@ -664,7 +665,7 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM, SOFTCAP>)) void flash_fwd_ke
   // has no softcap.)
   auto softmax_pv = [&](int kt, const T *vbuf, f32x16 (&sacc)[KB], bool masked, const BiasWords &bwt,
                         const MaskWords &mwt) __attribute__((always_inline)) {
-    constexpr bool GENERAL = (BIAS && !QS) || SOFTCAP;
+    constexpr bool GENERAL = (WORDS && !QS) || SOFTCAP;
     constexpr float kOut = SOFTCAP ? __builtin_huge_valf() : kNegInf;  // an excluded key
     const char *vl = (const char *)vbuf;
     const int j0 = kt * BN;
@@ -694,7 +695,7 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM, SOFTCAP>)) void flash_fwd_ke
               // r in [0, 1] without NaN (rcp of +inf is 0)
               t = __builtin_amdgcn_rcpf(ex2(x2) + 1.0f);
             }
-            else t = (sacc[kb][4 * q4 + e] * p.scale + bv[e]) * kLog2e;
+            else t = BIAS ? (sacc[kb][4 * q4 + e] * p.scale + bv[e]) * kLog2e : sacc[kb][4 * q4 + e] * sl;
             // a false BOOL element excludes the key after the score pipeline;
             // a zero binary (int32) element adds mask_filter_value to it
             sacc[kb][4 * q4 + e] = ((mw >> (8 * e)) & 0xffu) ? t : (mask_i32 ? t + mfv_l2 : kOut);
@@ -823,7 +824,7 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM, SOFTCAP>)) void flash_fwd_ke
     // previous one into the buffers that hold it (unread meanwhile), so every
     // tile issues the same loads and the wait for the words below can leave
     // these in flight
-    if (more || BIAS) issue_loads(more ? kt + 1 : max(kt - 1, kt0), kn, vn);
+    if (more || WORDS) issue_loads(more ? kt + 1 : max(kt - 1, kt0), kn, vn);
     if (more && BPRE) load_bias(kt + 1, bnext);
     if (BLDS && wave_active && bias_rows_whole(kt)) {
       bias_from_lds();
@@ -838,7 +839,7 @@ __global__ __launch_bounds__(kThreads, (kOcc<D, BM, SOFTCAP>)) void flash_fwd_ke
                              j0 < lo || (p.pad_add && j0 + BN > s.pad);
       // the words have landed once at most the 2 NLD K/V loads issued after
       // them are in flight (the counter is in order)
-      if constexpr (BIAS && !BPRE && !BLDS) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 | (2 * NLD));
+      if constexpr (WORDS && !BPRE && !BLDS) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 | (2 * NLD));
       f32x16 seed[KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
@@ -952,10 +953,11 @@ hipError_t launch_td(const Params &p, const FPlan &pl, hipStream_t st) {
   const int64_t n = (int64_t)p.B * p.Hkv * pl.n_hg * pl.n_qt;
   if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)n), block(kThreads);
-  const int bm = p.mask ? 2 : (p.bias ? 1 : 0);
+  const int bm = p.mask ? (p.bias ? 2 : 3) : (p.bias ? 1 : 0);
   const bool cap = p.softcap > 0.f;
 #define OLK_FLASH(BMV, CAPV) hipLaunchKernelGGL((flash_fwd_kernel<T, D, BMV, CAPV>), grid, block, 0, st, p, pl)
-  if (bm == 2) { if (cap) OLK_FLASH(2, true); else OLK_FLASH(2, false); }
+  if (bm == 3) { if (cap) OLK_FLASH(3, true); else OLK_FLASH(3, false); }
+  else if (bm == 2) { if (cap) OLK_FLASH(2, true); else OLK_FLASH(2, false); }
   else if (bm == 1 && pl.qs) hipLaunchKernelGGL((flash_fwd_kernel<T, D, 1, false, true>), grid, block, 0, st, p, pl);
   else if (bm == 1) { if (cap) OLK_FLASH(1, true); else OLK_FLASH(1, false); }
   else { if (cap) OLK_FLASH(0, true); else OLK_FLASH(0, false); }
