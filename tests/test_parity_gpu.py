@@ -234,6 +234,17 @@ SMALL = {
     "attention_d64_cache_softcap_f16": Problem(op="attention", dtype="f16", B=2, S=150, L=150,
                                                P=40, Hq=4, Hkv=2, D=64, Dv=64, causal=1,
                                                has_lens=True, lens_range=(60, 191), softcap=5.0),
+    # BOOL masks at head size 128 over several key tiles: with softcap and no
+    # bias (the mask-only form), and with a bias and no softcap
+    "attention_boolmask_softcap_bf16": Problem(op="attention", dtype="bf16", B=2, S=140, L=200,
+                                               P=20, Hq=4, Hkv=2, D=128, Dv=128, causal=1,
+                                               has_lens=True, lens_range=(120, 221),
+                                               mask_kind="bool", mask_bhs=(2, 4, 140),
+                                               softcap=4.0),
+    "attention_boolmask_bias_f16": Problem(op="attention", dtype="f16", B=2, S=130, L=190,
+                                           Hq=4, Hkv=2, D=128, Dv=128, causal=0, has_lens=False,
+                                           mask_kind="bool", mask_bhs=(1, 1, 130),
+                                           bias_bh=(2, 1)),
 }
 
 
