@@ -245,6 +245,23 @@ __global__ __launch_bounds__(kWave) void combine_kernel(Params p, int n_split, i
   // latencies overlap (records of splits the decode kernels skipped hold
   // stale values, read but never used).
   const float m_first = lane < n_split ? part[lane * rec] : kNegInf;
+  // Few splits of short records: every load the merge needs (this lane's
+  // split length, its two dimensions of every split's record) goes out now,
+  // beside the maxima, so the merge waits for memory once; the sums below
+  // keep the order of the general path.
+  constexpr int kFewSplits = 16;
+  const bool few = n_split <= kFewSplits && p.Dv <= 2 * kWave;
+  float l_first = 0.f, ov[kFewSplits][2];
+  if (few) {
+    l_first = lane < n_split ? part[lane * rec + 1] : 0.f;
+#pragma unroll
+    for (int sp = 0; sp < kFewSplits; ++sp)
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int d = lane + k * kWave;
+        ov[sp][k] = sp < n_split && d < p.Dv ? part[sp * rec + 4 + d] : 0.f;
+      }
+  }
   // Only the splits that hold keys of this row's range [lo, hi) are used:
   // every partial kernel writes the records of those (a split outside the
   // range contributes nothing, and the decode kernels write no record there).
@@ -267,6 +284,29 @@ __global__ __launch_bounds__(kWave) void combine_kernel(Params p, int n_split, i
   float z = kNegInf;
   if (p.sink) z = to_f32(((const T *)p.sink)[h]);
   const float Mf = fmaxf(M, z);
+  if (few) {
+    const bool use = lane >= sp0 && lane < sp1;
+    const float w = use && m_first != kNegInf ? expf(m_first - Mf) : 0.f;
+    // (the general path's lane sp - sp0 holds split sp's term: the same
+    // lanes here, so the wave sum adds in the same order)
+    float l = wave_sum(__shfl(use ? w * l_first : 0.f, (lane + sp0) & (kWave - 1), kWave));
+    if (p.sink) l += expf(z - Mf);
+    const float inv = 1.f / l;
+    float acc[2] = {0.f, 0.f};
+#pragma unroll
+    for (int sp = 0; sp < kFewSplits; ++sp) {
+      if (sp < sp0 || sp >= sp1) continue;
+      const float ws_ = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), sp));
+#pragma unroll
+      for (int k = 0; k < 2; ++k) acc[k] += ws_ * ov[sp][k];
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int d = lane + k * kWave;
+      if (d < p.Dv) yr[d] = from_f32<T>(acc[k] * inv);
+    }
+    return;
+  }
   float l = 0.f;
   for (int sp = sp0 + lane; sp < sp1; sp += kWave) {
     const float m = part[sp * rec];
